@@ -1,0 +1,208 @@
+"""TACO CPU oracle -- TEST INFRASTRUCTURE ONLY.
+
+Thin ctypes wrapper over ``taco_oracle.c`` (plain C, double precision, one
+thread).  Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg
+of ``bench.py`` may import this package; the GPU library and its Python binding
+never do.  What each function computes, and the readings of points the TACO
+paper leaves open, are documented in ``taco_oracle.c``.
+
+Arrays are numpy arrays: bf16 tensors travel as ``uint16`` bit patterns,
+codes as ``uint8``, alpha / s as ``float32``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "taco_oracle.c")
+_LIB = os.path.join(_HERE, "libtaco_oracle.so")
+
+#: epsilon of Eq. 6 that the GPU library documents; the oracle takes it as a
+#: parameter so tests can vary it.
+EPS = 1e-20
+
+_lib = None
+
+
+def build(force: bool = False) -> str:
+    """Compile the oracle with gcc (no fast-math, no FMA contraction)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + f".tmp{os.getpid()}"
+        subprocess.check_call([
+            "gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math",
+            "-fPIC", "-shared", _SRC, "-o", tmp, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        lib = ctypes.CDLL(build())
+        P = ctypes.c_void_p
+        i64, i32, f64 = ctypes.c_int64, ctypes.c_int, ctypes.c_double
+        lib.taco_oracle_e4m3_decode.argtypes = [ctypes.c_uint8]
+        lib.taco_oracle_e4m3_decode.restype = f64
+        lib.taco_oracle_e4m3_encode.argtypes = [ctypes.c_float]
+        lib.taco_oracle_e4m3_encode.restype = ctypes.c_uint8
+        lib.taco_oracle_double_to_bf16.argtypes = [f64]
+        lib.taco_oracle_double_to_bf16.restype = ctypes.c_uint16
+        lib.taco_oracle_e4m3_encode_array.argtypes = [P, i64, P]
+        lib.taco_oracle_e4m3_encode_array.restype = None
+        lib.taco_oracle_e4m3_decode_array.argtypes = [P, i64, P]
+        lib.taco_oracle_e4m3_decode_array.restype = None
+        lib.taco_oracle_double_to_bf16_array.argtypes = [P, i64, P]
+        lib.taco_oracle_double_to_bf16_array.restype = None
+        lib.taco_oracle_fwht.argtypes = [P, i32]
+        lib.taco_oracle_fwht.restype = None
+        lib.taco_oracle_ash_block.argtypes = [P, i32, f64, f64, P, P, P]
+        lib.taco_oracle_compress.argtypes = [P, i64, i32, f64, f64, P, P, P]
+        lib.taco_oracle_reconstruct_f64.argtypes = [P, P, P, i64, i32, P]
+        lib.taco_oracle_decompress.argtypes = [P, P, P, i64, i32, P]
+        lib.taco_oracle_decompress_accumulate.argtypes = [P, P, P, i64, i32, P]
+        lib.taco_oracle_roundtrip_noquant.argtypes = [P, i32, f64, f64, P]
+        _lib = lib
+    return _lib
+
+
+def _ptr(a: np.ndarray):
+    assert a.flags["C_CONTIGUOUS"]
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _check(rc: int):
+    if rc != 0:
+        raise ValueError("oracle rejected the arguments (block must be a power of two "
+                         "in [2, 4096] dividing the element count)")
+
+
+# ---------------------------------------------------------------- codecs ----
+
+def e4m3_decode(codes) -> np.ndarray:
+    """Values (float64) of E4M3 codes."""
+    lib = _load()
+    c = np.ascontiguousarray(codes, dtype=np.uint8)
+    out = np.empty(c.shape, np.float64)
+    lib.taco_oracle_e4m3_decode_array(_ptr(c), c.size, _ptr(out))
+    return out
+
+
+def e4m3_encode(values) -> np.ndarray:
+    """Nearest-even, saturating E4M3 codes of float32 values."""
+    lib = _load()
+    v = np.ascontiguousarray(values, dtype=np.float32)
+    out = np.empty(v.shape, np.uint8)
+    lib.taco_oracle_e4m3_encode_array(_ptr(v), v.size, _ptr(out))
+    return out
+
+
+def double_to_bf16(values) -> np.ndarray:
+    """bf16 bit patterns (uint16) of float64 values, nearest-even."""
+    lib = _load()
+    v = np.ascontiguousarray(values, dtype=np.float64)
+    out = np.empty(v.shape, np.uint16)
+    lib.taco_oracle_double_to_bf16_array(_ptr(v), v.size, _ptr(out))
+    return out
+
+
+def encode_function_address() -> int:
+    """Address of the scalar C encoder (for the exhaustive test helper)."""
+    return ctypes.cast(_load().taco_oracle_e4m3_encode, ctypes.c_void_p).value
+
+
+def decode_function_address() -> int:
+    """Address of the scalar C decoder (for the exhaustive test helper)."""
+    return ctypes.cast(_load().taco_oracle_e4m3_decode, ctypes.c_void_p).value
+
+
+def fwht(v) -> np.ndarray:
+    """Unnormalised Sylvester-order FWHT of the last axis (float64 copy)."""
+    lib = _load()
+    a = np.array(v, dtype=np.float64, copy=True)
+    n = a.shape[-1]
+    flat = a.reshape(-1, n)
+    for row in flat:
+        lib.taco_oracle_fwht(_ptr(row), n)
+    return flat.reshape(a.shape)
+
+
+# ------------------------------------------------------------ operator ----
+
+def ash_block(x_bits, block: int, tau: float = 1.0, eps: float = EPS):
+    """(alpha, Gt, Z) in float64 for one block of bf16 bit patterns."""
+    lib = _load()
+    x = np.ascontiguousarray(x_bits, dtype=np.uint16)
+    assert x.size == block
+    alpha = np.zeros(1, np.float64)
+    gt = np.zeros(block, np.float64)
+    z = np.zeros(block, np.float64)
+    _check(lib.taco_oracle_ash_block(_ptr(x), block, tau, eps, _ptr(alpha), _ptr(gt), _ptr(z)))
+    return float(alpha[0]), gt, z
+
+
+def compress(x_bits, block: int, tau: float = 1.0, eps: float = EPS):
+    """Codes (uint8, same shape as x), alpha and s (float32, one per block)."""
+    lib = _load()
+    x = np.ascontiguousarray(x_bits, dtype=np.uint16)
+    n = x.size
+    if block <= 0 or n % block:
+        raise ValueError("element count must be a multiple of the block size")
+    codes = np.empty(x.shape, np.uint8)
+    alpha = np.empty(n // block, np.float32)
+    scale = np.empty(n // block, np.float32)
+    _check(lib.taco_oracle_compress(_ptr(x), n, block, tau, eps, _ptr(codes), _ptr(alpha), _ptr(scale)))
+    return codes, alpha, scale
+
+
+def reconstruct_f64(codes, alpha, scale, block: int) -> np.ndarray:
+    """G' in float64 (before any output rounding), same shape as codes."""
+    lib = _load()
+    c = np.ascontiguousarray(codes, dtype=np.uint8)
+    a = np.ascontiguousarray(alpha, dtype=np.float32)
+    s = np.ascontiguousarray(scale, dtype=np.float32)
+    out = np.empty(c.shape, np.float64)
+    _check(lib.taco_oracle_reconstruct_f64(_ptr(c), _ptr(a), _ptr(s), c.size, block, _ptr(out)))
+    return out
+
+
+def decompress(codes, alpha, scale, block: int) -> np.ndarray:
+    """bf16 bit patterns (uint16) of the reconstruction."""
+    lib = _load()
+    c = np.ascontiguousarray(codes, dtype=np.uint8)
+    a = np.ascontiguousarray(alpha, dtype=np.float32)
+    s = np.ascontiguousarray(scale, dtype=np.float32)
+    y = np.empty(c.shape, np.uint16)
+    _check(lib.taco_oracle_decompress(_ptr(c), _ptr(a), _ptr(s), c.size, block, _ptr(y)))
+    return y
+
+
+def decompress_accumulate(codes, alpha, scale, block: int, acc: np.ndarray) -> np.ndarray:
+    """acc (float32, updated in place and returned) += G'."""
+    lib = _load()
+    c = np.ascontiguousarray(codes, dtype=np.uint8)
+    a = np.ascontiguousarray(alpha, dtype=np.float32)
+    s = np.ascontiguousarray(scale, dtype=np.float32)
+    assert acc.dtype == np.float32 and acc.flags["C_CONTIGUOUS"] and acc.size == c.size
+    _check(lib.taco_oracle_decompress_accumulate(_ptr(c), _ptr(a), _ptr(s), c.size, block, _ptr(acc)))
+    return acc
+
+
+def roundtrip_noquant(x_bits, block: int, tau: float = 1.0, eps: float = EPS) -> np.ndarray:
+    """Eq. 8 output fed straight to Eq. 12-13 (no quantisation), float64."""
+    lib = _load()
+    x = np.ascontiguousarray(x_bits, dtype=np.uint16)
+    out = np.empty(block, np.float64)
+    _check(lib.taco_oracle_roundtrip_noquant(_ptr(x), block, tau, eps, _ptr(out)))
+    return out
+
+
+# ------------------------------------------------------------ helpers ----
+
+def bf16_bits_to_f64(bits) -> np.ndarray:
+    """Exact widening of bf16 bit patterns."""
+    b = np.asarray(bits, dtype=np.uint16)
+    return (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)

@@ -1,0 +1,307 @@
+/*
+ * TACO CPU oracle -- TEST INFRASTRUCTURE ONLY.
+ *
+ * A plain, slow, single-threaded C implementation of what the TACO compression
+ * operator computes, written in double precision from the paper's equations.
+ * Only the test-suite, the smoke check and the CPU-baseline leg of the benchmark
+ * may load this library.  The GPU library never links it, includes it or
+ * calls it, and it shares no code, header or constant table with the GPU side.
+ *
+ * Source ([TACO] below): the page "TACO: Efficient Communication Compression of
+ * Intermediate Tensors for Scalable Tensor-Parallel LLM Training", sections
+ * 4.2.2 (ASH transform, Eq. 5-8), 4.3 (Dual-Scale FP8 quantization, Eq. 9-13)
+ * and Algorithm 1 (sender side and receiver side), plus section 2.3 / Figure 3
+ * / Eq. 4 for the E4M3 format.
+ *
+ * Readings of points the paper leaves open (all stated once here):
+ *  - epsilon sits inside the square root of Eq. 6 (the text calls sigma an RMS
+ *    amplitude); its value is a parameter (the library documents 1e-20).
+ *  - Q_max is the largest finite value of OCP E4M3 ("E4M3FN"): bias 7, no
+ *    infinities, NaN = S.1111.111, max 448.  The paper cites the FP8 formats
+ *    paper of Micikevicius et al. (2022) for the format.
+ *  - Cvt_FP8 of Eq. 10 takes a single-precision argument (the conversion the
+ *    paper names takes a float) and rounds to nearest, ties to even,
+ *    saturating to +-448.  Exact zeros of the rotated block carry no sign in the
+ *    code: they encode as 0x00.
+ *  - "max" in Eq. 9 is the maximum absolute value.  A block whose rotated
+ *    values are all zero gets s = 0 and all-zero codes, and reconstructs to 0.
+ *  - The Hadamard matrix of Eq. 8 / Eq. 12 is Sylvester's, in natural order:
+ *    H[i][j] = (-1)^popcount(i & j), the matrix an in-place FWHT applies.
+ *  - alpha and s travel as float32 (each rounded once from double), and the
+ *    receiver uses exactly those float32 values.
+ *  - The decompressed tensor is rounded once to bfloat16 (nearest, ties to
+ *    even); the accumulate variant rounds G' once to float32 and adds it to
+ *    the float32 accumulator with one float32 addition.
+ *
+ * Build:  gcc -O2 -std=c11 -ffp-contract=off -fno-fast-math -fPIC -shared
+ *         taco_oracle.c -o libtaco_oracle.so -lm
+ */
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#define ORACLE_QMAX 448.0          /* largest finite OCP E4M3 value */
+#define ORACLE_MAX_BLOCK 4096
+
+/* ------------------------------------------------------------------------ */
+/* bfloat16 <-> double                                                        */
+/* ------------------------------------------------------------------------ */
+
+/* bfloat16 is the upper half of an IEEE binary32; widening is exact. */
+static double bf16_to_double(uint16_t b)
+{
+    uint32_t u = (uint32_t)b << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+/* Round q to the nearest integer, ties to the even integer (q >= 0). */
+static double round_half_even(double q)
+{
+    double fl = floor(q);
+    double d = q - fl;               /* exact: q has few significant bits */
+    if (d > 0.5) return fl + 1.0;
+    if (d < 0.5) return fl;
+    return (fmod(fl, 2.0) == 0.0) ? fl : fl + 1.0;
+}
+
+/*
+ * double -> bfloat16, round to nearest, ties to even (one rounding from the
+ * double value).  bfloat16 has 8 significant bits, exponents -126..127, and
+ * subnormals with step 2^-133.
+ */
+uint16_t taco_oracle_double_to_bf16(double g)
+{
+    if (isnan(g)) return 0x7FC0;
+    uint16_t sign = signbit(g) ? 0x8000 : 0;
+    double a = fabs(g);
+    double r;
+    if (a == 0.0) {
+        r = 0.0;
+    } else {
+        int e;
+        frexp(a, &e);                /* a = f * 2^e, f in [0.5, 1) */
+        int E = e - 1;               /* a in [2^E, 2^(E+1)) */
+        if (E < -126) E = -126;      /* subnormal range: fixed step 2^-133 */
+        double step = ldexp(1.0, E - 7);
+        r = round_half_even(a / step) * step;
+    }
+    /* r is a bfloat16 value (or overflows): express it through binary32. */
+    float f = (float)r;              /* exact when representable; inf beyond */
+    uint32_t u;
+    memcpy(&u, &f, sizeof u);
+    return sign | (uint16_t)(u >> 16);
+}
+
+/* ------------------------------------------------------------------------ */
+/* E4M3 codec ([TACO] section 2.3, Eq. 4: 4 exponent bits, 3 mantissa bits)   */
+/* ------------------------------------------------------------------------ */
+
+/* Value of an E4M3 code: sign, 4-bit exponent with bias 7, 3-bit mantissa;
+ * exponent field 0 is subnormal (m * 2^-9); S.1111.111 is NaN. */
+double taco_oracle_e4m3_decode(uint8_t c)
+{
+    int s = c >> 7, e = (c >> 3) & 0xF, m = c & 0x7;
+    if (e == 0xF && m == 0x7) return NAN;
+    double mag = (e == 0) ? ldexp((double)m, -9) : ldexp(1.0 + m / 8.0, e - 7);
+    return s ? -mag : mag;
+}
+
+/* Nearest E4M3 code to v, ties to even mantissa, saturating to +-448. */
+uint8_t taco_oracle_e4m3_encode(float v)
+{
+    if (isnan(v)) return 0x7F;
+    uint8_t sign = signbit(v) ? 0x80 : 0x00;
+    double a = fabs((double)v);
+    if (a >= ORACLE_QMAX) return sign | 0x7E;
+    int code;
+    if (a < ldexp(1.0, -6)) {
+        /* Subnormal range: values m * 2^-9.  m = 8 is the smallest normal,
+         * which has code 0x08, so the code equals the rounded multiple. */
+        code = (int)round_half_even(a / ldexp(1.0, -9));
+    } else {
+        int e;
+        frexp(a, &e);
+        int E = e - 1;                          /* a in [2^E, 2^(E+1)) */
+        double q = a / ldexp(1.0, E - 3);       /* in [8, 16), exact */
+        int mq = (int)round_half_even(q);       /* 8..16; 16 carries */
+        code = ((E + 7) << 3) + (mq - 8);
+    }
+    if (code > 0x7E) code = 0x7E;               /* 480 would be the NaN slot */
+    return sign | (uint8_t)code;
+}
+
+/* Element-wise array forms of the three conversions above. */
+void taco_oracle_e4m3_encode_array(const float *v, int64_t n, uint8_t *out)
+{
+    for (int64_t i = 0; i < n; ++i) out[i] = taco_oracle_e4m3_encode(v[i]);
+}
+
+void taco_oracle_e4m3_decode_array(const uint8_t *c, int64_t n, double *out)
+{
+    for (int64_t i = 0; i < n; ++i) out[i] = taco_oracle_e4m3_decode(c[i]);
+}
+
+void taco_oracle_double_to_bf16_array(const double *g, int64_t n, uint16_t *out)
+{
+    for (int64_t i = 0; i < n; ++i) out[i] = taco_oracle_double_to_bf16(g[i]);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Hadamard ([TACO] Eq. 8, Eq. 12; section 4.2.2 "FWHT")                      */
+/* ------------------------------------------------------------------------ */
+
+/* In-place unnormalised Walsh-Hadamard transform, Sylvester natural order:
+ * v <- H_n v with H_n[i][j] = (-1)^popcount(i & j).  n is a power of two. */
+void taco_oracle_fwht(double *v, int n)
+{
+    for (int h = 1; h < n; h *= 2)
+        for (int i = 0; i < n; i += 2 * h)
+            for (int j = i; j < i + h; ++j) {
+                double a = v[j], b = v[j + h];
+                v[j] = a + b;
+                v[j + h] = a - b;
+            }
+}
+
+static int valid_block(int B)
+{
+    if (B < 2 || B > ORACLE_MAX_BLOCK) return 0;
+    return (B & (B - 1)) == 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Sender side ([TACO] Algorithm 1, Eq. 5-10)                                 */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * ASH transform of one block, in double: returns alpha_k (Eq. 6-7), the
+ * rescaled block Gt (Eq. 7, element-wise product) and Z (Eq. 8).
+ * Any of the output pointers may be NULL.
+ */
+int taco_oracle_ash_block(const uint16_t *x, int B, double tau, double eps,
+                          double *alpha_out, double *gt_out, double *z_out)
+{
+    if (!valid_block(B)) return -1;
+    double G[ORACLE_MAX_BLOCK], Z[ORACLE_MAX_BLOCK];
+    double energy = 0.0;
+    for (int j = 0; j < B; ++j) {
+        G[j] = bf16_to_double(x[j]);
+        energy += G[j] * G[j];
+    }
+    double sigma = sqrt(energy / B + eps);         /* Eq. 6 */
+    double alpha = tau / sigma;                    /* Eq. 7 */
+    for (int j = 0; j < B; ++j) Z[j] = alpha * G[j];
+    if (gt_out) memcpy(gt_out, Z, sizeof(double) * (size_t)B);
+    taco_oracle_fwht(Z, B);                        /* Eq. 8 */
+    double c = 1.0 / sqrt((double)B);
+    for (int j = 0; j < B; ++j) Z[j] *= c;
+    if (alpha_out) *alpha_out = alpha;
+    if (z_out) memcpy(z_out, Z, sizeof(double) * (size_t)B);
+    return 0;
+}
+
+/*
+ * Compress a flattened tensor of n bf16 values (n a multiple of B) into
+ * n E4M3 codes and n/B pairs (alpha_k, s_k), block by block.
+ */
+int taco_oracle_compress(const uint16_t *x, int64_t n, int B, double tau,
+                         double eps, uint8_t *codes, float *alpha, float *scale)
+{
+    if (!valid_block(B) || n < 0 || n % B) return -1;
+    double Z[ORACLE_MAX_BLOCK];
+    for (int64_t k = 0; k < n / B; ++k) {
+        const uint16_t *xb = x + k * B;
+        double a;
+        taco_oracle_ash_block(xb, B, tau, eps, &a, NULL, Z);
+        double zmax = 0.0;
+        for (int j = 0; j < B; ++j) zmax = fmax(zmax, fabs(Z[j]));
+        double s = zmax / ORACLE_QMAX;             /* Eq. 9 */
+        uint8_t *q = codes + k * B;
+        for (int j = 0; j < B; ++j) {              /* Eq. 10 */
+            float v = (s > 0.0) ? (float)(Z[j] / s) : 0.0f;
+            if (v == 0.0f) v = 0.0f;               /* zero carries no sign */
+            q[j] = taco_oracle_e4m3_encode(v);
+        }
+        alpha[k] = (float)a;
+        scale[k] = (float)s;
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Receiver side ([TACO] Algorithm 1, Eq. 11-13)                              */
+/* ------------------------------------------------------------------------ */
+
+/* Reconstruct one block G'_k in double from its codes and float32 scalars. */
+static void reconstruct_block(const uint8_t *q, float alpha, float s, int B,
+                              double *out)
+{
+    for (int j = 0; j < B; ++j)                    /* Eq. 11 */
+        out[j] = taco_oracle_e4m3_decode(q[j]) * (double)s;
+    taco_oracle_fwht(out, B);                      /* Eq. 12 */
+    double c = 1.0 / sqrt((double)B);
+    for (int j = 0; j < B; ++j) out[j] = out[j] * c / (double)alpha; /* Eq. 13 */
+}
+
+/* G' in double precision (no output rounding), for error analysis. */
+int taco_oracle_reconstruct_f64(const uint8_t *codes, const float *alpha,
+                                const float *scale, int64_t n, int B,
+                                double *out)
+{
+    if (!valid_block(B) || n < 0 || n % B) return -1;
+    for (int64_t k = 0; k < n / B; ++k)
+        reconstruct_block(codes + k * B, alpha[k], scale[k], B, out + k * B);
+    return 0;
+}
+
+/* Decompress to bf16 (round to nearest even, once). */
+int taco_oracle_decompress(const uint8_t *codes, const float *alpha,
+                           const float *scale, int64_t n, int B, uint16_t *y)
+{
+    if (!valid_block(B) || n < 0 || n % B) return -1;
+    double g[ORACLE_MAX_BLOCK];
+    for (int64_t k = 0; k < n / B; ++k) {
+        reconstruct_block(codes + k * B, alpha[k], scale[k], B, g);
+        for (int j = 0; j < B; ++j)
+            y[k * B + j] = taco_oracle_double_to_bf16(g[j]);
+    }
+    return 0;
+}
+
+/* acc += G' in float32: G' rounded once to float32, then one float32 add. */
+int taco_oracle_decompress_accumulate(const uint8_t *codes, const float *alpha,
+                                      const float *scale, int64_t n, int B,
+                                      float *acc)
+{
+    if (!valid_block(B) || n < 0 || n % B) return -1;
+    double g[ORACLE_MAX_BLOCK];
+    for (int64_t k = 0; k < n / B; ++k) {
+        reconstruct_block(codes + k * B, alpha[k], scale[k], B, g);
+        for (int j = 0; j < B; ++j) {
+            float gf = (float)g[j];
+            acc[k * B + j] = acc[k * B + j] + gf;
+        }
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Self-check mode: the ASH round trip with quantisation left out            */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * Z from Eq. 8 fed straight into Eq. 12-13 (Z-hat = Z): returns the
+ * reconstructed block in double.  In exact arithmetic this is x itself.
+ */
+int taco_oracle_roundtrip_noquant(const uint16_t *x, int B, double tau,
+                                  double eps, double *out)
+{
+    double a;
+    if (taco_oracle_ash_block(x, B, tau, eps, &a, NULL, out)) return -1;
+    taco_oracle_fwht(out, B);
+    double c = 1.0 / sqrt((double)B);
+    for (int j = 0; j < B; ++j) out[j] = out[j] * c / a;
+    return 0;
+}

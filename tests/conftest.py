@@ -1,0 +1,73 @@
+"""Shared fixtures.  Tests marked ``gpu`` need an MI355X; everything else runs on
+the CPU (oracle pins, host-side validation, symbol checks)."""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import sys
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HELPERS = os.path.join(ROOT, "tests", "helpers")
+GOLDEN = os.path.join(ROOT, "tests", "golden")
+
+
+def pytest_configure(config):
+    config.addinivalue_line("markers", "gpu: needs an AMD Instinct MI355X (gfx950) GPU")
+
+
+def build_helper(name: str) -> str:
+    """Compile tests/helpers/<name>.c into a shared library next to it."""
+    src = os.path.join(HELPERS, name + ".c")
+    lib = os.path.join(HELPERS, "lib" + name + ".so")
+    if not os.path.exists(lib) or os.path.getmtime(lib) < os.path.getmtime(src):
+        tmp = lib + f".tmp{os.getpid()}"
+        subprocess.check_call(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-pthread",
+                               src, "-o", tmp, "-lm"])
+        os.replace(tmp, lib)
+    return lib
+
+
+@pytest.fixture(scope="session")
+def oracle_mod():
+    import oracle
+    oracle.build()
+    return oracle
+
+
+@pytest.fixture(scope="session")
+def synth_mod():
+    import synth
+    synth.build()
+    return synth
+
+
+def read_golden(name: str):
+    """Rows of a whitespace-separated fixture, comments (#) stripped."""
+    rows = []
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.split("#", 1)[0].strip()
+            if line:
+                rows.append(line.split())
+    return rows
+
+
+def cpu_threads() -> int:
+    try:
+        return max(1, min(len(os.sched_getaffinity(0)), 16))
+    except AttributeError:  # pragma: no cover
+        return 1
+
+
+def torch_e4m3_table() -> np.ndarray:
+    """Values of all 256 E4M3 codes from torch's float8_e4m3fn decoder."""
+    import torch
+    codes = torch.arange(256, dtype=torch.int32).to(torch.uint8)
+    return codes.view(torch.float8_e4m3fn).to(torch.float64).numpy()
