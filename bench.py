@@ -1,0 +1,353 @@
+#!/usr/bin/env python3
+"""Benchmark of the TACO compression operator on one MI355X.
+
+One step = one pass of the whole operator over one batch of synthetic input:
+``taco_compress`` then ``taco_decompress`` (the round trip) for the
+round-trip workloads, or four ``taco_compress`` + four
+``taco_decompress_accumulate`` calls for the four-payload workload.
+Inputs are resident in HBM before timing starts.  Buffer sets are rotated so
+that consecutive steps touch more than 512 MB (twice the 256 MB Infinity
+Cache) and each step streams from HBM.  The timed steps are replayed from a
+HIP graph so that host launch overhead does not gap the GPU.
+
+Prints one JSON line (rank 0, the only rank): the headline metric is input
+GB/s of bf16 (2 bytes per element) per round trip, plus a roofline object for
+the dominant kernel and the CPU oracle's rate on the same workload.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--block B]
+    python bench.py --all --out results.json     # every workload (stderr table)
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "compress+decompress GB/s of bf16 input and % of MI355X HBM peak"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E peak (AMD specification), GB/s
+MALL_BYTES = 256 << 20
+ROTATE_BYTES = 2 * MALL_BYTES
+KERNEL_SRC = os.path.join(ROOT, "gradients_taco_compress_amd", "csrc", "taco.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=400)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--workload", default=None)
+    p.add_argument("--block", type=int, default=None)
+    p.add_argument("--all", action="store_true", help="time every workload and block size")
+    p.add_argument("--out", default=None, help="also write the JSON record(s) to this file")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=10.0,
+                   help="minimum CPU time of the oracle baseline")
+    p.add_argument("--copy-probe", action="store_true",
+                   help="run only a plain device copy of known size (HBM counter calibration)")
+    p.add_argument("--no-graph", action="store_true", help="launch eagerly instead of a HIP graph")
+    return p.parse_args()
+
+
+def algorithmic_bytes(op: str, n: int, block: int) -> float:
+    """Bytes the operator must move: bf16 in/out 2/elem, codes 1/elem,
+    alpha + s 8 bytes per block, float32 accumulator 4 + 4 per element."""
+    side = 8.0 * n / block
+    if op == "compress":
+        return 2.0 * n + n + side
+    if op == "decompress":
+        return n + side + 2.0 * n
+    if op == "accumulate":
+        return n + side + 8.0 * n
+    raise ValueError(op)
+
+
+def kernel_hash() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def traffic_for(kernel: str, workload: str, block: int):
+    """HBM bytes per launch from the committed rocprofv3 counter runs, if they
+    were taken on the current kernel source; else None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_sha256_16") != kernel_hash():
+        return None
+    e = t.get("entries", {}).get(f"{kernel}:{workload}:{block}")
+    return None if e is None else e.get("hbm_bytes_per_launch")
+
+
+class Timer:
+    """HIP events on the stream the kernels run on."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.stream = torch.cuda.current_stream()
+
+    def time(self, fn, reps: int) -> float:
+        torch = self.torch
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record(self.stream)
+        for _ in range(reps):
+            fn()
+        b.record(self.stream)
+        b.synchronize()
+        return a.elapsed_time(b) * 1e-3          # seconds
+
+
+def make_graph(torch, fn, use_graph: bool):
+    if not use_graph:
+        return fn
+    fn()                                          # warm caches and lazy init outside capture
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    return g.replay
+
+
+def roundtrip_case(torch, taco, synth, name: str, block: int, steps: int, warmup: int,
+                   use_graph: bool):
+    import numpy as np
+    r = synth.WORKLOADS[name]
+    n = r.numel
+    x_bits = synth.generate(r)
+    x0 = torch.from_numpy(x_bits.view(np.int16)).cuda().view(torch.bfloat16)
+    m = n // block
+    per_set = 2 * n + n + 8 * m + 2 * n
+    nsets = max(1, -(-ROTATE_BYTES // per_set))
+    sets = []
+    for _ in range(nsets):
+        x = x0.clone()
+        codes = torch.empty((r.rows, r.cols), dtype=torch.uint8, device="cuda")
+        alpha = torch.empty(m, dtype=torch.float32, device="cuda")
+        scale = torch.empty(m, dtype=torch.float32, device="cuda")
+        y = torch.empty((r.rows, r.cols), dtype=torch.bfloat16, device="cuda")
+        sets.append((x, codes, alpha, scale, y))
+    del x0
+
+    def run_compress():
+        for x, codes, alpha, scale, _ in sets:
+            taco.compress(x, block=block, codes=codes, alpha=alpha, scale=scale)
+
+    def run_decompress():
+        for _, codes, alpha, scale, y in sets:
+            taco.decompress(codes, alpha, scale, block=block, out=y)
+
+    def run_steps():
+        for x, codes, alpha, scale, y in sets:
+            taco.compress(x, block=block, codes=codes, alpha=alpha, scale=scale)
+            taco.decompress(codes, alpha, scale, block=block, out=y)
+
+    for _ in range(max(1, warmup // nsets)):
+        run_steps()
+    torch.cuda.synchronize()
+    step_fn = make_graph(torch, run_steps, use_graph)
+    comp_fn = make_graph(torch, run_compress, use_graph)
+    dec_fn = make_graph(torch, run_decompress, use_graph)
+    reps = max(1, -(-steps // nsets))
+    timer = Timer(torch)
+    step_fn()
+    t_steps = timer.time(step_fn, reps)
+    k = reps * nsets
+    t_c = timer.time(comp_fn, reps) / k
+    t_d = timer.time(dec_fn, reps) / k
+    return {"n": n, "block": block, "steps": k, "t_step": t_steps / k, "t_compress": t_c,
+            "t_decompress": t_d, "sets": nsets, "rows": r.rows, "cols": r.cols,
+            "bytes_step": algorithmic_bytes("compress", n, block)
+            + algorithmic_bytes("decompress", n, block),
+            "input_bytes_step": 2.0 * n, "kernels": {"compress": t_c, "decompress": t_d}}
+
+
+def accumulate_case(torch, taco, synth, name: str, block: int, steps: int, warmup: int,
+                    use_graph: bool):
+    import numpy as np
+    r = synth.WORKLOADS[name]
+    n = r.numel
+    m = n // block
+    payloads = []
+    for seed in synth.ACCUMULATE_SEEDS:
+        x_bits = synth.generate(r, seed=seed)
+        x = torch.from_numpy(x_bits.view(np.int16)).cuda().view(torch.bfloat16)
+        del x_bits
+        codes = torch.empty((r.rows, r.cols), dtype=torch.uint8, device="cuda")
+        alpha = torch.empty(m, dtype=torch.float32, device="cuda")
+        scale = torch.empty(m, dtype=torch.float32, device="cuda")
+        payloads.append((x, codes, alpha, scale))
+    acc = torch.zeros((r.rows, r.cols), dtype=torch.float32, device="cuda")
+
+    def run_compress():
+        for x, codes, alpha, scale in payloads:
+            taco.compress(x, block=block, codes=codes, alpha=alpha, scale=scale)
+
+    def run_accumulate():
+        for _, codes, alpha, scale in payloads:
+            taco.decompress_accumulate(codes, alpha, scale, acc, block=block)
+
+    def run_steps():
+        run_compress()
+        run_accumulate()
+
+    for _ in range(max(1, warmup // 8)):
+        run_steps()
+    torch.cuda.synchronize()
+    step_fn = make_graph(torch, run_steps, use_graph)
+    comp_fn = make_graph(torch, run_compress, use_graph)
+    acc_fn = make_graph(torch, run_accumulate, use_graph)
+    reps = max(1, steps)
+    timer = Timer(torch)
+    step_fn()
+    t_steps = timer.time(step_fn, reps)
+    t_c = timer.time(comp_fn, reps) / (4 * reps)
+    t_a = timer.time(acc_fn, reps) / (4 * reps)
+    nb = len(payloads)
+    return {"n": n, "block": block, "steps": reps, "t_step": t_steps / reps, "t_compress": t_c,
+            "t_accumulate": t_a, "sets": 1, "rows": r.rows, "cols": r.cols,
+            "bytes_step": nb * (algorithmic_bytes("compress", n, block)
+                                + algorithmic_bytes("accumulate", n, block)),
+            "input_bytes_step": nb * 2.0 * n, "kernels": {"compress": t_c, "accumulate": t_a}}
+
+
+def cpu_baseline(synth, name: str, block: int, min_seconds: float, accumulate: bool):
+    """The oracle (single-threaded C, double precision) on the same workload,
+    round trips repeated until min_seconds of CPU time have passed."""
+    import numpy as np
+    import oracle
+    r = synth.WORKLOADS[name]
+    rows = r.rows
+    if r.numel > (1 << 26):                       # bounded sample: whole rows, <= 64 Mi elements
+        rows = max(1, (1 << 26) // r.cols)
+    sample = r.with_shape(rows)
+    x = synth.generate(sample)
+    n = x.size
+    reps, t = 0, 0.0
+    t0 = time.perf_counter()
+    while t < min_seconds or reps == 0:
+        codes, alpha, scale = oracle.compress(x, block)
+        if accumulate:
+            acc = np.zeros(n, np.float32)
+            oracle.decompress_accumulate(codes, alpha, scale, block, acc)
+        else:
+            oracle.decompress(codes, alpha, scale, block)
+        reps += 1
+        t = time.perf_counter() - t0
+    return {"value": 2.0 * n * reps / t / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{rows}x{r.cols} rows of {name} (seed {r.seed}), block {block}, "
+                      f"{reps} x (compress + {'accumulate' if accumulate else 'decompress'}) "
+                      f"in {t:.1f} s, one thread"}
+
+
+def record(res, name: str, args, cpu=None):
+    t_step = res["t_step"]
+    value = res["input_bytes_step"] / t_step / 1e9
+    kern = max(res["kernels"], key=lambda k: res["kernels"][k])
+    dur = res["kernels"][kern]
+    op = {"compress": "compress", "decompress": "decompress", "accumulate": "accumulate"}[kern]
+    kbytes = algorithmic_bytes(op, res["n"], res["block"])
+    achieved = kbytes / dur / 1e9
+    traffic = traffic_for(kern, name, res["block"])
+    rec = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": res["steps"],
+        "warmup": args.warmup,
+        "ms_per_step": round(t_step * 1e3, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": name, "tokens": res["rows"], "hidden": res["cols"],
+                   "block": res["block"], "target_energy": 1.0,
+                   "step": ("4x compress + 4x decompress_accumulate" if "t_accumulate" in res
+                            else "compress + decompress"),
+                   "buffer_sets": res["sets"], "graph": not args.no_graph},
+        "pct_hbm_peak": round(100.0 * res["bytes_step"] / t_step / 1e9 / HBM_PEAK_GBS, 2),
+        "kernel_us": {k: round(v * 1e6, 3) for k, v in res["kernels"].items()},
+        "roofline": {"bound": "hbm", "kernel": kern, "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "algorithmic_bytes": kbytes,
+                     "traffic": traffic},
+    }
+    if cpu is not None:
+        rec["cpu_baseline"] = cpu
+    return rec
+
+
+def copy_probe(torch):
+    """A plain device-to-device copy of 1 GiB, for HBM counter calibration."""
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": n, "launches": 3}), flush=True)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the operator "
+              "has no multi-GPU path in this build).", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    if args.copy_probe:
+        copy_probe(torch)
+        return
+    import gradients_taco_compress_amd as taco
+    import synth
+
+    use_graph = not args.no_graph
+    if args.all:
+        cases = [("laplace_2048x1024", 128), ("gpt2.7b_rowpar_8192x2560", 128),
+                 ("qwen7b_act_16384x3584", 128), ("qwen7b_act_16384x3584", 256),
+                 ("grad_8192x8192", 256), ("gpt175b_hidden_32768x12288", 256)]
+    else:
+        name = args.workload or synth.DEFAULT_WORKLOAD
+        block = args.block or synth.WORKLOADS[name].blocks[0]
+        cases = [(name, block)]
+    recs = []
+    for i, (name, block) in enumerate(cases):
+        print(f"[bench] {name} block {block}", file=sys.stderr, flush=True)
+        acc = name.startswith("gpt175b")
+        steps = args.steps if not acc else max(1, min(args.steps, 10))
+        if acc:
+            res = accumulate_case(torch, taco, synth, name, block, steps, args.warmup, use_graph)
+        else:
+            res = roundtrip_case(torch, taco, synth, name, block, steps, args.warmup, use_graph)
+        torch.cuda.empty_cache()
+        cpu = None
+        if not args.no_cpu_baseline and i == 0:
+            print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
+            cpu = cpu_baseline(synth, name, block, args.cpu_seconds, acc)
+        rec = record(res, name, args, cpu)
+        recs.append(rec)
+        if args.all:
+            print(json.dumps(rec), file=sys.stderr, flush=True)
+    if args.out:
+        with open(args.out, "w") as f:
+            json.dump(recs if args.all else recs[0], f, indent=1)
+    print(json.dumps(recs[0]), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,682 @@
+// libtaco: the TACO compression operator as hand-written HIP for gfx950.
+//
+// Operator: [TACO] = the page "TACO: Efficient Communication Compression of
+// Intermediate Tensors for Scalable Tensor-Parallel LLM Training", section
+// 4.2.2 (Eq. 5-8), section 4.3 (Eq. 9-13), Algorithm 1 and section 4.4.1
+// (one fused kernel per direction).  The C ABI is documented in taco.h.
+//
+// Design (gfx950, wave64, no LDS, no MFMA: the path streams HBM and does
+// O(B log B) adds per block, nothing here is a dense contraction):
+//
+//  * Lane layout.  A block of B elements is owned by LPB = 8 lanes of one
+//    wavefront (4 lanes when B = 32).  Lane t of a block holds the 16-byte
+//    chunks k = 0..B/(8*LPB)-1 at element offset 8*LPB*k + 8*t, so each load
+//    instruction of the wave reads whole 128-byte lines.  Within a block the
+//    element index is  e = 8*LPB*k + 8*t + j:  bits of j (register) and k
+//    (register) are butterflied in registers, bits of t across lanes.
+//  * Lane bits of t are lane-id bits 0, 1 and 3, the three that gfx9 DPP
+//    reaches in one instruction (quad_perm [1,0,3,2], quad_perm [2,3,0,1],
+//    row_ror:8); lane-id bits 2, 4, 5 select one of the 8 blocks a wave
+//    handles per step.
+//  * Cross-lane butterfly in one instruction per element:
+//    v <- v + sgn * v@partner  (v_fmac_f32_dpp, sgn = -1 on the upper lane).
+//    The upper lane then holds the negated butterfly output; partners always
+//    carry the same accumulated sign, so after all stages lane t holds
+//    (-1)^popcount(t) * (H x).  That sign is folded into the per-lane
+//    quantisation factor (compress) or output factor (decompress), so it
+//    costs nothing per element.
+//  * Fused single pass ([TACO] section 4.4.1 fuses the energy reduction and
+//    the post-rotation max into the one kernel): since Z = alpha H x / sqrt(B)
+//    and s = max|Z| / Q, the code argument is Z / s = Q * (H x) / max|H x|, so
+//    the kernel rotates the raw block R = H x, reduces sum x^2 and max |R|,
+//    and quantises v = R * (Q / max|R|).  alpha and s are computed once per
+//    block from the two reductions.
+//  * Stores: packed E4M3 (v_cvt_pk_fp8_f32, OCP E4M3FN on gfx950, round to
+//    nearest even), 8 codes per lane per chunk; alpha / s as float32
+//    side-buffers.  Decompress decodes with v_cvt_pk_f32_fp8 and rounds to
+//    bf16 with v_cvt_pk_bf16_f32.
+//  * Persistent grid-stride loop over wave-steps with the next step's loads
+//    issued before the current step is processed.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <math.h>
+#include <atomic>
+
+#include "taco.h"
+
+namespace {
+
+typedef float f2v __attribute__((ext_vector_type(2)));
+typedef __bf16 bf2v __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+constexpr int kWavesPerGroup = 4;
+constexpr int kGroup = kWave * kWavesPerGroup;
+
+template <int B>
+struct Geo {
+    static constexpr int LPB = (B >= 64) ? 8 : 4;  // lanes per block
+    static constexpr int EPL = B / LPB;            // elements per lane
+    static constexpr int CH = EPL / 8;             // 16-byte bf16 chunks per lane
+    static constexpr int BPW = kWave / LPB;        // blocks per wave-step
+    static constexpr int SPAN = LPB * 8;           // element stride between chunks
+    static_assert(B >= 32 && B <= 512 && (B & (B - 1)) == 0, "block size");
+};
+
+// ---------------------------------------------------------------- lanes ----
+
+template <int LPB>
+__device__ __forceinline__ int lane_sub(int lane) {   // t: position inside the block
+    return (LPB == 8) ? ((lane & 3) | ((lane >> 1) & 4)) : (lane & 3);
+}
+template <int LPB>
+__device__ __forceinline__ int lane_slot(int lane) {  // which block of the wave-step
+    return (LPB == 8) ? (((lane >> 2) & 1) | ((lane >> 3) & 6)) : (lane >> 2);
+}
+
+// DPP controls (gfx9 encoding) for the three lane-id bits of t.
+constexpr int kDppXor1 = 0xB1;   // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;   // quad_perm [2,3,0,1]
+constexpr int kDppXor8 = 0x128;  // row_ror:8
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+template <int LPB>
+__device__ __forceinline__ float block_sum(float v) {
+    v += dpp<kDppXor1>(v);
+    v += dpp<kDppXor2>(v);
+    if (LPB == 8) v += dpp<kDppXor8>(v);
+    return v;
+}
+template <int LPB>
+__device__ __forceinline__ float block_max(float v) {
+    v = fmaxf(v, dpp<kDppXor1>(v));
+    v = fmaxf(v, dpp<kDppXor2>(v));
+    if (LPB == 8) v = fmaxf(v, dpp<kDppXor8>(v));
+    return v;
+}
+
+// v[i] <- v[i] + sgn * v[i]@partner for 8 registers, partner given by the
+// DPP control.  The leading s_nop covers the gfx9 requirement of two wait
+// states between a VALU write of a VGPR and a DPP read of it; inside the
+// group every register read was written before the group started.
+#define TACO_FMAC_DPP8(CTRL, v, o, sgn)                                         \
+    asm volatile("s_nop 1\n\t"                                                  \
+                 "v_fmac_f32_dpp %0, %0, %8 " CTRL " row_mask:0xf bank_mask:0xf\n\t" \
+                 "v_fmac_f32_dpp %1, %1, %8 " CTRL " row_mask:0xf bank_mask:0xf\n\t" \
+                 "v_fmac_f32_dpp %2, %2, %8 " CTRL " row_mask:0xf bank_mask:0xf\n\t" \
+                 "v_fmac_f32_dpp %3, %3, %8 " CTRL " row_mask:0xf bank_mask:0xf\n\t" \
+                 "v_fmac_f32_dpp %4, %4, %8 " CTRL " row_mask:0xf bank_mask:0xf\n\t" \
+                 "v_fmac_f32_dpp %5, %5, %8 " CTRL " row_mask:0xf bank_mask:0xf\n\t" \
+                 "v_fmac_f32_dpp %6, %6, %8 " CTRL " row_mask:0xf bank_mask:0xf\n\t" \
+                 "v_fmac_f32_dpp %7, %7, %8 " CTRL " row_mask:0xf bank_mask:0xf"      \
+                 : "+v"(v[o + 0]), "+v"(v[o + 1]), "+v"(v[o + 2]), "+v"(v[o + 3]),   \
+                   "+v"(v[o + 4]), "+v"(v[o + 5]), "+v"(v[o + 6]), "+v"(v[o + 7])    \
+                 : "v"(sgn))
+
+// Unnormalised Walsh-Hadamard transform of the block held by LPB lanes
+// (EPL registers each), Sylvester order over e = 8*LPB*k + 8*t + j.  Must
+// run with every lane of the wave active.  On return lane t holds
+// (-1)^popcount(t) times its outputs.
+template <int LPB, int EPL>
+__device__ __forceinline__ void fwht_block(float (&v)[EPL], float sg1, float sg2, float sg8) {
+    constexpr int CH = EPL / 8;
+    // Bits of j: h = 1, 2, 4 inside each 8-element chunk.
+#pragma unroll
+    for (int h = 1; h < 8; h *= 2) {
+#pragma unroll
+        for (int i = 0; i < EPL; ++i) {
+            if ((i & h) == 0) {
+                float a = v[i], b = v[i + h];
+                v[i] = a + b;
+                v[i + h] = a - b;
+            }
+        }
+    }
+    // Bits of k: chunk pairs (c, c + hc).
+#pragma unroll
+    for (int hc = 1; hc < CH; hc *= 2) {
+#pragma unroll
+        for (int c = 0; c < CH; ++c) {
+            if ((c & hc) == 0) {
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    float a = v[8 * c + j], b = v[8 * (c + hc) + j];
+                    v[8 * c + j] = a + b;
+                    v[8 * (c + hc) + j] = a - b;
+                }
+            }
+        }
+    }
+    // Bits of t: across lanes.
+#pragma unroll
+    for (int o = 0; o < EPL; o += 8) TACO_FMAC_DPP8("quad_perm:[1,0,3,2]", v, o, sg1);
+#pragma unroll
+    for (int o = 0; o < EPL; o += 8) TACO_FMAC_DPP8("quad_perm:[2,3,0,1]", v, o, sg2);
+    if (LPB == 8) {
+#pragma unroll
+        for (int o = 0; o < EPL; o += 8) TACO_FMAC_DPP8("row_ror:8", v, o, sg8);
+    }
+}
+
+// Empty asm that forces each value to exist in a VGPR at this point of the
+// program (it emits no instruction).
+template <int N>
+__device__ __forceinline__ void pin_values(float (&v)[N]) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) asm volatile("" : "+v"(v[i]));
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+__device__ __forceinline__ void unpack8(const uint4 w, float *v) {
+    v[0] = bf16_lo(w.x); v[1] = bf16_hi(w.x);
+    v[2] = bf16_lo(w.y); v[3] = bf16_hi(w.y);
+    v[4] = bf16_lo(w.z); v[5] = bf16_hi(w.z);
+    v[6] = bf16_lo(w.w); v[7] = bf16_hi(w.w);
+}
+
+// Sum of squares of EPL values by a pairwise tree: each x^2 of a bf16 value
+// is exact in float32, every partial sum is rounded once, and the depth is
+// log2(EPL) (plus log2(LPB) across lanes), which bounds the relative error
+// of the block energy by about 9 * 2^-24.
+template <int EPL>
+__device__ __forceinline__ float sum_squares(const float (&v)[EPL]) {
+    float p[EPL / 2];
+#pragma unroll
+    for (int i = 0; i < EPL / 2; ++i) p[i] = fmaf(v[2 * i], v[2 * i], v[2 * i + 1] * v[2 * i + 1]);
+#pragma unroll
+    for (int w = EPL / 4; w >= 1; w /= 2) {
+#pragma unroll
+        for (int i = 0; i < w; ++i) p[i] = p[i] + p[i + w];
+    }
+    return p[0];
+}
+
+// max |v| over EPL values with v_max3_f32 and |.| source modifiers, two
+// values per instruction.  (fmaxf would first quiet each operand, which
+// costs an extra instruction per element; NaN handling is not needed here.)
+template <int EPL>
+__device__ __forceinline__ float max_abs(const float (&v)[EPL]) {
+    float m0 = 0.0f, m1 = 0.0f;
+#pragma unroll
+    for (int i = 0; i < EPL; i += 4) {
+        asm("v_max3_f32 %0, %0, |%1|, |%2|" : "+v"(m0) : "v"(v[i]), "v"(v[i + 1]));
+        asm("v_max3_f32 %0, %0, |%1|, |%2|" : "+v"(m1) : "v"(v[i + 2]), "v"(v[i + 3]));
+    }
+    return fmaxf(m0, m1);
+}
+
+// Packs 8 values into 8 E4M3 codes (little-endian: element j in byte j).
+__device__ __forceinline__ uint2 encode8(const float *v, float r) {
+    // fma(.., 0) maps an exact zero of either sign to +0 (code 0x00).
+    float q[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) q[j] = fmaf(v[j], r, 0.0f);
+    int lo = __builtin_amdgcn_cvt_pk_fp8_f32(q[0], q[1], 0, false);
+    lo = __builtin_amdgcn_cvt_pk_fp8_f32(q[2], q[3], lo, true);
+    int hi = __builtin_amdgcn_cvt_pk_fp8_f32(q[4], q[5], 0, false);
+    hi = __builtin_amdgcn_cvt_pk_fp8_f32(q[6], q[7], hi, true);
+    return make_uint2((uint32_t)lo, (uint32_t)hi);
+}
+
+__device__ __forceinline__ void decode8(const uint2 c, float *v) {
+    f2v a = __builtin_amdgcn_cvt_pk_f32_fp8((int)c.x, false);
+    f2v b = __builtin_amdgcn_cvt_pk_f32_fp8((int)c.x, true);
+    f2v d = __builtin_amdgcn_cvt_pk_f32_fp8((int)c.y, false);
+    f2v e = __builtin_amdgcn_cvt_pk_f32_fp8((int)c.y, true);
+    v[0] = a.x; v[1] = a.y; v[2] = b.x; v[3] = b.y;
+    v[4] = d.x; v[5] = d.y; v[6] = e.x; v[7] = e.y;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+    bf2v r = __builtin_convertvector((f2v){a, b}, bf2v);   // round to nearest even
+    return __builtin_bit_cast(uint32_t, r);
+}
+
+// 1 / sqrt(B) for the supported block sizes (double literals, rounded once
+// to float where used).
+constexpr double inv_sqrt(int b) {
+    return b == 32    ? 0.17677669529663688110
+           : b == 64  ? 0.125
+           : b == 128 ? 0.08838834764831844055
+           : b == 256 ? 0.0625
+                      : 0.04419417382415922028;
+}
+
+// Blocks whose energy reaches this are rescaled by 2^-64 before squaring so
+// that sum x^2 stays finite for every bf16 input.
+constexpr float kBigEnergy = 0x1p100f;
+constexpr float kBigShift = 0x1p-64f;
+constexpr float kBigUnshift = 0x1p-64f;   // alpha of the original block = alpha' * 2^-64
+// Blocks with max|R| below this get R and max|R| scaled by 2^64 before
+// Q / max|R| is formed, so that the quotient cannot overflow.
+constexpr float kTinyMax = 0x1p-96f;
+constexpr float kTinyShift = 0x1p64f;
+// Output factors below this are applied in two steps (see decompress).
+constexpr float kTinyOut = 0x1p-100f;
+constexpr float kOutShift = 0x1p64f;
+constexpr float kOutUnshift = 0x1p-64f;
+
+// ----------------------------------------------------------- compress -----
+
+template <int B>
+__global__ __launch_bounds__(kGroup) void compress_kernel(
+    const uint16_t *__restrict__ x, int64_t nblocks, float tau,
+    uint8_t *__restrict__ codes, float *__restrict__ alpha, float *__restrict__ scale) {
+    using G = Geo<B>;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int t = lane_sub<G::LPB>(lane);
+    const int g = lane_slot<G::LPB>(lane);
+    const float sg1 = (lane & 1) ? -1.0f : 1.0f;
+    const float sg2 = (lane & 2) ? -1.0f : 1.0f;
+    const float sg8 = (lane & 8) ? -1.0f : 1.0f;
+    const float lane_sign = (__popc(t) & 1) ? -1.0f : 1.0f;
+    // 1 / (sqrt(B) * Q_max), rounded once.
+    constexpr float kScaleFactor = (float)(inv_sqrt(B) / 448.0);
+    constexpr float kInvB = 1.0f / (float)B;
+
+    const int64_t nsteps = (nblocks + G::BPW - 1) / G::BPW;
+    const int64_t wave0 = (int64_t)blockIdx.x * kWavesPerGroup + (threadIdx.x >> 6);
+    const int64_t nwaves = (int64_t)gridDim.x * kWavesPerGroup;
+
+    // Slots past the last block (only in the final wave-step) re-read the
+    // last block, so every load is in bounds and no lane needs zero-filling;
+    // their results are never stored.
+    uint4 buf[G::CH];
+    auto load = [&](int64_t step) {
+        int64_t blk = step * G::BPW + g;
+        blk = blk < nblocks ? blk : nblocks - 1;
+        const uint4 *p = reinterpret_cast<const uint4 *>(x + blk * B + 8 * t);
+#pragma unroll
+        for (int k = 0; k < G::CH; ++k) buf[k] = p[k * (G::SPAN / 8)];
+    };
+
+    if (wave0 < nsteps) load(wave0);
+    for (int64_t step = wave0; step < nsteps; step += nwaves) {
+        float v[G::EPL];
+#pragma unroll
+        for (int k = 0; k < G::CH; ++k) unpack8(buf[k], &v[8 * k]);
+        // Materialise the unpacked values here, so that the prefetch below
+        // can reuse buf's registers instead of copying them.
+        pin_values(v);
+        if (step + nwaves < nsteps) load(step + nwaves);
+
+        const int64_t blk = step * G::BPW + g;
+        const bool active = blk < nblocks;
+
+        // [TACO] Eq. 6: block energy (raw second moment).
+        float energy = block_sum<G::LPB>(sum_squares<G::EPL>(v));
+        float unshift = 1.0f;
+        if (__builtin_expect(energy >= kBigEnergy, 0)) {
+            // Huge block: work on x * 2^-64 (exact), undo it in alpha.
+#pragma unroll
+            for (int i = 0; i < G::EPL; ++i) v[i] *= kBigShift;
+            energy = block_sum<G::LPB>(sum_squares<G::EPL>(v));
+            unshift = kBigUnshift;
+        }
+        // [TACO] Eq. 6-7.
+        const float sigma = sqrtf(energy * kInvB + TACO_EPS);
+        const float a = tau / sigma;
+
+        // [TACO] Eq. 8 without its constant factors: R = H x.
+        fwht_block<G::LPB, G::EPL>(v, sg1, sg2, sg8);
+
+        // [TACO] Eq. 9: max|Z| = alpha max|R| / sqrt(B).
+        float m = block_max<G::LPB>(max_abs<G::EPL>(v));
+        const float s = a * m * kScaleFactor;
+        if (__builtin_expect(m < kTinyMax && m > 0.0f, 0)) {
+#pragma unroll
+            for (int i = 0; i < G::EPL; ++i) v[i] *= kTinyShift;
+            m *= kTinyShift;
+        }
+        // [TACO] Eq. 10: Z / s = Q * R / max|R|.
+        const float r = (m > 0.0f) ? (TACO_QMAX / m) * lane_sign : 0.0f;
+
+        if (active) {
+            uint8_t *cq = codes + blk * B + 8 * t;
+#pragma unroll
+            for (int k = 0; k < G::CH; ++k)
+                *reinterpret_cast<uint2 *>(cq + k * G::SPAN) = encode8(&v[8 * k], r);
+            if (t == 0) {
+                alpha[blk] = a * unshift;
+                scale[blk] = s;
+            }
+        }
+    }
+}
+
+// --------------------------------------------------------- decompress -----
+
+enum class Out { kBf16, kAccumulate };
+
+template <int B, Out MODE>
+__global__ __launch_bounds__(kGroup) void decompress_kernel(
+    const uint8_t *__restrict__ codes, const float *__restrict__ alpha,
+    const float *__restrict__ scale, int64_t nblocks, uint16_t *__restrict__ y,
+    float *__restrict__ acc) {
+    using G = Geo<B>;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int t = lane_sub<G::LPB>(lane);
+    const int g = lane_slot<G::LPB>(lane);
+    const float sg1 = (lane & 1) ? -1.0f : 1.0f;
+    const float sg2 = (lane & 2) ? -1.0f : 1.0f;
+    const float sg8 = (lane & 8) ? -1.0f : 1.0f;
+    const float lane_sign = (__popc(t) & 1) ? -1.0f : 1.0f;
+    // 1 / sqrt(B), rounded once.
+    constexpr float kInvSqrtB = (float)inv_sqrt(B);
+
+    const int64_t nsteps = (nblocks + G::BPW - 1) / G::BPW;
+    const int64_t wave0 = (int64_t)blockIdx.x * kWavesPerGroup + (threadIdx.x >> 6);
+    const int64_t nwaves = (int64_t)gridDim.x * kWavesPerGroup;
+
+    // Slots past the last block re-read the last block (never stored).
+    uint2 buf[G::CH];
+    float a_buf = 1.0f, s_buf = 0.0f;
+    auto load = [&](int64_t step) {
+        int64_t blk = step * G::BPW + g;
+        blk = blk < nblocks ? blk : nblocks - 1;
+        const uint2 *p = reinterpret_cast<const uint2 *>(codes + blk * B + 8 * t);
+#pragma unroll
+        for (int k = 0; k < G::CH; ++k) buf[k] = p[k * (G::SPAN / 8)];
+        a_buf = alpha[blk];
+        s_buf = scale[blk];
+    };
+
+    if (wave0 < nsteps) load(wave0);
+    for (int64_t step = wave0; step < nsteps; step += nwaves) {
+        float v[G::EPL];
+#pragma unroll
+        for (int k = 0; k < G::CH; ++k) decode8(buf[k], &v[8 * k]);   // Eq. 11 (before * s)
+        float a = a_buf, s = s_buf;
+        pin_values(v);
+        asm volatile("" : "+v"(a), "+v"(s));
+        if (step + nwaves < nsteps) load(step + nwaves);
+
+        const int64_t blk = step * G::BPW + g;
+        const bool active = blk < nblocks;
+
+        fwht_block<G::LPB, G::EPL>(v, sg1, sg2, sg8);                // Eq. 12 (unnormalised)
+        // Eq. 11-13 constant factors: s / sqrt(B) / alpha, with the lane sign.
+        const float f = ((s * kInvSqrtB) / a) * lane_sign;
+        if (__builtin_expect(s > 0.0f && fabsf(f) < kTinyOut, 0)) {
+            // The factor would lose bits as a float32 subnormal: apply it as
+            // (2^64 f) then 2^-64, so that only the final product rounds.
+            const float fs = (((s * kOutShift) * kInvSqrtB) / a) * lane_sign;
+#pragma unroll
+            for (int i = 0; i < G::EPL; ++i) v[i] = (v[i] * fs) * kOutUnshift;
+        } else {
+#pragma unroll
+            for (int i = 0; i < G::EPL; ++i) v[i] *= f;
+        }
+
+        if (active) {
+            const int64_t e0 = blk * B + 8 * t;
+            if (MODE == Out::kBf16) {
+#pragma unroll
+                for (int k = 0; k < G::CH; ++k) {
+                    const float *w = &v[8 * k];
+                    uint4 o;
+                    o.x = pack_bf16x2(w[0], w[1]);
+                    o.y = pack_bf16x2(w[2], w[3]);
+                    o.z = pack_bf16x2(w[4], w[5]);
+                    o.w = pack_bf16x2(w[6], w[7]);
+                    *reinterpret_cast<uint4 *>(y + e0 + k * G::SPAN) = o;
+                }
+            } else {
+#pragma unroll
+                for (int k = 0; k < G::CH; ++k) {
+                    const float *w = &v[8 * k];
+                    float4 *pa = reinterpret_cast<float4 *>(acc + e0 + k * G::SPAN);
+                    float4 p0 = pa[0], p1 = pa[1];
+                    p0.x += w[0]; p0.y += w[1]; p0.z += w[2]; p0.w += w[3];
+                    p1.x += w[4]; p1.y += w[5]; p1.z += w[6]; p1.w += w[7];
+                    pa[0] = p0;
+                    pa[1] = p1;
+                }
+            }
+        }
+    }
+}
+
+// ------------------------------------------------------------- codec ------
+
+__global__ __launch_bounds__(kGroup) void e4m3_encode_kernel(const float *__restrict__ x, int64_t n,
+                                                             uint8_t *__restrict__ codes) {
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i * 4 < n; i += stride) {
+        const int64_t e = i * 4;
+        float q[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) q[j] = (e + j < n) ? x[e + j] : 0.0f;
+        int w = __builtin_amdgcn_cvt_pk_fp8_f32(q[0], q[1], 0, false);
+        w = __builtin_amdgcn_cvt_pk_fp8_f32(q[2], q[3], w, true);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            if (e + j < n) codes[e + j] = (uint8_t)((uint32_t)w >> (8 * j));
+    }
+}
+
+__global__ __launch_bounds__(kGroup) void e4m3_decode_kernel(const uint8_t *__restrict__ codes,
+                                                             int64_t n, float *__restrict__ out) {
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i * 4 < n; i += stride) {
+        const int64_t e = i * 4;
+        uint32_t w = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            if (e + j < n) w |= (uint32_t)codes[e + j] << (8 * j);
+        f2v a = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
+        f2v b = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
+        const float r[4] = {a.x, a.y, b.x, b.y};
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            if (e + j < n) out[e + j] = r[j];
+    }
+}
+
+// -------------------------------------------------------------- host ------
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+bool overlap(const void *a, size_t na, const void *b, size_t nb) {
+    if (na == 0 || nb == 0) return false;
+    const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
+    return a0 < b0 + nb && b0 < a0 + na;
+}
+
+bool valid_block(int32_t block) {
+    return block == 32 || block == 64 || block == 128 || block == 256 || block == 512;
+}
+
+// N = tokens * hidden, or -1 on a bad shape (negative, zero hidden, overflow).
+int64_t numel(int64_t tokens, int64_t hidden) {
+    if (tokens < 0 || hidden <= 0) return -1;
+    if (tokens > 0 && hidden > (INT64_C(1) << 60) / tokens) return -1;
+    return tokens * hidden;
+}
+
+int cu_count() {
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 256;
+    if (dev >= 0 && dev < 64) {
+        int c = cache[dev].load(std::memory_order_relaxed);
+        if (c > 0) return c;
+    }
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+        n = 256;
+    if (dev >= 0 && dev < 64) cache[dev].store(n, std::memory_order_relaxed);
+    return n;
+}
+
+// Persistent grid: enough work-groups to cover every wave-step once, capped
+// at kGroupsPerCU groups per compute unit.
+constexpr int kGroupsPerCU = 8;
+
+unsigned grid_for(int64_t nsteps) {
+    const int64_t need = (nsteps + kWavesPerGroup - 1) / kWavesPerGroup;
+    const int64_t cap = (int64_t)cu_count() * kGroupsPerCU;
+    const int64_t g = need < cap ? need : cap;
+    return (unsigned)(g > 0 ? g : 1);
+}
+
+template <typename... Args>
+taco_status launch(const void *fn, unsigned grid, hipStream_t stream, Args... args) {
+    void *ptrs[] = {static_cast<void *>(&args)...};
+    const hipError_t err = hipLaunchKernel(fn, dim3(grid), dim3(kGroup), ptrs, 0, stream);
+    return err == hipSuccess ? TACO_OK : TACO_ERR_HIP;
+}
+
+template <int B>
+taco_status compress_launch(const uint16_t *x, int64_t nblocks, float tau, uint8_t *codes,
+                            float *alpha, float *scale, hipStream_t stream) {
+    const int64_t nsteps = (nblocks + Geo<B>::BPW - 1) / Geo<B>::BPW;
+    return launch(reinterpret_cast<const void *>(&compress_kernel<B>), grid_for(nsteps), stream, x,
+                  nblocks, tau, codes, alpha, scale);
+}
+
+template <int B, Out MODE>
+taco_status decompress_launch(const uint8_t *codes, const float *alpha, const float *scale,
+                              int64_t nblocks, uint16_t *y, float *acc, hipStream_t stream) {
+    const int64_t nsteps = (nblocks + Geo<B>::BPW - 1) / Geo<B>::BPW;
+    return launch(reinterpret_cast<const void *>(&decompress_kernel<B, MODE>), grid_for(nsteps),
+                  stream, codes, alpha, scale, nblocks, y, acc);
+}
+
+// Shared validation of the decompress-side calls.
+taco_status check_receiver(const uint8_t *codes, const float *alpha, const float *scale,
+                           int64_t tokens, int64_t hidden, int32_t block, const void *out,
+                           size_t out_elem, int64_t *nblocks_out) {
+    const int64_t n = numel(tokens, hidden);
+    if (n < 0) return TACO_ERR_SHAPE;
+    if (!valid_block(block)) return TACO_ERR_BLOCK;
+    if (n % block) return TACO_ERR_SHAPE;
+    *nblocks_out = n / block;
+    if (n == 0) return TACO_OK;
+    if (!codes || !alpha || !scale || !out) return TACO_ERR_NULL;
+    if (!aligned(codes, 16) || !aligned(out, 16) || !aligned(alpha, 4) || !aligned(scale, 4))
+        return TACO_ERR_ALIGN;
+    const size_t nb = (size_t)(n / block) * sizeof(float);
+    const size_t no = (size_t)n * out_elem;
+    if (overlap(out, no, codes, (size_t)n) || overlap(out, no, alpha, nb) || overlap(out, no, scale, nb))
+        return TACO_ERR_ALIAS;
+    return TACO_OK;
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------- C ABI ---
+
+extern "C" {
+
+int64_t taco_num_blocks(int64_t tokens, int64_t hidden, int32_t block) {
+    const int64_t n = numel(tokens, hidden);
+    if (n < 0 || !valid_block(block) || n % block) return -1;
+    return n / block;
+}
+
+taco_status taco_compress(const uint16_t *x_bf16, int64_t tokens, int64_t hidden, int32_t block,
+                          float target_energy, uint8_t *codes_e4m3, float *alpha, float *scale,
+                          hipStream_t stream) {
+    const int64_t n = numel(tokens, hidden);
+    if (n < 0) return TACO_ERR_SHAPE;
+    if (!valid_block(block)) return TACO_ERR_BLOCK;
+    if (n % block) return TACO_ERR_SHAPE;
+    if (!(target_energy > 0.0f) || !(target_energy <= TACO_MAX_TARGET_ENERGY)) return TACO_ERR_PARAM;
+    if (n == 0) return TACO_OK;
+    if (!x_bf16 || !codes_e4m3 || !alpha || !scale) return TACO_ERR_NULL;
+    if (!aligned(x_bf16, 16) || !aligned(codes_e4m3, 16) || !aligned(alpha, 4) || !aligned(scale, 4))
+        return TACO_ERR_ALIGN;
+    const int64_t m = n / block;
+    const size_t nx = (size_t)n * 2, nc = (size_t)n, nb = (size_t)m * sizeof(float);
+    if (overlap(codes_e4m3, nc, x_bf16, nx) || overlap(alpha, nb, x_bf16, nx) ||
+        overlap(scale, nb, x_bf16, nx) || overlap(codes_e4m3, nc, alpha, nb) ||
+        overlap(codes_e4m3, nc, scale, nb) || overlap(alpha, nb, scale, nb))
+        return TACO_ERR_ALIAS;
+    switch (block) {
+        case 32: return compress_launch<32>(x_bf16, m, target_energy, codes_e4m3, alpha, scale, stream);
+        case 64: return compress_launch<64>(x_bf16, m, target_energy, codes_e4m3, alpha, scale, stream);
+        case 128: return compress_launch<128>(x_bf16, m, target_energy, codes_e4m3, alpha, scale, stream);
+        case 256: return compress_launch<256>(x_bf16, m, target_energy, codes_e4m3, alpha, scale, stream);
+        default: return compress_launch<512>(x_bf16, m, target_energy, codes_e4m3, alpha, scale, stream);
+    }
+}
+
+taco_status taco_decompress(const uint8_t *codes_e4m3, const float *alpha, const float *scale,
+                            int64_t tokens, int64_t hidden, int32_t block, uint16_t *y_bf16,
+                            hipStream_t stream) {
+    int64_t m = 0;
+    taco_status st = check_receiver(codes_e4m3, alpha, scale, tokens, hidden, block, y_bf16, 2, &m);
+    if (st != TACO_OK || m == 0) return st;
+    constexpr Out O = Out::kBf16;
+    switch (block) {
+        case 32: return decompress_launch<32, O>(codes_e4m3, alpha, scale, m, y_bf16, nullptr, stream);
+        case 64: return decompress_launch<64, O>(codes_e4m3, alpha, scale, m, y_bf16, nullptr, stream);
+        case 128: return decompress_launch<128, O>(codes_e4m3, alpha, scale, m, y_bf16, nullptr, stream);
+        case 256: return decompress_launch<256, O>(codes_e4m3, alpha, scale, m, y_bf16, nullptr, stream);
+        default: return decompress_launch<512, O>(codes_e4m3, alpha, scale, m, y_bf16, nullptr, stream);
+    }
+}
+
+taco_status taco_decompress_accumulate(const uint8_t *codes_e4m3, const float *alpha,
+                                       const float *scale, int64_t tokens, int64_t hidden,
+                                       int32_t block, float *acc_f32, hipStream_t stream) {
+    int64_t m = 0;
+    taco_status st = check_receiver(codes_e4m3, alpha, scale, tokens, hidden, block, acc_f32, 4, &m);
+    if (st != TACO_OK || m == 0) return st;
+    constexpr Out O = Out::kAccumulate;
+    switch (block) {
+        case 32: return decompress_launch<32, O>(codes_e4m3, alpha, scale, m, nullptr, acc_f32, stream);
+        case 64: return decompress_launch<64, O>(codes_e4m3, alpha, scale, m, nullptr, acc_f32, stream);
+        case 128: return decompress_launch<128, O>(codes_e4m3, alpha, scale, m, nullptr, acc_f32, stream);
+        case 256: return decompress_launch<256, O>(codes_e4m3, alpha, scale, m, nullptr, acc_f32, stream);
+        default: return decompress_launch<512, O>(codes_e4m3, alpha, scale, m, nullptr, acc_f32, stream);
+    }
+}
+
+taco_status taco_e4m3_encode(const float *x, int64_t n, uint8_t *codes, hipStream_t stream) {
+    if (n < 0) return TACO_ERR_SHAPE;
+    if (n == 0) return TACO_OK;
+    if (!x || !codes) return TACO_ERR_NULL;
+    if (!aligned(x, 16) || !aligned(codes, 16)) return TACO_ERR_ALIGN;
+    if (overlap(codes, (size_t)n, x, (size_t)n * 4)) return TACO_ERR_ALIAS;
+    const int64_t items = (n + 3) / 4;
+    const int64_t need = (items + kGroup - 1) / kGroup;
+    const unsigned grid = (unsigned)(need < 65536 ? need : 65536);
+    return launch(reinterpret_cast<const void *>(&e4m3_encode_kernel), grid, stream, x, n, codes);
+}
+
+taco_status taco_e4m3_decode(const uint8_t *codes, int64_t n, float *out, hipStream_t stream) {
+    if (n < 0) return TACO_ERR_SHAPE;
+    if (n == 0) return TACO_OK;
+    if (!codes || !out) return TACO_ERR_NULL;
+    if (!aligned(out, 16) || !aligned(codes, 16)) return TACO_ERR_ALIGN;
+    if (overlap(out, (size_t)n * 4, codes, (size_t)n)) return TACO_ERR_ALIAS;
+    const int64_t items = (n + 3) / 4;
+    const int64_t need = (items + kGroup - 1) / kGroup;
+    const unsigned grid = (unsigned)(need < 65536 ? need : 65536);
+    return launch(reinterpret_cast<const void *>(&e4m3_decode_kernel), grid, stream, codes, n, out);
+}
+
+const char *taco_status_string(taco_status status) {
+    switch (status) {
+        case TACO_OK: return "ok";
+        case TACO_ERR_NULL: return "a required pointer is NULL";
+        case TACO_ERR_SHAPE: return "bad shape: tokens < 0, hidden <= 0, or N not a multiple of the block";
+        case TACO_ERR_BLOCK: return "block size must be 32, 64, 128, 256 or 512";
+        case TACO_ERR_PARAM: return "target energy must be finite and in (0, 1e20]";
+        case TACO_ERR_ALIGN: return "tensors must be 16-byte aligned, alpha and scale 4-byte aligned";
+        case TACO_ERR_ALIAS: return "an output buffer overlaps an input or another output";
+        case TACO_ERR_HIP: return "the HIP runtime refused the kernel launch";
+    }
+    return "unknown status";
+}
+
+}  // extern "C"

@@ -1,0 +1,141 @@
+/*
+ * libtaco -- the TACO fused FP8 compression operator for AMD Instinct MI355X
+ * (gfx950), as a C ABI.
+ *
+ * The operator is the one described on the page "TACO: Efficient Communication
+ * Compression of Intermediate Tensors for Scalable Tensor-Parallel LLM
+ * Training" (cited below as [TACO]):
+ *
+ *   sender   (section 4.2.2 Eq. 5-8, section 4.3 Eq. 9-10, Algorithm 1, sender
+ *             side): split the flattened tensor into contiguous blocks of B
+ *             elements; per block compute the RMS amplitude
+ *             sigma = sqrt(mean(G^2) + eps) and alpha = tau / sigma; rotate the
+ *             rescaled block with the orthonormal Walsh-Hadamard transform,
+ *             Z = H_B (alpha G) / sqrt(B); take s = max|Z| / Q_max and emit the
+ *             E4M3 codes of Z / s.
+ *   receiver (section 4.3 Eq. 11-13, Algorithm 1, receiver side):
+ *             G' = H_B (decode(q) * s) / sqrt(B) / alpha.
+ *   reduce   (section 4.4.2: the reduce-scatter phase of the two-shot
+ *             all-reduce ends in one local reduction of the received
+ *             payloads): acc += G'.
+ *
+ * Conventions shared by every call below
+ *   - All tensor pointers are DEVICE pointers (any device allocation, e.g. a
+ *     torch tensor's data pointer), owned by the caller; the library
+ *     allocates nothing and keeps no state between calls.
+ *   - A [tokens, hidden] tensor is row-major and is processed as its
+ *     flattened vector of N = tokens * hidden elements; block k covers
+ *     elements [k*B, (k+1)*B).  N must be a multiple of B; blocks may cross
+ *     rows.
+ *   - bf16 tensors are passed as uint16_t bit patterns.
+ *   - Calls are asynchronous on `stream` (NULL = the null stream).  The
+ *     returned status covers argument validation and the kernel launch only.
+ *     On any error nothing is launched and nothing is written.
+ *   - N == 0 is a no-op that returns TACO_OK (pointers may then be NULL).
+ *   - Inputs must be finite.  Blocks whose RMS exceeds ~2^126 / target_energy
+ *     get a subnormal float32 alpha (less precise); non-finite inputs give
+ *     unspecified codes and scalars (but never out-of-bounds accesses).
+ *   - Thread-safe: calls share no mutable state (a per-device compute-unit
+ *     count is cached once).  Calls on different streams may overlap if
+ *     their buffers do not.
+ */
+#ifndef TACO_H
+#define TACO_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Largest finite OCP E4M3 ("E4M3FN") value: Q_max of [TACO] Eq. 9. */
+#define TACO_QMAX 448.0f
+
+/* epsilon of [TACO] Eq. 6, inside the square root ("a small constant
+ * ensuring numerical stability for near-zero blocks"; its value is not
+ * given).  Far below the energy of any realistic block, yet it keeps alpha
+ * finite (tau * 1e10) for an all-zero block. */
+#define TACO_EPS 1e-20f
+
+/* Supported block sizes B.  [TACO] Table 2 sweeps 32..512; 256 is its best. */
+#define TACO_MIN_BLOCK 32
+#define TACO_MAX_BLOCK 512
+
+/* Largest accepted target energy tau: keeps alpha = tau / sigma finite for
+ * an all-zero block (sigma = sqrt(eps)). */
+#define TACO_MAX_TARGET_ENERGY 1e20f
+
+typedef enum {
+    TACO_OK = 0,
+    TACO_ERR_NULL = 1,   /* a required pointer is NULL                          */
+    TACO_ERR_SHAPE = 2,  /* tokens < 0, hidden <= 0, N overflows, N % block != 0 */
+    TACO_ERR_BLOCK = 3,  /* block is not one of 32, 64, 128, 256, 512            */
+    TACO_ERR_PARAM = 4,  /* target_energy not finite or outside (0, 1e20]        */
+    TACO_ERR_ALIGN = 5,  /* a tensor is not 16-byte aligned, or alpha / scale
+                            not 4-byte aligned                                  */
+    TACO_ERR_ALIAS = 6,  /* an output buffer overlaps an input or another output */
+    TACO_ERR_HIP = 7     /* the HIP runtime refused the launch                  */
+} taco_status;
+
+/* Number of blocks M = tokens * hidden / block, or -1 if the shape or block
+ * is invalid (same rules as the calls below). */
+int64_t taco_num_blocks(int64_t tokens, int64_t hidden, int32_t block);
+
+/*
+ * Compress ([TACO] Eq. 5-10, Algorithm 1, sender side).
+ *   x_bf16      [tokens*hidden] bf16 input, 16-byte aligned.
+ *   block       B in {32, 64, 128, 256, 512}.
+ *   target_energy  tau of Eq. 7 (the codes do not depend on it; alpha and s
+ *               scale with it).
+ *   codes_e4m3  [tokens*hidden] output: E4M3 code of element i, same order
+ *               as x; 16-byte aligned.  Exact zeros of Z encode as 0x00.
+ *   alpha       [M] float32 output: alpha_k of Eq. 7.
+ *   scale       [M] float32 output: s_k of Eq. 9 (0 for an all-zero block).
+ * Outputs must not overlap x or each other.
+ */
+taco_status taco_compress(const uint16_t *x_bf16, int64_t tokens, int64_t hidden,
+                          int32_t block, float target_energy, uint8_t *codes_e4m3,
+                          float *alpha, float *scale, hipStream_t stream);
+
+/*
+ * Decompress ([TACO] Eq. 11-13, Algorithm 1, receiver side): y = bf16(G'),
+ * rounded to nearest even.  codes / alpha / scale as produced by
+ * taco_compress for the same shape and block; y_bf16 [tokens*hidden] is
+ * 16-byte aligned and must not overlap the inputs.
+ */
+taco_status taco_decompress(const uint8_t *codes_e4m3, const float *alpha,
+                            const float *scale, int64_t tokens, int64_t hidden,
+                            int32_t block, uint16_t *y_bf16, hipStream_t stream);
+
+/*
+ * Decompress and accumulate ([TACO] Eq. 11-13 followed by the local
+ * reduction of section 4.4.2): acc_f32 += G' (G' in float32, one float32
+ * addition per element).  acc_f32 [tokens*hidden] is read and written,
+ * 16-byte aligned, and must not overlap the inputs.  Several payloads are
+ * summed by calling it once per payload on the same stream.
+ */
+taco_status taco_decompress_accumulate(const uint8_t *codes_e4m3, const float *alpha,
+                                       const float *scale, int64_t tokens,
+                                       int64_t hidden, int32_t block, float *acc_f32,
+                                       hipStream_t stream);
+
+/*
+ * The E4M3 conversions the kernels above use (Cvt_FP8 of [TACO] Eq. 10 and
+ * Cvt_FP32 of Eq. 11), exposed element-wise so that they can be checked
+ * exhaustively.  encode: round to nearest even, OCP E4M3FN; inputs of
+ * magnitude 464 or more are outside its contract (the operator never
+ * produces them).  decode: exact.  n >= 0 elements; x / out 16-byte aligned,
+ * codes 16-byte aligned; outputs must not overlap inputs.
+ */
+taco_status taco_e4m3_encode(const float *x, int64_t n, uint8_t *codes, hipStream_t stream);
+taco_status taco_e4m3_decode(const uint8_t *codes, int64_t n, float *out, hipStream_t stream);
+
+/* Static description of a status code (never NULL). */
+const char *taco_status_string(taco_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TACO_H */

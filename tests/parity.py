@@ -1,0 +1,102 @@
+"""Comparison of the HIP path against the oracle, with the tolerances of the
+contract:
+
+* E4M3 codes identical, except flips to the adjacent code where the oracle's
+  argument Z/s sits at a rounding tie (within the float32 error the kernel's
+  evaluation order can carry), on at most 1e-5 of the elements;
+* alpha and s within 1e-6 relative;
+* reconstructions within 1e-3 relative RMS of the oracle's reconstruction.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+import oracle
+import synth
+
+FLIP_RATE = 1e-5
+SCALAR_RTOL = 1e-6
+RECON_RTOL = 1e-3
+QMAX = 448.0
+U32 = 2.0 ** -24          # float32 unit roundoff
+
+
+def rel_rms(a, b) -> float:
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    den = np.linalg.norm(b)
+    return float(np.linalg.norm(a - b) / den) if den > 0 else float(np.linalg.norm(a))
+
+
+def max_rel(a, b) -> float:
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    den = np.maximum(np.abs(b), np.finfo(np.float64).tiny)
+    d = np.where(a == b, 0.0, np.abs(a - b) / den)
+    return float(d.max()) if d.size else 0.0
+
+
+def _tie_ok(x_block, code_gpu, code_or, j, B) -> tuple[bool, str]:
+    """Is element j's flip a flip between adjacent codes at a rounding tie?"""
+    _, _, z = oracle.ash_block(x_block, B)
+    s64 = np.max(np.abs(z)) / QMAX
+    v = float(np.float32(z[j] / s64))
+    cg, co = int(code_gpu), int(code_or)
+    dg, do = oracle.e4m3_decode(np.array([cg, co], np.uint8))
+    if (cg & 0x80) != (co & 0x80) and not (dg == 0 and do == 0):
+        # Sign differs: only possible when both round to zero.
+        return False, f"sign flip {cg:#x} vs {co:#x} (v={v})"
+    if abs((cg & 0x7F) - (co & 0x7F)) > 1:
+        return False, f"codes {cg:#x} vs {co:#x} not adjacent (v={v})"
+    mid = 0.5 * (abs(dg) + abs(do))
+    # Bound on the kernel's float32 error in v: the FWHT accumulates at most
+    # log2(B) roundings of partial sums bounded by sum|x|, then two roundings
+    # in the quotient and the product.
+    xs = synth.bits_to_f32(x_block).astype(np.float64)
+    m = np.max(np.abs(oracle.fwht(xs)))
+    bound = QMAX * np.log2(B) * U32 * np.sum(np.abs(xs)) / m + 4 * U32 * abs(v) if m > 0 else 0
+    if abs(abs(v) - mid) > bound:
+        return False, f"not at a tie: |v|={abs(v)!r}, midpoint={mid!r}, bound={bound:.3g}"
+    return True, ""
+
+
+def compare_compress(x_bits, B, codes, alpha, scale, tau=1.0, max_flip_checks=200):
+    """Check the GPU's (codes, alpha, scale) of x_bits against the oracle.
+    Returns a dict of statistics; raises AssertionError on a violation."""
+    x_bits = np.ascontiguousarray(x_bits).reshape(-1)
+    codes = np.ascontiguousarray(codes).reshape(-1)
+    o_codes, o_alpha, o_scale = oracle.compress(x_bits, B, tau)
+    o_codes = o_codes.reshape(-1)
+    bad = np.nonzero(codes != o_codes)[0]
+    n = x_bits.size
+    assert bad.size <= max(FLIP_RATE * n, 0), \
+        f"{bad.size} code mismatches in {n} elements (allowed {FLIP_RATE * n:.1f})"
+    for i in bad[:max_flip_checks]:
+        k, j = divmod(int(i), B)
+        ok, why = _tie_ok(x_bits[k * B:(k + 1) * B], codes[i], o_codes[i], j, B)
+        assert ok, f"element {i} (block {k}): {why}"
+    ea = max_rel(alpha, o_alpha)
+    es = max_rel(scale, o_scale)
+    assert ea <= SCALAR_RTOL, f"alpha max rel err {ea:.3g}"
+    assert es <= SCALAR_RTOL, f"scale max rel err {es:.3g}"
+    return {"flips": int(bad.size), "n": int(n), "alpha_rel": ea, "scale_rel": es,
+            "oracle": (o_codes, o_alpha, o_scale)}
+
+
+def compare_decompress(y_bits, o_codes, o_alpha, o_scale, B):
+    """GPU bf16 output y_bits (from the oracle's codes) against the oracle's
+    bf16 output (relative RMS) and against its exact reconstruction
+    (element-wise, one bf16 rounding plus the kernel's float32 error)."""
+    ref = oracle.reconstruct_f64(o_codes, o_alpha, o_scale, B).reshape(-1)
+    ref_bf16 = synth.bits_to_f32(oracle.decompress(o_codes, o_alpha, o_scale, B)).reshape(-1)
+    y = synth.bits_to_f32(np.asarray(y_bits).reshape(-1)).astype(np.float64)
+    r = rel_rms(y, ref_bf16)
+    assert r <= RECON_RTOL, f"decompress rel RMS {r:.3g}"
+    # Element-wise: within one bf16 step of the exact value, plus the
+    # kernel's float32 rounding relative to the block's largest output.
+    blk_max = np.repeat(np.max(np.abs(ref.reshape(-1, B)), axis=1), B)
+    # (bf16 subnormals, below 2^-126, are spaced 2^-133 apart.)
+    tol = 2.0 ** -8 * np.abs(ref) + 2.0 ** -16 * blk_max + 2.0 ** -133
+    worst = float(np.max(np.abs(y - ref) - tol))
+    assert worst <= 0, f"decompress element error exceeds tolerance by {worst:.3g}"
+    return {"rel_rms": r}

@@ -1,0 +1,142 @@
+"""The C ABI without a GPU: the library loads, exports every function the
+header declares, and rejects every bad argument before touching the device."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from conftest import ROOT
+
+HEADER = os.path.join(ROOT, "include", "taco.h")
+LIB = os.path.join(ROOT, "gradients_taco_compress_amd", "libtaco.so")
+
+OK, NULL, SHAPE, BLOCK, PARAM, ALIGN, ALIAS, HIP = range(8)
+A = 1 << 20          # fake, 16-byte aligned "device" addresses: never dereferenced
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(taco_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        pytest.fail("libtaco.so is not built; run __graft_entry__.build()")
+    L = ctypes.CDLL(LIB)
+    P, I64, I32, F32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_float
+    L.taco_num_blocks.argtypes = [I64, I64, I32]
+    L.taco_num_blocks.restype = I64
+    L.taco_compress.argtypes = [P, I64, I64, I32, F32, P, P, P, P]
+    L.taco_decompress.argtypes = [P, P, P, I64, I64, I32, P, P]
+    L.taco_decompress_accumulate.argtypes = [P, P, P, I64, I64, I32, P, P]
+    L.taco_e4m3_encode.argtypes = [P, I64, P, P]
+    L.taco_e4m3_decode.argtypes = [P, I64, P, P]
+    L.taco_status_string.argtypes = [ctypes.c_int]
+    L.taco_status_string.restype = ctypes.c_char_p
+    return L
+
+
+def test_every_declared_function_is_exported(lib):
+    names = declared_functions()
+    assert len(names) == 7, names
+    for n in names:
+        assert hasattr(lib, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True).stdout
+    exported = set(re.findall(r" T (taco_\w+)", out))
+    assert exported == set(names), exported ^ set(names)
+
+
+def test_binding_names_match_header():
+    import importlib.util
+    spec = importlib.util.find_spec("gradients_taco_compress_amd")
+    assert spec is not None
+    import gradients_taco_compress_amd as taco
+    assert set(taco.EXPORTS) == set(declared_functions())
+    for n in declared_functions():
+        assert callable(getattr(taco, n))
+
+
+def test_status_strings(lib):
+    for s in range(8):
+        assert lib.taco_status_string(s)
+    assert lib.taco_status_string(99) == b"unknown status"
+
+
+def test_num_blocks(lib):
+    assert lib.taco_num_blocks(8192, 2560, 128) == 8192 * 2560 // 128
+    assert lib.taco_num_blocks(0, 1024, 256) == 0
+    assert lib.taco_num_blocks(3, 96, 128) == -1          # 288 % 128 != 0
+    assert lib.taco_num_blocks(4, 96, 128) == 3          # blocks may cross rows
+    assert lib.taco_num_blocks(-1, 128, 128) == -1
+    assert lib.taco_num_blocks(1, 0, 128) == -1
+    assert lib.taco_num_blocks(1, 1024, 100) == -1
+    assert lib.taco_num_blocks(1 << 40, 1 << 40, 128) == -1   # overflow
+
+
+def compress(lib, x=A, tokens=4, hidden=256, block=128, tau=1.0,
+             codes=2 * A, alpha=3 * A, scale=4 * A):
+    return lib.taco_compress(x, tokens, hidden, block, tau, codes, alpha, scale, None)
+
+
+def test_compress_validation(lib):
+    assert compress(lib, tokens=-1) == SHAPE
+    assert compress(lib, hidden=0) == SHAPE
+    assert compress(lib, tokens=3, hidden=96) == SHAPE
+    assert compress(lib, tokens=1 << 40, hidden=1 << 40) == SHAPE
+    for b in (0, 16, 100, 1024, -128):
+        assert compress(lib, block=b) == BLOCK
+    for tau in (0.0, -1.0, float("inf"), float("nan"), 1e21):
+        assert compress(lib, tau=tau) == PARAM
+    assert compress(lib, x=None) == NULL
+    assert compress(lib, codes=None) == NULL
+    assert compress(lib, alpha=None) == NULL
+    assert compress(lib, scale=None) == NULL
+    assert compress(lib, x=A + 8) == ALIGN
+    assert compress(lib, codes=2 * A + 4) == ALIGN
+    assert compress(lib, alpha=3 * A + 2) == ALIGN
+    # Outputs overlapping the input or each other.
+    assert compress(lib, codes=A + 1024) == ALIAS
+    assert compress(lib, alpha=A + 16) == ALIAS
+    assert compress(lib, scale=3 * A + 4) == ALIAS
+    assert compress(lib, codes=3 * A - 512) == ALIAS
+    # Empty tensors are a no-op, even with NULL pointers.
+    assert compress(lib, tokens=0, x=None, codes=None, alpha=None, scale=None) == OK
+
+
+def receiver(fn, lib, codes=A, alpha=2 * A, scale=3 * A, tokens=4, hidden=256, block=128,
+             out=4 * A):
+    return fn(codes, alpha, scale, tokens, hidden, block, out, None)
+
+
+@pytest.mark.parametrize("name,elem", [("taco_decompress", 2), ("taco_decompress_accumulate", 4)])
+def test_receiver_validation(lib, name, elem):
+    fn = getattr(lib, name)
+    assert receiver(fn, lib, tokens=-2) == SHAPE
+    assert receiver(fn, lib, tokens=3, hidden=96) == SHAPE
+    assert receiver(fn, lib, block=48) == BLOCK
+    assert receiver(fn, lib, codes=None) == NULL
+    assert receiver(fn, lib, alpha=None) == NULL
+    assert receiver(fn, lib, scale=None) == NULL
+    assert receiver(fn, lib, out=None) == NULL
+    assert receiver(fn, lib, out=4 * A + 8) == ALIGN
+    assert receiver(fn, lib, codes=A + 8) == ALIGN
+    assert receiver(fn, lib, scale=3 * A + 1) == ALIGN
+    assert receiver(fn, lib, out=A + 512) == ALIAS
+    assert receiver(fn, lib, out=2 * A - 16) == ALIAS
+    assert receiver(fn, lib, scale=4 * A + 4 * 256 * elem - 4) == ALIAS
+    assert receiver(fn, lib, tokens=0, codes=None, alpha=None, scale=None, out=None) == OK
+
+
+def test_codec_validation(lib):
+    assert lib.taco_e4m3_encode(A, -1, 2 * A, None) == SHAPE
+    assert lib.taco_e4m3_encode(A, 0, None, None) == OK
+    assert lib.taco_e4m3_encode(None, 16, 2 * A, None) == NULL
+    assert lib.taco_e4m3_encode(A + 4, 16, 2 * A, None) == ALIGN
+    assert lib.taco_e4m3_encode(A, 16, A + 32, None) == ALIAS
+    assert lib.taco_e4m3_decode(A, 16, None, None) == NULL
+    assert lib.taco_e4m3_decode(A, 16, A, None) == ALIAS
+    assert lib.taco_e4m3_decode(A + 1, 16, 2 * A, None) == ALIGN
