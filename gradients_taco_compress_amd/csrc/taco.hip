@@ -35,13 +35,15 @@
 //    nearest even), 8 codes per lane per chunk; alpha / s as float32
 //    side-buffers.  Decompress decodes with v_cvt_pk_f32_fp8 and rounds to
 //    bf16 with v_cvt_pk_bf16_f32.
-//  * Persistent grid-stride loop over wave-steps with the next step's loads
-//    issued before the current step is processed.
+//  * Grid-stride loop over wave-steps (one step per wave by default, so a
+//    large tensor launches tens of thousands of work-groups); when a wave
+//    has several steps, the next step's loads are issued before the current
+//    step is processed.  Loads and stores are non-temporal: every byte is
+//    streamed once.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <math.h>
-#include <atomic>
 
 #include "taco.h"
 
@@ -50,18 +52,62 @@ namespace {
 typedef float f2v __attribute__((ext_vector_type(2)));
 typedef __bf16 bf2v __attribute__((ext_vector_type(2)));
 
+#ifndef TACO_WAVES_PER_GROUP
+#define TACO_WAVES_PER_GROUP 4
+#endif
 constexpr int kWave = 64;
-constexpr int kWavesPerGroup = 4;
+constexpr int kWavesPerGroup = TACO_WAVES_PER_GROUP;
 constexpr int kGroup = kWave * kWavesPerGroup;
+
+// Lanes per block for each block size (4 or 8; 4 halves the per-block
+// scalar work per element but doubles the registers per lane).
+#ifndef TACO_LPB_32
+#define TACO_LPB_32 4
+#endif
+#ifndef TACO_LPB_64
+#define TACO_LPB_64 8
+#endif
+#ifndef TACO_LPB_128
+#define TACO_LPB_128 8
+#endif
+#ifndef TACO_LPB_256
+#define TACO_LPB_256 8
+#endif
+#ifndef TACO_LPB_512
+#define TACO_LPB_512 8
+#endif
+// Non-temporal (streaming) global loads and stores for the tensors.
+#ifndef TACO_NT
+#define TACO_NT 1
+#endif
+// Block energy from packed bf16 pairs with v_dot2_f32_bf16 (else from
+// float32 squares).
+#ifndef TACO_DOT2_ENERGY
+#define TACO_DOT2_ENERGY 1
+#endif
+// Wave-steps (BPW blocks each) that one wave processes; the grid is sized
+// so that every wave gets this many (the last ones fewer).
+#ifndef TACO_STEPS_PER_WAVE
+#define TACO_STEPS_PER_WAVE 1
+#endif
+
+constexpr int lanes_per_block(int b) {
+    return b == 32    ? TACO_LPB_32
+           : b == 64  ? TACO_LPB_64
+           : b == 128 ? TACO_LPB_128
+           : b == 256 ? TACO_LPB_256
+                      : TACO_LPB_512;
+}
 
 template <int B>
 struct Geo {
-    static constexpr int LPB = (B >= 64) ? 8 : 4;  // lanes per block
+    static constexpr int LPB = lanes_per_block(B);  // lanes per block
     static constexpr int EPL = B / LPB;            // elements per lane
     static constexpr int CH = EPL / 8;             // 16-byte bf16 chunks per lane
     static constexpr int BPW = kWave / LPB;        // blocks per wave-step
     static constexpr int SPAN = LPB * 8;           // element stride between chunks
     static_assert(B >= 32 && B <= 512 && (B & (B - 1)) == 0, "block size");
+    static_assert((LPB == 4 || LPB == 8) && EPL >= 8, "lane layout");
 };
 
 // ---------------------------------------------------------------- lanes ----
@@ -92,12 +138,20 @@ __device__ __forceinline__ float block_sum(float v) {
     if (LPB == 8) v += dpp<kDppXor8>(v);
     return v;
 }
+// Maximum over the block's lanes of a non-negative float.  Non-negative
+// floats order like their bit patterns, so the reduction runs on unsigned
+// integers (which need no NaN quieting and fuse with the DPP move).
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, true);
+}
 template <int LPB>
-__device__ __forceinline__ float block_max(float v) {
-    v = fmaxf(v, dpp<kDppXor1>(v));
-    v = fmaxf(v, dpp<kDppXor2>(v));
-    if (LPB == 8) v = fmaxf(v, dpp<kDppXor8>(v));
-    return v;
+__device__ __forceinline__ float block_max(float f) {
+    uint32_t v = __float_as_uint(f);
+    v = max(v, dpp_u<kDppXor1>(v));
+    v = max(v, dpp_u<kDppXor2>(v));
+    if (LPB == 8) v = max(v, dpp_u<kDppXor8>(v));
+    return __uint_as_float(v);
 }
 
 // v[i] <- v[i] + sgn * v[i]@partner for 8 registers, partner given by the
@@ -121,7 +175,8 @@ __device__ __forceinline__ float block_max(float v) {
 // Unnormalised Walsh-Hadamard transform of the block held by LPB lanes
 // (EPL registers each), Sylvester order over e = 8*LPB*k + 8*t + j.  Must
 // run with every lane of the wave active.  On return lane t holds
-// (-1)^popcount(t) times its outputs.
+// (-1)^popcount(t) times its outputs.  The stages commute, so any order
+// gives H x (float32 rounding aside).
 template <int LPB, int EPL>
 __device__ __forceinline__ void fwht_block(float (&v)[EPL], float sg1, float sg2, float sg8) {
     constexpr int CH = EPL / 8;
@@ -163,6 +218,49 @@ __device__ __forceinline__ void fwht_block(float (&v)[EPL], float sg1, float sg2
     }
 }
 
+// Streaming global memory access (each byte is touched once).
+typedef unsigned int u4v __attribute__((ext_vector_type(4)));
+typedef unsigned int u2v __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ u4v ld16(const void *p) {
+#if TACO_NT
+    return __builtin_nontemporal_load(reinterpret_cast<const u4v *>(p));
+#else
+    return *reinterpret_cast<const u4v *>(p);
+#endif
+}
+__device__ __forceinline__ u2v ld8(const void *p) {
+#if TACO_NT
+    return __builtin_nontemporal_load(reinterpret_cast<const u2v *>(p));
+#else
+    return *reinterpret_cast<const u2v *>(p);
+#endif
+}
+__device__ __forceinline__ void st16(void *p, u4v v) {
+#if TACO_NT
+    __builtin_nontemporal_store(v, reinterpret_cast<u4v *>(p));
+#else
+    *reinterpret_cast<u4v *>(p) = v;
+#endif
+}
+__device__ __forceinline__ void st8(void *p, u2v v) {
+#if TACO_NT
+    __builtin_nontemporal_store(v, reinterpret_cast<u2v *>(p));
+#else
+    *reinterpret_cast<u2v *>(p) = v;
+#endif
+}
+
+// Sum of squares of packed bf16 pairs accumulated in float32
+// (v_dot2_f32_bf16: c + a*a + b*b).  Only the block energy uses it; its
+// rounding of the sum need not match a float32 addition, as alpha's
+// tolerance (1e-6 relative) is far above the few ulps at stake.
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ float dot2_acc(uint32_t w, float c) {
+    const bf16x2 v = __builtin_bit_cast(bf16x2, w);
+    return __builtin_amdgcn_fdot2_f32_bf16(v, v, c, false);
+}
+
 // Empty asm that forces each value to exist in a VGPR at this point of the
 // program (it emits no instruction).
 template <int N>
@@ -174,11 +272,23 @@ __device__ __forceinline__ void pin_values(float (&v)[N]) {
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
-__device__ __forceinline__ void unpack8(const uint4 w, float *v) {
+__device__ __forceinline__ void unpack8(const u4v w, float *v) {
     v[0] = bf16_lo(w.x); v[1] = bf16_hi(w.x);
     v[2] = bf16_lo(w.y); v[3] = bf16_hi(w.y);
     v[4] = bf16_lo(w.z); v[5] = bf16_hi(w.z);
     v[6] = bf16_lo(w.w); v[7] = bf16_hi(w.w);
+}
+
+// Block energy from packed bf16: four accumulator chains of dot2 (so the
+// rounding depth is CH + 2 in-lane, plus log2(LPB) across lanes).
+template <int CH>
+__device__ __forceinline__ float energy_packed(const u4v (&buf)[CH]) {
+    float e[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int k = 0; k < CH; ++k)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) e[i] = dot2_acc(buf[k][i], e[i]);
+    return (e[0] + e[1]) + (e[2] + e[3]);
 }
 
 // Sum of squares of EPL values by a pairwise tree: each x^2 of a bf16 value
@@ -209,11 +319,12 @@ __device__ __forceinline__ float max_abs(const float (&v)[EPL]) {
         asm("v_max3_f32 %0, %0, |%1|, |%2|" : "+v"(m0) : "v"(v[i]), "v"(v[i + 1]));
         asm("v_max3_f32 %0, %0, |%1|, |%2|" : "+v"(m1) : "v"(v[i + 2]), "v"(v[i + 3]));
     }
-    return fmaxf(m0, m1);
+    asm("v_max_f32 %0, %0, %1" : "+v"(m0) : "v"(m1));
+    return m0;
 }
 
 // Packs 8 values into 8 E4M3 codes (little-endian: element j in byte j).
-__device__ __forceinline__ uint2 encode8(const float *v, float r) {
+__device__ __forceinline__ u2v encode8(const float *v, float r) {
     // fma(.., 0) maps an exact zero of either sign to +0 (code 0x00).
     float q[8];
 #pragma unroll
@@ -222,10 +333,10 @@ __device__ __forceinline__ uint2 encode8(const float *v, float r) {
     lo = __builtin_amdgcn_cvt_pk_fp8_f32(q[2], q[3], lo, true);
     int hi = __builtin_amdgcn_cvt_pk_fp8_f32(q[4], q[5], 0, false);
     hi = __builtin_amdgcn_cvt_pk_fp8_f32(q[6], q[7], hi, true);
-    return make_uint2((uint32_t)lo, (uint32_t)hi);
+    return (u2v){(uint32_t)lo, (uint32_t)hi};
 }
 
-__device__ __forceinline__ void decode8(const uint2 c, float *v) {
+__device__ __forceinline__ void decode8(const u2v c, float *v) {
     f2v a = __builtin_amdgcn_cvt_pk_f32_fp8((int)c.x, false);
     f2v b = __builtin_amdgcn_cvt_pk_f32_fp8((int)c.x, true);
     f2v d = __builtin_amdgcn_cvt_pk_f32_fp8((int)c.y, false);
@@ -282,19 +393,27 @@ __global__ __launch_bounds__(kGroup) void compress_kernel(
     constexpr float kInvB = 1.0f / (float)B;
 
     const int64_t nsteps = (nblocks + G::BPW - 1) / G::BPW;
-    const int64_t wave0 = (int64_t)blockIdx.x * kWavesPerGroup + (threadIdx.x >> 6);
+    const int64_t wave0 = (int64_t)blockIdx.x * kWavesPerGroup +
+                          __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int64_t nwaves = (int64_t)gridDim.x * kWavesPerGroup;
+    // Element offset of this lane's data inside one wave-step's span of
+    // BPW blocks; addresses are a wave-uniform base plus this 32-bit offset.
+    const uint32_t lane_elem = (uint32_t)(g * B + 8 * t);
 
     // Slots past the last block (only in the final wave-step) re-read the
     // last block, so every load is in bounds and no lane needs zero-filling;
     // their results are never stored.
-    uint4 buf[G::CH];
+    auto lane_offset = [&](int64_t step) -> uint32_t {
+        const int64_t left = nblocks - step * G::BPW;          // wave-uniform
+        if (left >= G::BPW) return lane_elem;
+        const int gl = g < left ? g : (int)left - 1;
+        return (uint32_t)(gl * B + 8 * t);
+    };
+    u4v buf[G::CH];
     auto load = [&](int64_t step) {
-        int64_t blk = step * G::BPW + g;
-        blk = blk < nblocks ? blk : nblocks - 1;
-        const uint4 *p = reinterpret_cast<const uint4 *>(x + blk * B + 8 * t);
+        const uint16_t *p = x + step * (G::BPW * B) + lane_offset(step);
 #pragma unroll
-        for (int k = 0; k < G::CH; ++k) buf[k] = p[k * (G::SPAN / 8)];
+        for (int k = 0; k < G::CH; ++k) buf[k] = ld16(p + k * G::SPAN);
     };
 
     if (wave0 < nsteps) load(wave0);
@@ -302,27 +421,36 @@ __global__ __launch_bounds__(kGroup) void compress_kernel(
         float v[G::EPL];
 #pragma unroll
         for (int k = 0; k < G::CH; ++k) unpack8(buf[k], &v[8 * k]);
-        // Materialise the unpacked values here, so that the prefetch below
-        // can reuse buf's registers instead of copying them.
+        // [TACO] Eq. 6: block energy (raw second moment), this lane's part.
+#if TACO_DOT2_ENERGY
+        float energy = energy_packed<G::CH>(buf);
+#else
+        float energy = sum_squares<G::EPL>(v);
+#endif
+        // Materialise these values here, so that the prefetch below can
+        // reuse buf's registers instead of copying them.
         pin_values(v);
+        asm volatile("" : "+v"(energy));
         if (step + nwaves < nsteps) load(step + nwaves);
 
         const int64_t blk = step * G::BPW + g;
         const bool active = blk < nblocks;
 
-        // [TACO] Eq. 6: block energy (raw second moment).
-        float energy = block_sum<G::LPB>(sum_squares<G::EPL>(v));
+        energy = block_sum<G::LPB>(energy);
         float unshift = 1.0f;
         if (__builtin_expect(energy >= kBigEnergy, 0)) {
-            // Huge block: work on x * 2^-64 (exact), undo it in alpha.
+            // Huge block (sum x^2 near or past float32 range): reload it and
+            // work on x * 2^-64 (exact), undoing the factor in alpha.
+            const uint16_t *p = x + step * (G::BPW * B) + lane_offset(step);
+#pragma unroll
+            for (int k = 0; k < G::CH; ++k) unpack8(ld16(p + k * G::SPAN), &v[8 * k]);
 #pragma unroll
             for (int i = 0; i < G::EPL; ++i) v[i] *= kBigShift;
             energy = block_sum<G::LPB>(sum_squares<G::EPL>(v));
             unshift = kBigUnshift;
         }
-        // [TACO] Eq. 6-7.
-        const float sigma = sqrtf(energy * kInvB + TACO_EPS);
-        const float a = tau / sigma;
+        // [TACO] Eq. 6-7: alpha = tau / sqrt(mean(x^2) + eps).
+        const float a = tau * __builtin_amdgcn_rsqf(energy * kInvB + TACO_EPS);
 
         // [TACO] Eq. 8 without its constant factors: R = H x.
         fwht_block<G::LPB, G::EPL>(v, sg1, sg2, sg8);
@@ -335,17 +463,20 @@ __global__ __launch_bounds__(kGroup) void compress_kernel(
             for (int i = 0; i < G::EPL; ++i) v[i] *= kTinyShift;
             m *= kTinyShift;
         }
-        // [TACO] Eq. 10: Z / s = Q * R / max|R|.
-        const float r = (m > 0.0f) ? (TACO_QMAX / m) * lane_sign : 0.0f;
+        // [TACO] Eq. 10: Z / s = Q * R / max|R|.  Q / max|R| from the
+        // hardware reciprocal refined by one Newton step on the quotient.
+        const float rc = __builtin_amdgcn_rcpf(m);
+        const float q0 = TACO_QMAX * rc;
+        const float q1 = fmaf(fmaf(-m, q0, TACO_QMAX), rc, q0);
+        const float r = (m > 0.0f) ? q1 * lane_sign : 0.0f;
 
         if (active) {
-            uint8_t *cq = codes + blk * B + 8 * t;
+            uint8_t *cq = codes + step * (G::BPW * B) + lane_elem;
 #pragma unroll
-            for (int k = 0; k < G::CH; ++k)
-                *reinterpret_cast<uint2 *>(cq + k * G::SPAN) = encode8(&v[8 * k], r);
+            for (int k = 0; k < G::CH; ++k) st8(cq + k * G::SPAN, encode8(&v[8 * k], r));
             if (t == 0) {
-                alpha[blk] = a * unshift;
-                scale[blk] = s;
+                alpha[step * G::BPW + g] = a * unshift;
+                scale[step * G::BPW + g] = s;
             }
         }
     }
@@ -376,14 +507,14 @@ __global__ __launch_bounds__(kGroup) void decompress_kernel(
     const int64_t nwaves = (int64_t)gridDim.x * kWavesPerGroup;
 
     // Slots past the last block re-read the last block (never stored).
-    uint2 buf[G::CH];
+    u2v buf[G::CH];
     float a_buf = 1.0f, s_buf = 0.0f;
     auto load = [&](int64_t step) {
         int64_t blk = step * G::BPW + g;
         blk = blk < nblocks ? blk : nblocks - 1;
-        const uint2 *p = reinterpret_cast<const uint2 *>(codes + blk * B + 8 * t);
+        const uint8_t *p = codes + blk * B + 8 * t;
 #pragma unroll
-        for (int k = 0; k < G::CH; ++k) buf[k] = p[k * (G::SPAN / 8)];
+        for (int k = 0; k < G::CH; ++k) buf[k] = ld8(p + k * G::SPAN);
         a_buf = alpha[blk];
         s_buf = scale[blk];
     };
@@ -421,23 +552,24 @@ __global__ __launch_bounds__(kGroup) void decompress_kernel(
 #pragma unroll
                 for (int k = 0; k < G::CH; ++k) {
                     const float *w = &v[8 * k];
-                    uint4 o;
-                    o.x = pack_bf16x2(w[0], w[1]);
-                    o.y = pack_bf16x2(w[2], w[3]);
-                    o.z = pack_bf16x2(w[4], w[5]);
-                    o.w = pack_bf16x2(w[6], w[7]);
-                    *reinterpret_cast<uint4 *>(y + e0 + k * G::SPAN) = o;
+                    const u4v o = {pack_bf16x2(w[0], w[1]), pack_bf16x2(w[2], w[3]),
+                                   pack_bf16x2(w[4], w[5]), pack_bf16x2(w[6], w[7])};
+                    st16(y + e0 + k * G::SPAN, o);
                 }
             } else {
 #pragma unroll
                 for (int k = 0; k < G::CH; ++k) {
                     const float *w = &v[8 * k];
-                    float4 *pa = reinterpret_cast<float4 *>(acc + e0 + k * G::SPAN);
-                    float4 p0 = pa[0], p1 = pa[1];
-                    p0.x += w[0]; p0.y += w[1]; p0.z += w[2]; p0.w += w[3];
-                    p1.x += w[4]; p1.y += w[5]; p1.z += w[6]; p1.w += w[7];
-                    pa[0] = p0;
-                    pa[1] = p1;
+                    float *pa = acc + e0 + k * G::SPAN;
+                    const u4v p0 = ld16(pa), p1 = ld16(pa + 4);
+                    u4v o0, o1;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        o0[j] = __float_as_uint(__uint_as_float(p0[j]) + w[j]);
+                        o1[j] = __float_as_uint(__uint_as_float(p1[j]) + w[4 + j]);
+                    }
+                    st16(pa, o0);
+                    st16(pa + 4, o1);
                 }
             }
         }
@@ -501,29 +633,14 @@ int64_t numel(int64_t tokens, int64_t hidden) {
     return tokens * hidden;
 }
 
-int cu_count() {
-    static std::atomic<int> cache[64];
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return 256;
-    if (dev >= 0 && dev < 64) {
-        int c = cache[dev].load(std::memory_order_relaxed);
-        if (c > 0) return c;
-    }
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
-        n = 256;
-    if (dev >= 0 && dev < 64) cache[dev].store(n, std::memory_order_relaxed);
-    return n;
-}
-
-// Persistent grid: enough work-groups to cover every wave-step once, capped
-// at kGroupsPerCU groups per compute unit.
-constexpr int kGroupsPerCU = 8;
-
+// Grid: each wave takes TACO_STEPS_PER_WAVE wave-steps (grid-stride), so
+// large tensors launch many work-groups, which keeps every compute unit
+// busy up to the tail.
 unsigned grid_for(int64_t nsteps) {
-    const int64_t need = (nsteps + kWavesPerGroup - 1) / kWavesPerGroup;
-    const int64_t cap = (int64_t)cu_count() * kGroupsPerCU;
-    const int64_t g = need < cap ? need : cap;
+    constexpr int64_t per_group = (int64_t)kWavesPerGroup * TACO_STEPS_PER_WAVE;
+    int64_t g = (nsteps + per_group - 1) / per_group;
+    const int64_t cap = INT64_C(1) << 30;
+    g = g < cap ? g : cap;
     return (unsigned)(g > 0 ? g : 1);
 }
 

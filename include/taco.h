@@ -35,9 +35,8 @@
  *   - Inputs must be finite.  Blocks whose RMS exceeds ~2^126 / target_energy
  *     get a subnormal float32 alpha (less precise); non-finite inputs give
  *     unspecified codes and scalars (but never out-of-bounds accesses).
- *   - Thread-safe: calls share no mutable state (a per-device compute-unit
- *     count is cached once).  Calls on different streams may overlap if
- *     their buffers do not.
+ *   - Thread-safe: the library has no mutable state.  Calls on different
+ *     streams may overlap if their buffers do not.
  */
 #ifndef TACO_H
 #define TACO_H
