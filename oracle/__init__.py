@@ -65,6 +65,8 @@ def _load():
         lib.taco_oracle_decompress.argtypes = [P, P, P, i64, i32, P]
         lib.taco_oracle_decompress_accumulate.argtypes = [P, P, P, i64, i32, P]
         lib.taco_oracle_roundtrip_noquant.argtypes = [P, i32, f64, f64, P]
+        lib.taco_oracle_compress_f64.argtypes = [P, i64, i32, f64, f64, P, P, P]
+        lib.taco_oracle_reduce_compress.argtypes = [P, i32, P, P, P, i64, i32, f64, f64, P, P, P]
         _lib = lib
     return _lib
 
@@ -155,6 +157,48 @@ def compress(x_bits, block: int, tau: float = 1.0, eps: float = EPS):
     alpha = np.empty(n // block, np.float32)
     scale = np.empty(n // block, np.float32)
     _check(lib.taco_oracle_compress(_ptr(x), n, block, tau, eps, _ptr(codes), _ptr(alpha), _ptr(scale)))
+    return codes, alpha, scale
+
+
+def compress_f64(x, block: int, tau: float = 1.0, eps: float = EPS):
+    """Like compress() for a tensor of float64 values."""
+    lib = _load()
+    xv = np.ascontiguousarray(x, dtype=np.float64)
+    n = xv.size
+    if block <= 0 or n % block:
+        raise ValueError("element count must be a multiple of the block size")
+    codes = np.empty(xv.shape, np.uint8)
+    alpha = np.empty(n // block, np.float32)
+    scale = np.empty(n // block, np.float32)
+    _check(lib.taco_oracle_compress_f64(_ptr(xv), n, block, tau, eps, _ptr(codes), _ptr(alpha), _ptr(scale)))
+    return codes, alpha, scale
+
+
+def reduce_compress(own_bits, payloads, block: int, tau: float = 1.0, eps: float = EPS):
+    """Owner step: compress own + sum of the payloads' reconstructions.
+    own_bits: bf16 bit patterns or None; payloads: list of (codes, alpha, scale)."""
+    lib = _load()
+    pay = [(np.ascontiguousarray(c, dtype=np.uint8), np.ascontiguousarray(a, dtype=np.float32),
+            np.ascontiguousarray(s, dtype=np.float32)) for c, a, s in payloads]
+    if own_bits is not None:
+        own = np.ascontiguousarray(own_bits, dtype=np.uint16)
+        shape, n = own.shape, own.size
+    else:
+        own = None
+        shape, n = pay[0][0].shape, pay[0][0].size
+    for c, a, s in pay:
+        assert c.size == n and a.size == n // block and s.size == n // block
+    arr = ctypes.c_void_p * max(1, len(pay))
+    cp = arr(*[c.ctypes.data for c, _, _ in pay])
+    ap = arr(*[a.ctypes.data for _, a, _ in pay])
+    sp = arr(*[s.ctypes.data for _, _, s in pay])
+    codes = np.empty(shape, np.uint8)
+    alpha = np.empty(n // block, np.float32)
+    scale = np.empty(n // block, np.float32)
+    _check(lib.taco_oracle_reduce_compress(None if own is None else _ptr(own), len(pay),
+                                           ctypes.cast(cp, ctypes.c_void_p), ctypes.cast(ap, ctypes.c_void_p),
+                                           ctypes.cast(sp, ctypes.c_void_p), n, block, tau, eps,
+                                           _ptr(codes), _ptr(alpha), _ptr(scale)))
     return codes, alpha, scale
 
 

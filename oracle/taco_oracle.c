@@ -176,20 +176,16 @@ static int valid_block(int B)
 /* ------------------------------------------------------------------------ */
 
 /*
- * ASH transform of one block, in double: returns alpha_k (Eq. 6-7), the
- * rescaled block Gt (Eq. 7, element-wise product) and Z (Eq. 8).
- * Any of the output pointers may be NULL.
+ * ASH transform of one block given as doubles: alpha_k (Eq. 6-7), the
+ * rescaled block Gt (Eq. 7, element-wise product) and Z (Eq. 8).  Any of the
+ * output pointers may be NULL.
  */
-int taco_oracle_ash_block(const uint16_t *x, int B, double tau, double eps,
+static void ash_block_f64(const double *G, int B, double tau, double eps,
                           double *alpha_out, double *gt_out, double *z_out)
 {
-    if (!valid_block(B)) return -1;
-    double G[ORACLE_MAX_BLOCK], Z[ORACLE_MAX_BLOCK];
+    double Z[ORACLE_MAX_BLOCK];
     double energy = 0.0;
-    for (int j = 0; j < B; ++j) {
-        G[j] = bf16_to_double(x[j]);
-        energy += G[j] * G[j];
-    }
+    for (int j = 0; j < B; ++j) energy += G[j] * G[j];
     double sigma = sqrt(energy / B + eps);         /* Eq. 6 */
     double alpha = tau / sigma;                    /* Eq. 7 */
     for (int j = 0; j < B; ++j) Z[j] = alpha * G[j];
@@ -199,7 +195,33 @@ int taco_oracle_ash_block(const uint16_t *x, int B, double tau, double eps,
     for (int j = 0; j < B; ++j) Z[j] *= c;
     if (alpha_out) *alpha_out = alpha;
     if (z_out) memcpy(z_out, Z, sizeof(double) * (size_t)B);
+}
+
+/* The same for one block of bf16 values. */
+int taco_oracle_ash_block(const uint16_t *x, int B, double tau, double eps,
+                          double *alpha_out, double *gt_out, double *z_out)
+{
+    if (!valid_block(B)) return -1;
+    double G[ORACLE_MAX_BLOCK];
+    for (int j = 0; j < B; ++j) G[j] = bf16_to_double(x[j]);
+    ash_block_f64(G, B, tau, eps, alpha_out, gt_out, z_out);
     return 0;
+}
+
+/* Eq. 9-10 for one block with its Z and alpha (Algorithm 1, sender side). */
+static void quantise_block(const double *Z, double a, int B, uint8_t *q,
+                           float *alpha_out, float *scale_out)
+{
+    double zmax = 0.0;
+    for (int j = 0; j < B; ++j) zmax = fmax(zmax, fabs(Z[j]));
+    double s = zmax / ORACLE_QMAX;                 /* Eq. 9 */
+    for (int j = 0; j < B; ++j) {                  /* Eq. 10 */
+        float v = (s > 0.0) ? (float)(Z[j] / s) : 0.0f;
+        if (v == 0.0f) v = 0.0f;                   /* zero carries no sign */
+        q[j] = taco_oracle_e4m3_encode(v);
+    }
+    *alpha_out = (float)a;
+    *scale_out = (float)s;
 }
 
 /*
@@ -212,20 +234,23 @@ int taco_oracle_compress(const uint16_t *x, int64_t n, int B, double tau,
     if (!valid_block(B) || n < 0 || n % B) return -1;
     double Z[ORACLE_MAX_BLOCK];
     for (int64_t k = 0; k < n / B; ++k) {
-        const uint16_t *xb = x + k * B;
         double a;
-        taco_oracle_ash_block(xb, B, tau, eps, &a, NULL, Z);
-        double zmax = 0.0;
-        for (int j = 0; j < B; ++j) zmax = fmax(zmax, fabs(Z[j]));
-        double s = zmax / ORACLE_QMAX;             /* Eq. 9 */
-        uint8_t *q = codes + k * B;
-        for (int j = 0; j < B; ++j) {              /* Eq. 10 */
-            float v = (s > 0.0) ? (float)(Z[j] / s) : 0.0f;
-            if (v == 0.0f) v = 0.0f;               /* zero carries no sign */
-            q[j] = taco_oracle_e4m3_encode(v);
-        }
-        alpha[k] = (float)a;
-        scale[k] = (float)s;
+        taco_oracle_ash_block(x + k * B, B, tau, eps, &a, NULL, Z);
+        quantise_block(Z, a, B, codes + k * B, alpha + k, scale + k);
+    }
+    return 0;
+}
+
+/* The same for a tensor given as doubles. */
+int taco_oracle_compress_f64(const double *x, int64_t n, int B, double tau,
+                             double eps, uint8_t *codes, float *alpha, float *scale)
+{
+    if (!valid_block(B) || n < 0 || n % B) return -1;
+    double Z[ORACLE_MAX_BLOCK];
+    for (int64_t k = 0; k < n / B; ++k) {
+        double a;
+        ash_block_f64(x + k * B, B, tau, eps, &a, NULL, Z);
+        quantise_block(Z, a, B, codes + k * B, alpha + k, scale + k);
     }
     return 0;
 }
@@ -283,6 +308,38 @@ int taco_oracle_decompress_accumulate(const uint8_t *codes, const float *alpha,
             float gf = (float)g[j];
             acc[k * B + j] = acc[k * B + j] + gf;
         }
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Owner step of the two-shot all-reduce ([TACO] section 4.4.2)              */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * The reduce-scatter phase ends in one local reduction of the received
+ * payloads, and the reduced segment is compressed again for the all-gather:
+ * X = own + sum_p G'_p (Eq. 11-13 per payload, summed in double; own may be
+ * NULL for a pure sum), then (codes, alpha, s) of X by Eq. 5-10.
+ */
+int taco_oracle_reduce_compress(const uint16_t *own, int npay,
+                                const uint8_t *const *codes_in,
+                                const float *const *alpha_in,
+                                const float *const *scale_in, int64_t n, int B,
+                                double tau, double eps, uint8_t *codes,
+                                float *alpha, float *scale)
+{
+    if (!valid_block(B) || n < 0 || n % B || npay < 0) return -1;
+    double X[ORACLE_MAX_BLOCK], g[ORACLE_MAX_BLOCK], Z[ORACLE_MAX_BLOCK];
+    for (int64_t k = 0; k < n / B; ++k) {
+        for (int j = 0; j < B; ++j) X[j] = own ? bf16_to_double(own[k * B + j]) : 0.0;
+        for (int p = 0; p < npay; ++p) {
+            reconstruct_block(codes_in[p] + k * B, alpha_in[p][k], scale_in[p][k], B, g);
+            for (int j = 0; j < B; ++j) X[j] += g[j];
+        }
+        double a;
+        ash_block_f64(X, B, tau, eps, &a, NULL, Z);
+        quantise_block(Z, a, B, codes + k * B, alpha + k, scale + k);
     }
     return 0;
 }
