@@ -14,8 +14,11 @@ Prints one JSON line (rank 0, the only rank): the headline metric is input
 GB/s of bf16 (2 bytes per element) per round trip, plus a roofline object for
 the dominant kernel and the CPU oracle's rate on the same workload.
 
-    python bench.py [--steps K] [--warmup W] [--workload NAME] [--block B]
+    python bench.py [--steps K] [--warmup W] [--workload NAME[:owner]] [--block B]
     python bench.py --all --out results.json     # every workload (stderr table)
+
+``NAME:owner`` times the fused owner step of the two-shot all-reduce
+(``taco_reduce_compress`` of an own partial plus three payloads) instead.
 """
 from __future__ import annotations
 
@@ -59,6 +62,9 @@ def algorithmic_bytes(op: str, n: int, block: int) -> float:
     """Bytes the operator must move: bf16 in/out 2/elem, codes 1/elem,
     alpha + s 8 bytes per block, float32 accumulator 4 + 4 per element."""
     side = 8.0 * n / block
+    if op.startswith("reduce_compress"):
+        npay = int(op.split(":")[1]) if ":" in op else 3
+        return 2.0 * n + npay * (n + side) + n + side
     if op == "compress":
         return 2.0 * n + n + side
     if op == "decompress":
@@ -220,6 +226,44 @@ def accumulate_case(torch, taco, synth, name: str, block: int, steps: int, warmu
             "input_bytes_step": nb * 2.0 * n, "kernels": {"compress": t_c, "accumulate": t_a}}
 
 
+def owner_case(torch, taco, synth, name: str, block: int, steps: int, warmup: int,
+               use_graph: bool):
+    """Owner step of the two-shot all-reduce: own bf16 partial plus three
+    received payloads (four independently seeded tensors) reduced and
+    compressed again in one taco_reduce_compress call."""
+    import numpy as np
+    r = synth.WORKLOADS[name]
+    n = r.numel
+    m = n // block
+    seeds = synth.ACCUMULATE_SEEDS
+    own = torch.from_numpy(synth.generate(r, seed=seeds[0]).view(np.int16)).cuda().view(torch.bfloat16)
+    pay = []
+    for seed in seeds[1:]:
+        x = torch.from_numpy(synth.generate(r, seed=seed).view(np.int16)).cuda().view(torch.bfloat16)
+        pay.append(taco.compress(x, block=block))
+        del x
+    codes = torch.empty((r.rows, r.cols), dtype=torch.uint8, device="cuda")
+    alpha = torch.empty(m, dtype=torch.float32, device="cuda")
+    scale = torch.empty(m, dtype=torch.float32, device="cuda")
+
+    def run_steps():
+        taco.reduce_compress(own, pay, block=block, codes=codes, alpha=alpha, scale=scale)
+
+    for _ in range(max(1, warmup)):
+        run_steps()
+    torch.cuda.synchronize()
+    step_fn = make_graph(torch, run_steps, use_graph)
+    reps = max(1, steps)
+    timer = Timer(torch)
+    step_fn()
+    t = timer.time(step_fn, reps) / reps
+    npay = len(pay)
+    kbytes = 2.0 * n + npay * (n + 8.0 * n / block) + n + 8.0 * n / block
+    return {"n": n, "block": block, "steps": reps, "t_step": t, "sets": 1, "rows": r.rows,
+            "cols": r.cols, "bytes_step": kbytes, "input_bytes_step": 2.0 * n,
+            "kernels": {"reduce_compress": t}, "npayloads": npay}
+
+
 def cpu_baseline(synth, name: str, block: int, min_seconds: float, accumulate: bool):
     """The oracle (single-threaded C, double precision) on the same workload,
     round trips repeated until min_seconds of CPU time have passed."""
@@ -254,7 +298,7 @@ def record(res, name: str, args, cpu=None):
     value = res["input_bytes_step"] / t_step / 1e9
     kern = max(res["kernels"], key=lambda k: res["kernels"][k])
     dur = res["kernels"][kern]
-    op = {"compress": "compress", "decompress": "decompress", "accumulate": "accumulate"}[kern]
+    op = kern if kern != "reduce_compress" else f"reduce_compress:{res['npayloads']}"
     kbytes = algorithmic_bytes(op, res["n"], res["block"])
     achieved = kbytes / dur / 1e9
     traffic = traffic_for(kern, name, res["block"])
@@ -274,7 +318,8 @@ def record(res, name: str, args, cpu=None):
         "config": {"workload": name, "tokens": res["rows"], "hidden": res["cols"],
                    "block": res["block"], "target_energy": 1.0,
                    "step": ("4x compress + 4x decompress_accumulate" if "t_accumulate" in res
-                            else "compress + decompress"),
+                            else f"reduce_compress of own + {res['npayloads']} payloads"
+                            if "npayloads" in res else "compress + decompress"),
                    "buffer_sets": res["sets"], "graph": not args.no_graph},
         "pct_hbm_peak": round(100.0 * res["bytes_step"] / t_step / 1e9 / HBM_PEAK_GBS, 2),
         "kernel_us": {k: round(v * 1e6, 3) for k, v in res["kernels"].items()},
@@ -320,17 +365,22 @@ def main():
     if args.all:
         cases = [("laplace_2048x1024", 128), ("gpt2.7b_rowpar_8192x2560", 128),
                  ("qwen7b_act_16384x3584", 128), ("qwen7b_act_16384x3584", 256),
-                 ("grad_8192x8192", 256), ("gpt175b_hidden_32768x12288", 256)]
+                 ("grad_8192x8192", 256), ("gpt175b_hidden_32768x12288", 256),
+                 ("gpt175b_hidden_32768x12288:owner", 256)]
     else:
         name = args.workload or synth.DEFAULT_WORKLOAD
-        block = args.block or synth.WORKLOADS[name].blocks[0]
+        block = args.block or synth.WORKLOADS[name.split(":")[0]].blocks[0]
         cases = [(name, block)]
     recs = []
     for i, (name, block) in enumerate(cases):
         print(f"[bench] {name} block {block}", file=sys.stderr, flush=True)
         acc = name.startswith("gpt175b")
         steps = args.steps if not acc else max(1, min(args.steps, 10))
-        if acc:
+        if name.endswith(":owner"):
+            name = name.split(":")[0]
+            res = owner_case(torch, taco, synth, name, block, steps, args.warmup, use_graph)
+            acc = False
+        elif acc:
             res = accumulate_case(torch, taco, synth, name, block, steps, args.warmup, use_graph)
         else:
             res = roundtrip_case(torch, taco, synth, name, block, steps, args.warmup, use_graph)

@@ -8,12 +8,14 @@ the library has not been built (``python -m gradients_taco_compress_amd.build``)
 Two layers:
 
 * ``taco_compress``, ``taco_decompress``, ``taco_decompress_accumulate``,
-  ``taco_e4m3_encode``, ``taco_e4m3_decode``, ``taco_num_blocks``,
-  ``taco_status_string``: the C ABI of ``include/taco.h`` with the same
-  names and arguments (device pointers as ints, stream handle as int).
-* ``compress``, ``decompress``, ``decompress_accumulate``, ``e4m3_encode``,
-  ``e4m3_decode``: the same calls on torch tensors, allocating outputs when
-  none are given and launching on torch's current stream.
+  ``taco_reduce_compress``, ``taco_e4m3_encode``, ``taco_e4m3_decode``,
+  ``taco_num_blocks``, ``taco_status_string``: the C ABI of ``include/taco.h``
+  with the same names and arguments (device pointers as ints, stream handle
+  as int, pointer arrays as sequences of ints).
+* ``compress``, ``decompress``, ``decompress_accumulate``, ``reduce_compress``,
+  ``e4m3_encode``, ``e4m3_decode``: the same calls on torch tensors,
+  allocating outputs when none are given and launching on torch's current
+  stream.
 """
 from __future__ import annotations
 
@@ -57,6 +59,8 @@ _lib.taco_decompress.argtypes = [_P, _P, _P, _I64, _I64, _I32, _P, _P]
 _lib.taco_decompress.restype = ctypes.c_int
 _lib.taco_decompress_accumulate.argtypes = [_P, _P, _P, _I64, _I64, _I32, _P, _P]
 _lib.taco_decompress_accumulate.restype = ctypes.c_int
+_lib.taco_reduce_compress.argtypes = [_P, _I32, _P, _P, _P, _I64, _I64, _I32, _F32, _P, _P, _P, _P]
+_lib.taco_reduce_compress.restype = ctypes.c_int
 _lib.taco_e4m3_encode.argtypes = [_P, _I64, _P, _P]
 _lib.taco_e4m3_encode.restype = ctypes.c_int
 _lib.taco_e4m3_decode.argtypes = [_P, _I64, _P, _P]
@@ -66,8 +70,11 @@ _lib.taco_status_string.restype = ctypes.c_char_p
 
 #: Symbols the library exports (checked against include/taco.h by the tests).
 EXPORTS = ("taco_num_blocks", "taco_compress", "taco_decompress",
-           "taco_decompress_accumulate", "taco_e4m3_encode", "taco_e4m3_decode",
-           "taco_status_string")
+           "taco_decompress_accumulate", "taco_reduce_compress", "taco_e4m3_encode",
+           "taco_e4m3_decode", "taco_status_string")
+
+#: Most payloads one taco_reduce_compress call sums.
+MAX_PAYLOADS = 8
 
 
 # ------------------------------------------------------------- raw C ABI --
@@ -95,6 +102,23 @@ def taco_decompress_accumulate(codes_e4m3: int, alpha: int, scale: int, tokens: 
                                hidden: int, block: int, acc_f32: int, stream: int) -> int:
     return _lib.taco_decompress_accumulate(codes_e4m3, alpha, scale, tokens, hidden, block,
                                            acc_f32, stream)
+
+
+def _ptr_array(ptrs):
+    arr = (ctypes.c_void_p * max(1, len(ptrs)))(*[int(p) for p in ptrs])
+    return arr
+
+
+def taco_reduce_compress(own_bf16: int, npayloads: int, codes_e4m3, alpha, scale, tokens: int,
+                         hidden: int, block: int, target_energy: float, out_codes: int,
+                         out_alpha: int, out_scale: int, stream: int) -> int:
+    """codes_e4m3 / alpha / scale: sequences of npayloads device pointers
+    (passed to the library as host arrays), or None when npayloads is 0."""
+    arrs = [None if a is None else _ptr_array(a) for a in (codes_e4m3, alpha, scale)]
+    args = [None if a is None else ctypes.cast(a, ctypes.c_void_p) for a in arrs]
+    return _lib.taco_reduce_compress(own_bf16, npayloads, args[0], args[1], args[2], tokens,
+                                     hidden, block, target_energy, out_codes, out_alpha,
+                                     out_scale, stream)
 
 
 def taco_e4m3_encode(x: int, n: int, codes: int, stream: int) -> int:
@@ -207,6 +231,52 @@ def decompress_accumulate(codes, alpha, scale, acc, block: int = 256, stream=Non
                                       hidden, block, acc.data_ptr(), _stream(stream)),
            "taco_decompress_accumulate")
     return acc
+
+
+def reduce_compress(own, payloads, block: int = 256, target_energy: float = DEFAULT_TARGET_ENERGY,
+                    codes=None, alpha=None, scale=None, stream=None):
+    """Owner step: compress own + the sum of the payloads' reconstructions.
+    own: bf16 tensor or None; payloads: list of (codes, alpha, scale) as
+    returned by compress().  Returns (codes, alpha, scale)."""
+    torch = _torch()
+    ref = own if own is not None else (payloads[0][0] if payloads else None)
+    if ref is None:
+        raise ValueError("need own or at least one payload")
+    if own is not None:
+        _need(own, torch.bfloat16, "own")
+    tokens, hidden = _shape2(ref)
+    for c, a, s in payloads:
+        _need(c, torch.uint8, "payload codes")
+        _need(a, torch.float32, "payload alpha")
+        _need(s, torch.float32, "payload scale")
+        if c.numel() != ref.numel():
+            raise ValueError("every payload must have as many codes as own has elements")
+    m = taco_num_blocks(tokens, hidden, block)
+    if m < 0:
+        m = 0
+    if codes is None:
+        codes = torch.empty(ref.shape, dtype=torch.uint8, device=ref.device)
+    if alpha is None:
+        alpha = torch.empty(m, dtype=torch.float32, device=ref.device)
+    if scale is None:
+        scale = torch.empty(m, dtype=torch.float32, device=ref.device)
+    _need(codes, torch.uint8, "codes")
+    _need(alpha, torch.float32, "alpha")
+    _need(scale, torch.float32, "scale")
+    for _, a, s in payloads:
+        if a.numel() < m or s.numel() < m:
+            raise ValueError("payload alpha / scale hold fewer than numel / block entries")
+    if codes.numel() != ref.numel() or alpha.numel() < m or scale.numel() < m:
+        raise ValueError("output buffers are too small")
+    n = len(payloads)
+    _check(taco_reduce_compress(0 if own is None else own.data_ptr(), n,
+                                [c.data_ptr() for c, _, _ in payloads] if n else None,
+                                [a.data_ptr() for _, a, _ in payloads] if n else None,
+                                [s.data_ptr() for _, _, s in payloads] if n else None,
+                                tokens, hidden, block, float(target_energy), codes.data_ptr(),
+                                alpha.data_ptr(), scale.data_ptr(), _stream(stream)),
+           "taco_reduce_compress")
+    return codes, alpha, scale
 
 
 def e4m3_encode(x, out=None, stream=None):

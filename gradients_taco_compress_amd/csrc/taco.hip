@@ -323,12 +323,27 @@ __device__ __forceinline__ float max_abs(const float (&v)[EPL]) {
     return m0;
 }
 
+// Q / m as an unevaluated sum hi + lo (|lo| <= ulp(hi)): the hardware
+// reciprocal refined by one Newton step gives hi, and the exact residual
+// Q - m hi (one fma) divided by m gives lo.  m must be a positive normal.
+struct Quot { float hi, lo; };
+__device__ __forceinline__ Quot quotient(float q, float m) {
+    const float rc = __builtin_amdgcn_rcpf(m);
+    const float q0 = q * rc;
+    const float hi = fmaf(fmaf(-m, q0, q), rc, q0);
+    const float lo = fmaf(-m, hi, q) * rc;
+    return {hi, lo};
+}
+
 // Packs 8 values into 8 E4M3 codes (little-endian: element j in byte j).
-__device__ __forceinline__ u2v encode8(const float *v, float r) {
-    // fma(.., 0) maps an exact zero of either sign to +0 (code 0x00).
+// The argument of the conversion is v * (hi + lo) with a single final
+// rounding, i.e. float32 of v * Q / m almost always correctly rounded; the
+// +0 addend of the inner fma maps an exact zero of either sign to +0 (code
+// 0x00).
+__device__ __forceinline__ u2v encode8(const float *v, Quot r) {
     float q[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) q[j] = fmaf(v[j], r, 0.0f);
+    for (int j = 0; j < 8; ++j) q[j] = fmaf(v[j], r.hi, fmaf(v[j], r.lo, 0.0f));
     int lo = __builtin_amdgcn_cvt_pk_fp8_f32(q[0], q[1], 0, false);
     lo = __builtin_amdgcn_cvt_pk_fp8_f32(q[2], q[3], lo, true);
     int hi = __builtin_amdgcn_cvt_pk_fp8_f32(q[4], q[5], 0, false);
@@ -463,12 +478,10 @@ __global__ __launch_bounds__(kGroup) void compress_kernel(
             for (int i = 0; i < G::EPL; ++i) v[i] *= kTinyShift;
             m *= kTinyShift;
         }
-        // [TACO] Eq. 10: Z / s = Q * R / max|R|.  Q / max|R| from the
-        // hardware reciprocal refined by one Newton step on the quotient.
-        const float rc = __builtin_amdgcn_rcpf(m);
-        const float q0 = TACO_QMAX * rc;
-        const float q1 = fmaf(fmaf(-m, q0, TACO_QMAX), rc, q0);
-        const float r = (m > 0.0f) ? q1 * lane_sign : 0.0f;
+        // [TACO] Eq. 10: Z / s = Q * R / max|R|.
+        Quot r = quotient(TACO_QMAX, m);
+        r.hi = (m > 0.0f) ? r.hi * lane_sign : 0.0f;
+        r.lo = (m > 0.0f) ? r.lo * lane_sign : 0.0f;
 
         if (active) {
             uint8_t *cq = codes + step * (G::BPW * B) + lane_elem;
@@ -576,6 +589,152 @@ __global__ __launch_bounds__(kGroup) void decompress_kernel(
     }
 }
 
+// ------------------------------------------------------ owner step -------
+
+// Device pointers of the received payloads, passed by value.
+struct Payloads {
+    const uint8_t *codes[TACO_MAX_PAYLOADS];
+    const float *alpha[TACO_MAX_PAYLOADS];
+    const float *scale[TACO_MAX_PAYLOADS];
+};
+
+// Owner step of the two-shot all-reduce ([TACO] section 4.4.2): compress
+// X = own + sum_p G'_p without materialising X.  With H H = B I,
+// H G'_p = sqrt(B) (s_p / alpha_p) decode(q_p), so
+//     H X = H own + sum_p sqrt(B) (s_p / alpha_p) decode(q_p):
+// one transform (of own) plus one multiply-add per payload element, all in
+// the rotated domain.  The block energy follows from Parseval,
+// sum X^2 = sum (H X)^2 / B, and Eq. 6-10 proceed as in compress_kernel.
+template <int B, int P>
+__global__ __launch_bounds__(kGroup) void reduce_compress_kernel(
+    const uint16_t *__restrict__ own, Payloads pay, int64_t nblocks, float tau,
+    uint8_t *__restrict__ codes, float *__restrict__ alpha, float *__restrict__ scale) {
+    using G = Geo<B>;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int t = lane_sub<G::LPB>(lane);
+    const int g = lane_slot<G::LPB>(lane);
+    const float sg1 = (lane & 1) ? -1.0f : 1.0f;
+    const float sg2 = (lane & 2) ? -1.0f : 1.0f;
+    const float sg8 = (lane & 8) ? -1.0f : 1.0f;
+    const float lane_sign = (__popc(t) & 1) ? -1.0f : 1.0f;
+    constexpr float kScaleFactor = (float)(inv_sqrt(B) / 448.0);
+    // sqrt(B) = kSqrtBHi + kSqrtBLo to about 2^-48.
+    constexpr float kSqrtBHi = (float)(1.0 / inv_sqrt(B));
+    constexpr float kSqrtBLo = (float)(1.0 / inv_sqrt(B) - (double)kSqrtBHi);
+    // mean(X^2) = sum over the block of (H X)^2 / B^2.
+    constexpr float kInvB2 = 1.0f / ((float)B * (float)B);
+    const bool has_own = own != nullptr;
+
+    const int64_t nsteps = (nblocks + G::BPW - 1) / G::BPW;
+    const int64_t wave0 = (int64_t)blockIdx.x * kWavesPerGroup +
+                          __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t nwaves = (int64_t)gridDim.x * kWavesPerGroup;
+    const uint32_t lane_elem = (uint32_t)(g * B + 8 * t);
+
+    for (int64_t step = wave0; step < nsteps; step += nwaves) {
+        // Slots past the last block re-read the last block and store nothing.
+        const int64_t left = nblocks - step * G::BPW;
+        const uint32_t off = left >= G::BPW ? lane_elem
+                                            : (uint32_t)((g < left ? g : (int)left - 1) * B + 8 * t);
+        const int64_t base = step * (G::BPW * B);
+        const int64_t lblk = (base + off) / B;
+
+        // Loads: own (bf16) and every payload's codes and scalars.
+        u4v xo[G::CH];
+        if (has_own) {
+#pragma unroll
+            for (int k = 0; k < G::CH; ++k) xo[k] = ld16(own + base + off + k * G::SPAN);
+        }
+        u2v qc[P > 0 ? P : 1][G::CH];
+        float wa[P > 0 ? P : 1], ws[P > 0 ? P : 1];
+#pragma unroll
+        for (int p = 0; p < P; ++p) {
+#pragma unroll
+            for (int k = 0; k < G::CH; ++k) qc[p][k] = ld8(pay.codes[p] + base + off + k * G::SPAN);
+            wa[p] = pay.alpha[p][lblk];
+            ws[p] = pay.scale[p][lblk];
+        }
+
+        float v[G::EPL];
+        if (has_own) {
+#pragma unroll
+            for (int k = 0; k < G::CH; ++k) unpack8(xo[k], &v[8 * k]);
+            fwht_block<G::LPB, G::EPL>(v, sg1, sg2, sg8);          // H own (lane-signed)
+        } else {
+#pragma unroll
+            for (int i = 0; i < G::EPL; ++i) v[i] = 0.0f;
+        }
+#pragma unroll
+        for (int p = 0; p < P; ++p) {
+            // c = sqrt(B) s_p / alpha_p (with the lane sign of the stored
+            // layout) as hi + lo, added high part first: each fma then
+            // rounds relative to the running sum, so a payload that nearly
+            // cancels own keeps the precision of the result.
+            Quot sa = {0.0f, 0.0f};
+            if (ws[p] > 0.0f)   // (a subnormal alpha would overflow the reciprocal)
+                sa = wa[p] >= 0x1p-120f ? quotient(ws[p], wa[p]) : Quot{ws[p] / wa[p], 0.0f};
+            const float ch = kSqrtBHi * sa.hi;
+            const float cl = fmaf(kSqrtBHi, sa.hi, -ch) + fmaf(kSqrtBHi, sa.lo, kSqrtBLo * sa.hi);
+            const float chs = ch * lane_sign, cls = cl * lane_sign;
+            float d[G::EPL];
+#pragma unroll
+            for (int k = 0; k < G::CH; ++k) decode8(qc[p][k], &d[8 * k]);
+#pragma unroll
+            for (int i = 0; i < G::EPL; ++i) v[i] = fmaf(d[i], cls, fmaf(d[i], chs, v[i]));
+        }
+
+        // Eq. 6 via Parseval.
+        float e0 = 0.0f, e1 = 0.0f;
+#pragma unroll
+        for (int i = 0; i < G::EPL; i += 2) {
+            e0 = fmaf(v[i], v[i], e0);
+            e1 = fmaf(v[i + 1], v[i + 1], e1);
+        }
+        float energy = block_sum<G::LPB>(e0 + e1);
+        float unshift = 1.0f;
+        if (__builtin_expect(energy >= kBigEnergy, 0)) {
+            // Work on (H X) * 2^-64 (exact), undoing the factor in alpha.
+            e0 = 0.0f;
+            e1 = 0.0f;
+#pragma unroll
+            for (int i = 0; i < G::EPL; i += 2) {
+                v[i] *= kBigShift;
+                v[i + 1] *= kBigShift;
+                e0 = fmaf(v[i], v[i], e0);
+                e1 = fmaf(v[i + 1], v[i + 1], e1);
+            }
+            energy = block_sum<G::LPB>(e0 + e1);
+            unshift = kBigUnshift;
+        }
+        // Eq. 7.
+        const float a = tau * __builtin_amdgcn_rsqf(energy * kInvB2 + TACO_EPS);
+        // Eq. 9-10 exactly as in compress_kernel.
+        float m = block_max<G::LPB>(max_abs<G::EPL>(v));
+        const float s = a * m * kScaleFactor;
+        if (__builtin_expect(m < kTinyMax && m > 0.0f, 0)) {
+#pragma unroll
+            for (int i = 0; i < G::EPL; ++i) v[i] *= kTinyShift;
+            m *= kTinyShift;
+        }
+        // As in compress_kernel, v holds lane_sign * (H X), so r carries the
+        // lane sign too.
+        Quot r = quotient(TACO_QMAX, m);
+        r.hi = (m > 0.0f) ? r.hi * lane_sign : 0.0f;
+        r.lo = (m > 0.0f) ? r.lo * lane_sign : 0.0f;
+
+        const int64_t blk = step * G::BPW + g;
+        if (blk < nblocks) {
+            uint8_t *cq = codes + base + lane_elem;
+#pragma unroll
+            for (int k = 0; k < G::CH; ++k) st8(cq + k * G::SPAN, encode8(&v[8 * k], r));
+            if (t == 0) {
+                alpha[blk] = a * unshift;
+                scale[blk] = s;
+            }
+        }
+    }
+}
+
 // ------------------------------------------------------------- codec ------
 
 __global__ __launch_bounds__(kGroup) void e4m3_encode_kernel(const float *__restrict__ x, int64_t n,
@@ -665,6 +824,31 @@ taco_status decompress_launch(const uint8_t *codes, const float *alpha, const fl
     const int64_t nsteps = (nblocks + Geo<B>::BPW - 1) / Geo<B>::BPW;
     return launch(reinterpret_cast<const void *>(&decompress_kernel<B, MODE>), grid_for(nsteps),
                   stream, codes, alpha, scale, nblocks, y, acc);
+}
+
+template <int B, int P>
+taco_status reduce_launch(const uint16_t *own, const Payloads &pay, int64_t nblocks, float tau,
+                          uint8_t *codes, float *alpha, float *scale, hipStream_t stream) {
+    const int64_t nsteps = (nblocks + Geo<B>::BPW - 1) / Geo<B>::BPW;
+    return launch(reinterpret_cast<const void *>(&reduce_compress_kernel<B, P>), grid_for(nsteps),
+                  stream, own, pay, nblocks, tau, codes, alpha, scale);
+}
+
+template <int B>
+taco_status reduce_dispatch(int npay, const uint16_t *own, const Payloads &pay, int64_t nblocks,
+                            float tau, uint8_t *codes, float *alpha, float *scale,
+                            hipStream_t stream) {
+    switch (npay) {
+        case 0: return reduce_launch<B, 0>(own, pay, nblocks, tau, codes, alpha, scale, stream);
+        case 1: return reduce_launch<B, 1>(own, pay, nblocks, tau, codes, alpha, scale, stream);
+        case 2: return reduce_launch<B, 2>(own, pay, nblocks, tau, codes, alpha, scale, stream);
+        case 3: return reduce_launch<B, 3>(own, pay, nblocks, tau, codes, alpha, scale, stream);
+        case 4: return reduce_launch<B, 4>(own, pay, nblocks, tau, codes, alpha, scale, stream);
+        case 5: return reduce_launch<B, 5>(own, pay, nblocks, tau, codes, alpha, scale, stream);
+        case 6: return reduce_launch<B, 6>(own, pay, nblocks, tau, codes, alpha, scale, stream);
+        case 7: return reduce_launch<B, 7>(own, pay, nblocks, tau, codes, alpha, scale, stream);
+        default: return reduce_launch<B, 8>(own, pay, nblocks, tau, codes, alpha, scale, stream);
+    }
 }
 
 // Shared validation of the decompress-side calls.
@@ -758,6 +942,59 @@ taco_status taco_decompress_accumulate(const uint8_t *codes_e4m3, const float *a
     }
 }
 
+taco_status taco_reduce_compress(const uint16_t *own_bf16, int32_t npayloads,
+                                 const uint8_t *const *codes_e4m3, const float *const *alpha,
+                                 const float *const *scale, int64_t tokens, int64_t hidden,
+                                 int32_t block, float target_energy, uint8_t *out_codes,
+                                 float *out_alpha, float *out_scale, hipStream_t stream) {
+    const int64_t n = numel(tokens, hidden);
+    if (n < 0) return TACO_ERR_SHAPE;
+    if (!valid_block(block)) return TACO_ERR_BLOCK;
+    if (n % block) return TACO_ERR_SHAPE;
+    if (!(target_energy > 0.0f) || !(target_energy <= TACO_MAX_TARGET_ENERGY)) return TACO_ERR_PARAM;
+    if (npayloads < 0 || npayloads > TACO_MAX_PAYLOADS) return TACO_ERR_PARAM;
+    if (npayloads == 0 && !own_bf16) return TACO_ERR_PARAM;
+    if (n == 0) return TACO_OK;
+    if (!out_codes || !out_alpha || !out_scale) return TACO_ERR_NULL;
+    if (npayloads > 0 && (!codes_e4m3 || !alpha || !scale)) return TACO_ERR_NULL;
+    const int64_t m = n / block;
+    const size_t nc = (size_t)n, nb = (size_t)m * sizeof(float);
+    if (!aligned(out_codes, 16) || !aligned(out_alpha, 4) || !aligned(out_scale, 4)) return TACO_ERR_ALIGN;
+    if (overlap(out_codes, nc, out_alpha, nb) || overlap(out_codes, nc, out_scale, nb) ||
+        overlap(out_alpha, nb, out_scale, nb))
+        return TACO_ERR_ALIAS;
+    if (own_bf16) {
+        if (!aligned(own_bf16, 16)) return TACO_ERR_ALIGN;
+        const size_t no = (size_t)n * 2;
+        if (overlap(out_codes, nc, own_bf16, no) || overlap(out_alpha, nb, own_bf16, no) ||
+            overlap(out_scale, nb, own_bf16, no))
+            return TACO_ERR_ALIAS;
+    }
+    Payloads pay = {};
+    for (int p = 0; p < npayloads; ++p) {
+        const uint8_t *c = codes_e4m3[p];
+        const float *a = alpha[p], *sc = scale[p];
+        if (!c || !a || !sc) return TACO_ERR_NULL;
+        if (!aligned(c, 16) || !aligned(a, 4) || !aligned(sc, 4)) return TACO_ERR_ALIGN;
+        const void *ins[3] = {c, a, sc};
+        const size_t lens[3] = {nc, nb, nb};
+        for (int i = 0; i < 3; ++i)
+            if (overlap(out_codes, nc, ins[i], lens[i]) || overlap(out_alpha, nb, ins[i], lens[i]) ||
+                overlap(out_scale, nb, ins[i], lens[i]))
+                return TACO_ERR_ALIAS;
+        pay.codes[p] = c;
+        pay.alpha[p] = a;
+        pay.scale[p] = sc;
+    }
+    switch (block) {
+        case 32: return reduce_dispatch<32>(npayloads, own_bf16, pay, m, target_energy, out_codes, out_alpha, out_scale, stream);
+        case 64: return reduce_dispatch<64>(npayloads, own_bf16, pay, m, target_energy, out_codes, out_alpha, out_scale, stream);
+        case 128: return reduce_dispatch<128>(npayloads, own_bf16, pay, m, target_energy, out_codes, out_alpha, out_scale, stream);
+        case 256: return reduce_dispatch<256>(npayloads, own_bf16, pay, m, target_energy, out_codes, out_alpha, out_scale, stream);
+        default: return reduce_dispatch<512>(npayloads, own_bf16, pay, m, target_energy, out_codes, out_alpha, out_scale, stream);
+    }
+}
+
 taco_status taco_e4m3_encode(const float *x, int64_t n, uint8_t *codes, hipStream_t stream) {
     if (n < 0) return TACO_ERR_SHAPE;
     if (n == 0) return TACO_OK;
@@ -788,7 +1025,7 @@ const char *taco_status_string(taco_status status) {
         case TACO_ERR_NULL: return "a required pointer is NULL";
         case TACO_ERR_SHAPE: return "bad shape: tokens < 0, hidden <= 0, or N not a multiple of the block";
         case TACO_ERR_BLOCK: return "block size must be 32, 64, 128, 256 or 512";
-        case TACO_ERR_PARAM: return "target energy must be finite and in (0, 1e20]";
+        case TACO_ERR_PARAM: return "target energy must be finite and in (0, 1e20], and the payload count in 0..8 (0 only with own data)";
         case TACO_ERR_ALIGN: return "tensors must be 16-byte aligned, alpha and scale 4-byte aligned";
         case TACO_ERR_ALIAS: return "an output buffer overlaps an input or another output";
         case TACO_ERR_HIP: return "the HIP runtime refused the kernel launch";

@@ -65,12 +65,17 @@ extern "C" {
  * an all-zero block (sigma = sqrt(eps)). */
 #define TACO_MAX_TARGET_ENERGY 1e20f
 
+/* Most received payloads one taco_reduce_compress call sums (tensor
+ * parallelism up to 9 ranks). */
+#define TACO_MAX_PAYLOADS 8
+
 typedef enum {
     TACO_OK = 0,
     TACO_ERR_NULL = 1,   /* a required pointer is NULL                          */
     TACO_ERR_SHAPE = 2,  /* tokens < 0, hidden <= 0, N overflows, N % block != 0 */
     TACO_ERR_BLOCK = 3,  /* block is not one of 32, 64, 128, 256, 512            */
-    TACO_ERR_PARAM = 4,  /* target_energy not finite or outside (0, 1e20]        */
+    TACO_ERR_PARAM = 4,  /* target_energy not finite or outside (0, 1e20], or a
+                            payload count outside 0..TACO_MAX_PAYLOADS          */
     TACO_ERR_ALIGN = 5,  /* a tensor is not 16-byte aligned, or alpha / scale
                             not 4-byte aligned                                  */
     TACO_ERR_ALIAS = 6,  /* an output buffer overlaps an input or another output */
@@ -118,6 +123,32 @@ taco_status taco_decompress_accumulate(const uint8_t *codes_e4m3, const float *a
                                        const float *scale, int64_t tokens,
                                        int64_t hidden, int32_t block, float *acc_f32,
                                        hipStream_t stream);
+
+/*
+ * Owner step of the two-shot all-reduce ([TACO] section 4.4.2: the
+ * reduce-scatter phase is one compressed all-to-all followed by a single
+ * local reduction, and the reduced segment is compressed again for the
+ * all-gather).  Computes the codes, alpha and s ([TACO] Eq. 5-10) of
+ *     X = own + sum_p G'_p,     G'_p = the reconstruction (Eq. 11-13) of payload p,
+ * in one pass and without materialising X or any G'_p.
+ *   own_bf16     [tokens*hidden] bf16, 16-byte aligned, or NULL (X = sum of
+ *                the payloads).
+ *   npayloads    0..TACO_MAX_PAYLOADS (0 needs own_bf16).
+ *   codes_e4m3, alpha, scale
+ *                HOST arrays of npayloads DEVICE pointers: payload p is
+ *                (codes_e4m3[p] [tokens*hidden], alpha[p] [M], scale[p] [M])
+ *                as produced by taco_compress with the same shape and block.
+ *   out_codes, out_alpha, out_scale
+ *                outputs as in taco_compress; they must not overlap any input
+ *                or each other.
+ * Rounding differs from decompressing, summing and compressing separately
+ * only by float32 evaluation order.
+ */
+taco_status taco_reduce_compress(const uint16_t *own_bf16, int32_t npayloads,
+                                 const uint8_t *const *codes_e4m3, const float *const *alpha,
+                                 const float *const *scale, int64_t tokens, int64_t hidden,
+                                 int32_t block, float target_energy, uint8_t *out_codes,
+                                 float *out_alpha, float *out_scale, hipStream_t stream);
 
 /*
  * The E4M3 conversions the kernels above use (Cvt_FP8 of [TACO] Eq. 10 and

@@ -33,6 +33,7 @@ def lib():
     L.taco_compress.argtypes = [P, I64, I64, I32, F32, P, P, P, P]
     L.taco_decompress.argtypes = [P, P, P, I64, I64, I32, P, P]
     L.taco_decompress_accumulate.argtypes = [P, P, P, I64, I64, I32, P, P]
+    L.taco_reduce_compress.argtypes = [P, I32, P, P, P, I64, I64, I32, F32, P, P, P, P]
     L.taco_e4m3_encode.argtypes = [P, I64, P, P]
     L.taco_e4m3_decode.argtypes = [P, I64, P, P]
     L.taco_status_string.argtypes = [ctypes.c_int]
@@ -42,7 +43,7 @@ def lib():
 
 def test_every_declared_function_is_exported(lib):
     names = declared_functions()
-    assert len(names) == 7, names
+    assert len(names) == 8, names
     for n in names:
         assert hasattr(lib, n), n
     out = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True).stdout
@@ -140,3 +141,37 @@ def test_codec_validation(lib):
     assert lib.taco_e4m3_decode(A, 16, None, None) == NULL
     assert lib.taco_e4m3_decode(A, 16, A, None) == ALIAS
     assert lib.taco_e4m3_decode(A + 1, 16, 2 * A, None) == ALIGN
+
+
+def reduce_call(lib, own=A, npay=2, codes=(5 * A, 6 * A), alpha=(7 * A, 8 * A),
+                scale=(9 * A, 10 * A), tokens=4, hidden=256, block=128, tau=1.0,
+                out_codes=2 * A, out_alpha=3 * A, out_scale=4 * A):
+    arr = ctypes.c_void_p * 8
+    c = None if codes is None else ctypes.cast(arr(*codes), ctypes.c_void_p)
+    a = None if alpha is None else ctypes.cast(arr(*alpha), ctypes.c_void_p)
+    s = None if scale is None else ctypes.cast(arr(*scale), ctypes.c_void_p)
+    return lib.taco_reduce_compress(own, npay, c, a, s, tokens, hidden, block, tau,
+                                    out_codes, out_alpha, out_scale, None)
+
+
+def test_reduce_compress_validation(lib):
+    assert reduce_call(lib, tokens=-1) == SHAPE
+    assert reduce_call(lib, tokens=3, hidden=96) == SHAPE
+    assert reduce_call(lib, block=96) == BLOCK
+    assert reduce_call(lib, tau=0.0) == PARAM
+    assert reduce_call(lib, npay=9) == PARAM
+    assert reduce_call(lib, npay=-1) == PARAM
+    assert reduce_call(lib, own=None, npay=0) == PARAM
+    assert reduce_call(lib, out_codes=None) == NULL
+    assert reduce_call(lib, codes=None) == NULL
+    assert reduce_call(lib, codes=(5 * A, None)) == NULL
+    assert reduce_call(lib, own=A + 8) == ALIGN
+    assert reduce_call(lib, codes=(5 * A, 6 * A + 4)) == ALIGN
+    assert reduce_call(lib, scale=(9 * A + 2, 10 * A)) == ALIGN
+    assert reduce_call(lib, out_codes=A + 256) == ALIAS          # overlaps own
+    assert reduce_call(lib, out_alpha=5 * A + 64) == ALIAS       # overlaps payload 0 codes
+    assert reduce_call(lib, out_scale=8 * A) == ALIAS            # overlaps payload 1 alpha
+    assert reduce_call(lib, out_scale=3 * A + 4) == ALIAS        # overlaps out_alpha
+    # Empty tensors: a no-op once the arguments that do not depend on N are valid.
+    assert reduce_call(lib, tokens=0, out_codes=None, out_alpha=None, out_scale=None) == OK
+    assert reduce_call(lib, own=None, npay=1, tokens=0) == OK   # own is optional

@@ -317,3 +317,11 @@ def test_deterministic_and_stream_ordered(taco):
     torch.cuda.synchronize()
     assert torch.equal(c1, c2) and torch.equal(a1, a2) and torch.equal(s1, s2)
     assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
+
+
+def test_aggregate_flip_rate():
+    """All code comparisons of this session together: at most 1e-5 flips."""
+    import parity
+    t = parity.TOTALS
+    print(f"session total: {t['flips']} flips in {t['n']} elements", flush=True)
+    assert t["flips"] <= parity.FLIP_RATE * max(t["n"], 1)
