@@ -244,6 +244,35 @@ def roundtrip_noquant(x_bits, block: int, tau: float = 1.0, eps: float = EPS) ->
     return out
 
 
+# ---------------------------------------------------- wire layout -------
+
+def pack(codes, alpha, scale, block: int) -> np.ndarray:
+    """Interleaved wire layout of TACO section 4.4.2 (alpha_k and s_k stored
+    contiguously with block k's FP8 payload): one record of block + 8 bytes
+    per block, the block's codes followed by alpha_k and s_k as
+    little-endian float32 (Algorithm 1 communicates the tuple in the order
+    (q_k, alpha_k, s_k)).  Returns uint8 [M, block + 8]."""
+    c = np.ascontiguousarray(codes, dtype=np.uint8).reshape(-1)
+    a = np.ascontiguousarray(alpha, dtype='<f4').reshape(-1)
+    s = np.ascontiguousarray(scale, dtype='<f4').reshape(-1)
+    m = a.size
+    assert c.size == m * block and s.size == m
+    out = np.empty((m, block + 8), np.uint8)
+    out[:, :block] = c.reshape(m, block)
+    out[:, block:block + 4] = a.view(np.uint8).reshape(m, 4)
+    out[:, block + 4:] = s.view(np.uint8).reshape(m, 4)
+    return out
+
+
+def unpack(payload, block: int):
+    """(codes [M*block], alpha [M], scale [M]) of an interleaved payload."""
+    p = np.ascontiguousarray(payload, dtype=np.uint8).reshape(-1, block + 8)
+    codes = p[:, :block].reshape(-1).copy()
+    alpha = p[:, block:block + 4].copy().view('<f4').reshape(-1).astype(np.float32)
+    scale = p[:, block + 4:].copy().view('<f4').reshape(-1).astype(np.float32)
+    return codes, alpha, scale
+
+
 # ------------------------------------------------------------ helpers ----
 
 def bf16_bits_to_f64(bits) -> np.ndarray:
