@@ -18,7 +18,8 @@ the dominant kernel and the CPU oracle's rate on the same workload.
     python bench.py --all --out results.json     # every workload (stderr table)
 
 ``NAME:owner`` times the fused owner step of the two-shot all-reduce
-(``taco_reduce_compress`` of an own partial plus three payloads) instead.
+(``taco_reduce_compress`` of an own partial plus three payloads) instead;
+``NAME:packed`` the round trip through the interleaved wire layout.
 """
 from __future__ import annotations
 
@@ -177,6 +178,55 @@ def roundtrip_case(torch, taco, synth, name: str, block: int, steps: int, warmup
             "input_bytes_step": 2.0 * n, "kernels": {"compress": t_c, "decompress": t_d}}
 
 
+def packed_case(torch, taco, synth, name: str, block: int, steps: int, warmup: int,
+                use_graph: bool):
+    """Round trip through the interleaved wire layout (one payload buffer per
+    direction, codes and scalars together)."""
+    import numpy as np
+    r = synth.WORKLOADS[name]
+    n = r.numel
+    m = n // block
+    x0 = torch.from_numpy(synth.generate(r).view(np.int16)).cuda().view(torch.bfloat16)
+    nbytes = taco.taco_packed_bytes(r.rows, r.cols, block)
+    per_set = 2 * n + nbytes + 2 * n
+    nsets = max(1, -(-ROTATE_BYTES // per_set))
+    sets = [(x0.clone(), torch.empty(nbytes, dtype=torch.uint8, device="cuda"),
+             torch.empty((r.rows, r.cols), dtype=torch.bfloat16, device="cuda")) for _ in range(nsets)]
+    del x0
+
+    def run_steps():
+        for x, pay, y in sets:
+            taco.compress_packed(x, block=block, payload=pay)
+            taco.decompress_packed(pay, y.shape, block=block, out=y)
+
+    def run_compress():
+        for x, pay, _ in sets:
+            taco.compress_packed(x, block=block, payload=pay)
+
+    def run_decompress():
+        for _, pay, y in sets:
+            taco.decompress_packed(pay, y.shape, block=block, out=y)
+
+    for _ in range(max(1, warmup // nsets)):
+        run_steps()
+    torch.cuda.synchronize()
+    step_fn = make_graph(torch, run_steps, use_graph)
+    comp_fn = make_graph(torch, run_compress, use_graph)
+    dec_fn = make_graph(torch, run_decompress, use_graph)
+    reps = max(1, -(-steps // nsets))
+    timer = Timer(torch)
+    step_fn()
+    k = reps * nsets
+    t_steps = timer.time(step_fn, reps)
+    t_c = timer.time(comp_fn, reps) / k
+    t_d = timer.time(dec_fn, reps) / k
+    return {"n": n, "block": block, "steps": k, "t_step": t_steps / k, "sets": nsets,
+            "rows": r.rows, "cols": r.cols, "packed": True,
+            "bytes_step": algorithmic_bytes("compress", n, block)
+            + algorithmic_bytes("decompress", n, block),
+            "input_bytes_step": 2.0 * n, "kernels": {"compress": t_c, "decompress": t_d}}
+
+
 def accumulate_case(torch, taco, synth, name: str, block: int, steps: int, warmup: int,
                     use_graph: bool):
     import numpy as np
@@ -319,7 +369,9 @@ def record(res, name: str, args, cpu=None):
                    "block": res["block"], "target_energy": 1.0,
                    "step": ("4x compress + 4x decompress_accumulate" if "t_accumulate" in res
                             else f"reduce_compress of own + {res['npayloads']} payloads"
-                            if "npayloads" in res else "compress + decompress"),
+                            if "npayloads" in res
+                            else "compress_packed + decompress_packed" if res.get("packed")
+                            else "compress + decompress"),
                    "buffer_sets": res["sets"], "graph": not args.no_graph},
         "pct_hbm_peak": round(100.0 * res["bytes_step"] / t_step / 1e9 / HBM_PEAK_GBS, 2),
         "kernel_us": {k: round(v * 1e6, 3) for k, v in res["kernels"].items()},
@@ -366,7 +418,8 @@ def main():
         cases = [("laplace_2048x1024", 128), ("gpt2.7b_rowpar_8192x2560", 128),
                  ("qwen7b_act_16384x3584", 128), ("qwen7b_act_16384x3584", 256),
                  ("grad_8192x8192", 256), ("gpt175b_hidden_32768x12288", 256),
-                 ("gpt175b_hidden_32768x12288:owner", 256)]
+                 ("gpt175b_hidden_32768x12288:owner", 256),
+                 ("gpt2.7b_rowpar_8192x2560:packed", 128)]
     else:
         name = args.workload or synth.DEFAULT_WORKLOAD
         block = args.block or synth.WORKLOADS[name.split(":")[0]].blocks[0]
@@ -380,6 +433,9 @@ def main():
             name = name.split(":")[0]
             res = owner_case(torch, taco, synth, name, block, steps, args.warmup, use_graph)
             acc = False
+        elif name.endswith(":packed"):
+            name = name.split(":")[0]
+            res = packed_case(torch, taco, synth, name, block, steps, args.warmup, use_graph)
         elif acc:
             res = accumulate_case(torch, taco, synth, name, block, steps, args.warmup, use_graph)
         else:

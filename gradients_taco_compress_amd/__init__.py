@@ -8,12 +8,14 @@ the library has not been built (``python -m gradients_taco_compress_amd.build``)
 Two layers:
 
 * ``taco_compress``, ``taco_decompress``, ``taco_decompress_accumulate``,
-  ``taco_reduce_compress``, ``taco_e4m3_encode``, ``taco_e4m3_decode``,
-  ``taco_num_blocks``, ``taco_status_string``: the C ABI of ``include/taco.h``
+  ``taco_reduce_compress``, their ``*_packed`` forms, ``taco_packed_bytes``,
+  ``taco_e4m3_encode``, ``taco_e4m3_decode``, ``taco_num_blocks``,
+  ``taco_status_string``: the C ABI of ``include/taco.h``
   with the same names and arguments (device pointers as ints, stream handle
   as int, pointer arrays as sequences of ints).
 * ``compress``, ``decompress``, ``decompress_accumulate``, ``reduce_compress``,
-  ``e4m3_encode``, ``e4m3_decode``: the same calls on torch tensors,
+  their ``*_packed`` forms on interleaved payloads, ``e4m3_encode``,
+  ``e4m3_decode``: the same calls on torch tensors,
   allocating outputs when none are given and launching on torch's current
   stream.
 """
@@ -61,6 +63,16 @@ _lib.taco_decompress_accumulate.argtypes = [_P, _P, _P, _I64, _I64, _I32, _P, _P
 _lib.taco_decompress_accumulate.restype = ctypes.c_int
 _lib.taco_reduce_compress.argtypes = [_P, _I32, _P, _P, _P, _I64, _I64, _I32, _F32, _P, _P, _P, _P]
 _lib.taco_reduce_compress.restype = ctypes.c_int
+_lib.taco_packed_bytes.argtypes = [_I64, _I64, _I32]
+_lib.taco_packed_bytes.restype = _I64
+_lib.taco_compress_packed.argtypes = [_P, _I64, _I64, _I32, _F32, _P, _P]
+_lib.taco_compress_packed.restype = ctypes.c_int
+_lib.taco_decompress_packed.argtypes = [_P, _I64, _I64, _I32, _P, _P]
+_lib.taco_decompress_packed.restype = ctypes.c_int
+_lib.taco_decompress_accumulate_packed.argtypes = [_P, _I64, _I64, _I32, _P, _P]
+_lib.taco_decompress_accumulate_packed.restype = ctypes.c_int
+_lib.taco_reduce_compress_packed.argtypes = [_P, _I32, _P, _I64, _I64, _I32, _F32, _P, _P]
+_lib.taco_reduce_compress_packed.restype = ctypes.c_int
 _lib.taco_e4m3_encode.argtypes = [_P, _I64, _P, _P]
 _lib.taco_e4m3_encode.restype = ctypes.c_int
 _lib.taco_e4m3_decode.argtypes = [_P, _I64, _P, _P]
@@ -70,8 +82,10 @@ _lib.taco_status_string.restype = ctypes.c_char_p
 
 #: Symbols the library exports (checked against include/taco.h by the tests).
 EXPORTS = ("taco_num_blocks", "taco_compress", "taco_decompress",
-           "taco_decompress_accumulate", "taco_reduce_compress", "taco_e4m3_encode",
-           "taco_e4m3_decode", "taco_status_string")
+           "taco_decompress_accumulate", "taco_reduce_compress", "taco_packed_bytes",
+           "taco_compress_packed", "taco_decompress_packed", "taco_decompress_accumulate_packed",
+           "taco_reduce_compress_packed", "taco_e4m3_encode", "taco_e4m3_decode",
+           "taco_status_string")
 
 #: Most payloads one taco_reduce_compress call sums.
 MAX_PAYLOADS = 8
@@ -119,6 +133,34 @@ def taco_reduce_compress(own_bf16: int, npayloads: int, codes_e4m3, alpha, scale
     return _lib.taco_reduce_compress(own_bf16, npayloads, args[0], args[1], args[2], tokens,
                                      hidden, block, target_energy, out_codes, out_alpha,
                                      out_scale, stream)
+
+
+def taco_packed_bytes(tokens: int, hidden: int, block: int) -> int:
+    return _lib.taco_packed_bytes(tokens, hidden, block)
+
+
+def taco_compress_packed(x_bf16: int, tokens: int, hidden: int, block: int, target_energy: float,
+                         payload: int, stream: int) -> int:
+    return _lib.taco_compress_packed(x_bf16, tokens, hidden, block, target_energy, payload, stream)
+
+
+def taco_decompress_packed(payload: int, tokens: int, hidden: int, block: int, y_bf16: int,
+                           stream: int) -> int:
+    return _lib.taco_decompress_packed(payload, tokens, hidden, block, y_bf16, stream)
+
+
+def taco_decompress_accumulate_packed(payload: int, tokens: int, hidden: int, block: int,
+                                      acc_f32: int, stream: int) -> int:
+    return _lib.taco_decompress_accumulate_packed(payload, tokens, hidden, block, acc_f32, stream)
+
+
+def taco_reduce_compress_packed(own_bf16: int, npayloads: int, payloads, tokens: int, hidden: int,
+                                block: int, target_energy: float, out_payload: int,
+                                stream: int) -> int:
+    """payloads: sequence of npayloads device pointers (a host array), or None."""
+    arr = None if payloads is None else ctypes.cast(_ptr_array(payloads), ctypes.c_void_p)
+    return _lib.taco_reduce_compress_packed(own_bf16, npayloads, arr, tokens, hidden, block,
+                                            target_energy, out_payload, stream)
 
 
 def taco_e4m3_encode(x: int, n: int, codes: int, stream: int) -> int:
@@ -277,6 +319,92 @@ def reduce_compress(own, payloads, block: int = 256, target_energy: float = DEFA
                                 alpha.data_ptr(), scale.data_ptr(), _stream(stream)),
            "taco_reduce_compress")
     return codes, alpha, scale
+
+
+def _packed_len(tokens, hidden, block):
+    nb = taco_packed_bytes(tokens, hidden, block)
+    if nb < 0:
+        raise TacoError(2 if block in BLOCKS else 3, "taco_packed_bytes")
+    return nb
+
+
+def compress_packed(x, block: int = 256, target_energy: float = DEFAULT_TARGET_ENERGY,
+                    payload=None, stream=None):
+    """Compress a bf16 tensor into one interleaved payload (uint8, 1-D)."""
+    torch = _torch()
+    _need(x, torch.bfloat16, "x")
+    tokens, hidden = _shape2(x)
+    nb = _packed_len(tokens, hidden, block)
+    if payload is None:
+        payload = torch.empty(nb, dtype=torch.uint8, device=x.device)
+    _need(payload, torch.uint8, "payload")
+    if payload.numel() < nb:
+        raise ValueError("payload buffer is too small")
+    _check(taco_compress_packed(x.data_ptr(), tokens, hidden, block, float(target_energy),
+                                payload.data_ptr(), _stream(stream)), "taco_compress_packed")
+    return payload
+
+
+def decompress_packed(payload, shape, block: int = 256, out=None, stream=None):
+    """Reconstruct a bf16 tensor of the given shape from an interleaved payload."""
+    torch = _torch()
+    _need(payload, torch.uint8, "payload")
+    hidden = shape[-1]
+    tokens = 1
+    for d in shape[:-1]:
+        tokens *= d
+    if payload.numel() < _packed_len(tokens, hidden, block):
+        raise ValueError("payload is too small for this shape")
+    if out is None:
+        out = torch.empty(shape, dtype=torch.bfloat16, device=payload.device)
+    _need(out, torch.bfloat16, "out")
+    _check(taco_decompress_packed(payload.data_ptr(), tokens, hidden, block, out.data_ptr(),
+                                  _stream(stream)), "taco_decompress_packed")
+    return out
+
+
+def decompress_accumulate_packed(payload, acc, block: int = 256, stream=None):
+    """acc (float32) += reconstruction of an interleaved payload."""
+    torch = _torch()
+    _need(payload, torch.uint8, "payload")
+    _need(acc, torch.float32, "acc")
+    tokens, hidden = _shape2(acc)
+    if payload.numel() < _packed_len(tokens, hidden, block):
+        raise ValueError("payload is too small for acc's shape")
+    _check(taco_decompress_accumulate_packed(payload.data_ptr(), tokens, hidden, block,
+                                             acc.data_ptr(), _stream(stream)),
+           "taco_decompress_accumulate_packed")
+    return acc
+
+
+def reduce_compress_packed(own, payloads, shape=None, block: int = 256,
+                           target_energy: float = DEFAULT_TARGET_ENERGY, out=None, stream=None):
+    """Owner step on interleaved payloads: returns one interleaved payload."""
+    torch = _torch()
+    if own is not None:
+        _need(own, torch.bfloat16, "own")
+        shape = own.shape
+    if shape is None:
+        raise ValueError("shape is required without own")
+    hidden = shape[-1]
+    tokens = 1
+    for d in shape[:-1]:
+        tokens *= d
+    nb = _packed_len(tokens, hidden, block)
+    for p in payloads:
+        _need(p, torch.uint8, "payload")
+        if p.numel() < nb:
+            raise ValueError("payload is too small for this shape")
+    dev = own.device if own is not None else payloads[0].device
+    if out is None:
+        out = torch.empty(nb, dtype=torch.uint8, device=dev)
+    _need(out, torch.uint8, "out")
+    n = len(payloads)
+    _check(taco_reduce_compress_packed(0 if own is None else own.data_ptr(), n,
+                                       [p.data_ptr() for p in payloads] if n else None,
+                                       tokens, hidden, block, float(target_energy), out.data_ptr(),
+                                       _stream(stream)), "taco_reduce_compress_packed")
+    return out
 
 
 def e4m3_encode(x, out=None, stream=None):

@@ -110,6 +110,20 @@ struct Geo {
     static_assert((LPB == 4 || LPB == 8) && EPL >= 8, "lane layout");
 };
 
+// Where block k's codes, alpha and s live.
+//  kSide:   codes[k*B .. k*B+B), alpha[k], scale[k] (three buffers).
+//  kPacked: one record of B + 8 bytes per block ([TACO] section 4.4.2, the
+//           zero-copy metadata layout): the block's codes, then alpha_k and
+//           s_k as float32; `alpha` and `scale` point at record 0's
+//           scalars, so block k's are alpha[k * kScalarStride].
+enum class Layout { kSide, kPacked };
+
+template <int B, Layout L>
+struct Wire {
+    static constexpr int64_t kRecord = (L == Layout::kPacked) ? B + 8 : B;     // bytes
+    static constexpr int64_t kScalarStride = (L == Layout::kPacked) ? (B + 8) / 4 : 1;  // floats
+};
+
 // ---------------------------------------------------------------- lanes ----
 
 template <int LPB>
@@ -391,11 +405,12 @@ constexpr float kOutUnshift = 0x1p-64f;
 
 // ----------------------------------------------------------- compress -----
 
-template <int B>
+template <int B, Layout L>
 __global__ __launch_bounds__(kGroup) void compress_kernel(
     const uint16_t *__restrict__ x, int64_t nblocks, float tau,
     uint8_t *__restrict__ codes, float *__restrict__ alpha, float *__restrict__ scale) {
     using G = Geo<B>;
+    using W = Wire<B, L>;
     const int lane = threadIdx.x & (kWave - 1);
     const int t = lane_sub<G::LPB>(lane);
     const int g = lane_slot<G::LPB>(lane);
@@ -484,12 +499,12 @@ __global__ __launch_bounds__(kGroup) void compress_kernel(
         r.lo = (m > 0.0f) ? r.lo * lane_sign : 0.0f;
 
         if (active) {
-            uint8_t *cq = codes + step * (G::BPW * B) + lane_elem;
+            uint8_t *cq = codes + blk * W::kRecord + 8 * t;
 #pragma unroll
             for (int k = 0; k < G::CH; ++k) st8(cq + k * G::SPAN, encode8(&v[8 * k], r));
             if (t == 0) {
-                alpha[step * G::BPW + g] = a * unshift;
-                scale[step * G::BPW + g] = s;
+                alpha[blk * W::kScalarStride] = a * unshift;
+                scale[blk * W::kScalarStride] = s;
             }
         }
     }
@@ -499,12 +514,13 @@ __global__ __launch_bounds__(kGroup) void compress_kernel(
 
 enum class Out { kBf16, kAccumulate };
 
-template <int B, Out MODE>
+template <int B, Out MODE, Layout L>
 __global__ __launch_bounds__(kGroup) void decompress_kernel(
     const uint8_t *__restrict__ codes, const float *__restrict__ alpha,
     const float *__restrict__ scale, int64_t nblocks, uint16_t *__restrict__ y,
     float *__restrict__ acc) {
     using G = Geo<B>;
+    using W = Wire<B, L>;
     const int lane = threadIdx.x & (kWave - 1);
     const int t = lane_sub<G::LPB>(lane);
     const int g = lane_slot<G::LPB>(lane);
@@ -525,11 +541,11 @@ __global__ __launch_bounds__(kGroup) void decompress_kernel(
     auto load = [&](int64_t step) {
         int64_t blk = step * G::BPW + g;
         blk = blk < nblocks ? blk : nblocks - 1;
-        const uint8_t *p = codes + blk * B + 8 * t;
+        const uint8_t *p = codes + blk * W::kRecord + 8 * t;
 #pragma unroll
         for (int k = 0; k < G::CH; ++k) buf[k] = ld8(p + k * G::SPAN);
-        a_buf = alpha[blk];
-        s_buf = scale[blk];
+        a_buf = alpha[blk * W::kScalarStride];
+        s_buf = scale[blk * W::kScalarStride];
     };
 
     if (wave0 < nsteps) load(wave0);
@@ -605,11 +621,12 @@ struct Payloads {
 // one transform (of own) plus one multiply-add per payload element, all in
 // the rotated domain.  The block energy follows from Parseval,
 // sum X^2 = sum (H X)^2 / B, and Eq. 6-10 proceed as in compress_kernel.
-template <int B, int P>
+template <int B, int P, Layout L>
 __global__ __launch_bounds__(kGroup) void reduce_compress_kernel(
     const uint16_t *__restrict__ own, Payloads pay, int64_t nblocks, float tau,
     uint8_t *__restrict__ codes, float *__restrict__ alpha, float *__restrict__ scale) {
     using G = Geo<B>;
+    using W = Wire<B, L>;
     const int lane = threadIdx.x & (kWave - 1);
     const int t = lane_sub<G::LPB>(lane);
     const int g = lane_slot<G::LPB>(lane);
@@ -638,6 +655,8 @@ __global__ __launch_bounds__(kGroup) void reduce_compress_kernel(
                                             : (uint32_t)((g < left ? g : (int)left - 1) * B + 8 * t);
         const int64_t base = step * (G::BPW * B);
         const int64_t lblk = (base + off) / B;
+        const uint32_t coff = (uint32_t)(lblk - step * G::BPW) * (uint32_t)W::kRecord + 8 * t;
+        const int64_t cbase = step * G::BPW * W::kRecord;
 
         // Loads: own (bf16) and every payload's codes and scalars.
         u4v xo[G::CH];
@@ -650,9 +669,9 @@ __global__ __launch_bounds__(kGroup) void reduce_compress_kernel(
 #pragma unroll
         for (int p = 0; p < P; ++p) {
 #pragma unroll
-            for (int k = 0; k < G::CH; ++k) qc[p][k] = ld8(pay.codes[p] + base + off + k * G::SPAN);
-            wa[p] = pay.alpha[p][lblk];
-            ws[p] = pay.scale[p][lblk];
+            for (int k = 0; k < G::CH; ++k) qc[p][k] = ld8(pay.codes[p] + cbase + coff + k * G::SPAN);
+            wa[p] = pay.alpha[p][lblk * W::kScalarStride];
+            ws[p] = pay.scale[p][lblk * W::kScalarStride];
         }
 
         float v[G::EPL];
@@ -724,12 +743,12 @@ __global__ __launch_bounds__(kGroup) void reduce_compress_kernel(
 
         const int64_t blk = step * G::BPW + g;
         if (blk < nblocks) {
-            uint8_t *cq = codes + base + lane_elem;
+            uint8_t *cq = codes + blk * W::kRecord + 8 * t;
 #pragma unroll
             for (int k = 0; k < G::CH; ++k) st8(cq + k * G::SPAN, encode8(&v[8 * k], r));
             if (t == 0) {
-                alpha[blk] = a * unshift;
-                scale[blk] = s;
+                alpha[blk * W::kScalarStride] = a * unshift;
+                scale[blk * W::kScalarStride] = s;
             }
         }
     }
@@ -810,55 +829,83 @@ taco_status launch(const void *fn, unsigned grid, hipStream_t stream, Args... ar
     return err == hipSuccess ? TACO_OK : TACO_ERR_HIP;
 }
 
-template <int B>
-taco_status compress_launch(const uint16_t *x, int64_t nblocks, float tau, uint8_t *codes,
-                            float *alpha, float *scale, hipStream_t stream) {
-    const int64_t nsteps = (nblocks + Geo<B>::BPW - 1) / Geo<B>::BPW;
-    return launch(reinterpret_cast<const void *>(&compress_kernel<B>), grid_for(nsteps), stream, x,
-                  nblocks, tau, codes, alpha, scale);
-}
-
-template <int B, Out MODE>
-taco_status decompress_launch(const uint8_t *codes, const float *alpha, const float *scale,
-                              int64_t nblocks, uint16_t *y, float *acc, hipStream_t stream) {
-    const int64_t nsteps = (nblocks + Geo<B>::BPW - 1) / Geo<B>::BPW;
-    return launch(reinterpret_cast<const void *>(&decompress_kernel<B, MODE>), grid_for(nsteps),
-                  stream, codes, alpha, scale, nblocks, y, acc);
-}
-
-template <int B, int P>
-taco_status reduce_launch(const uint16_t *own, const Payloads &pay, int64_t nblocks, float tau,
-                          uint8_t *codes, float *alpha, float *scale, hipStream_t stream) {
-    const int64_t nsteps = (nblocks + Geo<B>::BPW - 1) / Geo<B>::BPW;
-    return launch(reinterpret_cast<const void *>(&reduce_compress_kernel<B, P>), grid_for(nsteps),
-                  stream, own, pay, nblocks, tau, codes, alpha, scale);
-}
-
-template <int B>
-taco_status reduce_dispatch(int npay, const uint16_t *own, const Payloads &pay, int64_t nblocks,
-                            float tau, uint8_t *codes, float *alpha, float *scale,
-                            hipStream_t stream) {
-    switch (npay) {
-        case 0: return reduce_launch<B, 0>(own, pay, nblocks, tau, codes, alpha, scale, stream);
-        case 1: return reduce_launch<B, 1>(own, pay, nblocks, tau, codes, alpha, scale, stream);
-        case 2: return reduce_launch<B, 2>(own, pay, nblocks, tau, codes, alpha, scale, stream);
-        case 3: return reduce_launch<B, 3>(own, pay, nblocks, tau, codes, alpha, scale, stream);
-        case 4: return reduce_launch<B, 4>(own, pay, nblocks, tau, codes, alpha, scale, stream);
-        case 5: return reduce_launch<B, 5>(own, pay, nblocks, tau, codes, alpha, scale, stream);
-        case 6: return reduce_launch<B, 6>(own, pay, nblocks, tau, codes, alpha, scale, stream);
-        case 7: return reduce_launch<B, 7>(own, pay, nblocks, tau, codes, alpha, scale, stream);
-        default: return reduce_launch<B, 8>(own, pay, nblocks, tau, codes, alpha, scale, stream);
+// Calls f.template run<B>() for the runtime block size (validated before).
+template <typename F>
+taco_status for_block(int32_t block, F &&f) {
+    switch (block) {
+        case 32: return f.template run<32>();
+        case 64: return f.template run<64>();
+        case 128: return f.template run<128>();
+        case 256: return f.template run<256>();
+        default: return f.template run<512>();
     }
 }
 
-// Shared validation of the decompress-side calls.
-taco_status check_receiver(const uint8_t *codes, const float *alpha, const float *scale,
-                           int64_t tokens, int64_t hidden, int32_t block, const void *out,
-                           size_t out_elem, int64_t *nblocks_out) {
+template <int B>
+int64_t steps_of(int64_t nblocks) { return (nblocks + Geo<B>::BPW - 1) / Geo<B>::BPW; }
+
+template <Layout L>
+struct CompressLaunch {
+    const uint16_t *x; int64_t m; float tau; uint8_t *codes; float *alpha; float *scale;
+    hipStream_t stream;
+    template <int B> taco_status run() const {
+        return launch(reinterpret_cast<const void *>(&compress_kernel<B, L>), grid_for(steps_of<B>(m)),
+                      stream, x, m, tau, codes, alpha, scale);
+    }
+};
+
+template <Out MODE, Layout L>
+struct DecompressLaunch {
+    const uint8_t *codes; const float *alpha; const float *scale; int64_t m; uint16_t *y;
+    float *acc; hipStream_t stream;
+    template <int B> taco_status run() const {
+        return launch(reinterpret_cast<const void *>(&decompress_kernel<B, MODE, L>),
+                      grid_for(steps_of<B>(m)), stream, codes, alpha, scale, m, y, acc);
+    }
+};
+
+template <Layout L>
+struct ReduceLaunch {
+    int npay; const uint16_t *own; Payloads pay; int64_t m; float tau; uint8_t *codes;
+    float *alpha; float *scale; hipStream_t stream;
+    template <int B, int P> taco_status go() const {
+        return launch(reinterpret_cast<const void *>(&reduce_compress_kernel<B, P, L>),
+                      grid_for(steps_of<B>(m)), stream, own, pay, m, tau, codes, alpha, scale);
+    }
+    template <int B> taco_status run() const {
+        switch (npay) {
+            case 0: return go<B, 0>();
+            case 1: return go<B, 1>();
+            case 2: return go<B, 2>();
+            case 3: return go<B, 3>();
+            case 4: return go<B, 4>();
+            case 5: return go<B, 5>();
+            case 6: return go<B, 6>();
+            case 7: return go<B, 7>();
+            default: return go<B, 8>();
+        }
+    }
+};
+
+// Shape, block and element count checks shared by every entry point.
+taco_status check_shape(int64_t tokens, int64_t hidden, int32_t block, int64_t *n_out) {
     const int64_t n = numel(tokens, hidden);
     if (n < 0) return TACO_ERR_SHAPE;
     if (!valid_block(block)) return TACO_ERR_BLOCK;
     if (n % block) return TACO_ERR_SHAPE;
+    *n_out = n;
+    return TACO_OK;
+}
+
+bool valid_tau(float tau) { return tau > 0.0f && tau <= TACO_MAX_TARGET_ENERGY; }
+
+// Shared validation of the decompress-side calls (side-buffer layout).
+taco_status check_receiver(const uint8_t *codes, const float *alpha, const float *scale,
+                           int64_t tokens, int64_t hidden, int32_t block, const void *out,
+                           size_t out_elem, int64_t *nblocks_out) {
+    int64_t n = 0;
+    const taco_status st = check_shape(tokens, hidden, block, &n);
+    if (st != TACO_OK) return st;
     *nblocks_out = n / block;
     if (n == 0) return TACO_OK;
     if (!codes || !alpha || !scale || !out) return TACO_ERR_NULL;
@@ -871,6 +918,49 @@ taco_status check_receiver(const uint8_t *codes, const float *alpha, const float
     return TACO_OK;
 }
 
+// Shared validation of the decompress-side calls (interleaved layout).
+taco_status check_receiver_packed(const uint8_t *payload, int64_t tokens, int64_t hidden,
+                                  int32_t block, const void *out, size_t out_elem,
+                                  int64_t *nblocks_out) {
+    int64_t n = 0;
+    const taco_status st = check_shape(tokens, hidden, block, &n);
+    if (st != TACO_OK) return st;
+    *nblocks_out = n / block;
+    if (n == 0) return TACO_OK;
+    if (!payload || !out) return TACO_ERR_NULL;
+    if (!aligned(payload, 16) || !aligned(out, 16)) return TACO_ERR_ALIGN;
+    if (overlap(out, (size_t)n * out_elem, payload, (size_t)(n / block) * (size_t)(block + 8)))
+        return TACO_ERR_ALIAS;
+    return TACO_OK;
+}
+
+// Validation of the owner step's payloads; fills pay.  `bytes` is the size
+// of one payload (codes + scalars as laid out), `packed` selects how the
+// scalar pointers are derived.
+taco_status check_payloads(int npay, const uint8_t *const *codes, const float *const *alpha,
+                           const float *const *scale, int64_t n, int32_t block, bool packed,
+                           const void *const *outs, const size_t *out_len, int nouts,
+                           Payloads *pay) {
+    const size_t nc = (size_t)n, nb = (size_t)(n / block) * sizeof(float);
+    for (int p = 0; p < npay; ++p) {
+        const uint8_t *c = codes[p];
+        const float *a = packed ? (c ? reinterpret_cast<const float *>(c + block) : nullptr) : alpha[p];
+        const float *sc = packed ? (c ? reinterpret_cast<const float *>(c + block + 4) : nullptr) : scale[p];
+        if (!c || !a || !sc) return TACO_ERR_NULL;
+        if (!aligned(c, 16) || !aligned(a, 4) || !aligned(sc, 4)) return TACO_ERR_ALIGN;
+        const void *ins[3] = {c, a, sc};
+        const size_t lens[3] = {packed ? (size_t)(n / block) * (size_t)(block + 8) : nc,
+                                packed ? 0 : nb, packed ? 0 : nb};
+        for (int i = 0; i < 3; ++i)
+            for (int o = 0; o < nouts; ++o)
+                if (overlap(outs[o], out_len[o], ins[i], lens[i])) return TACO_ERR_ALIAS;
+        pay->codes[p] = c;
+        pay->alpha[p] = a;
+        pay->scale[p] = sc;
+    }
+    return TACO_OK;
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------- C ABI ---
@@ -878,19 +968,24 @@ taco_status check_receiver(const uint8_t *codes, const float *alpha, const float
 extern "C" {
 
 int64_t taco_num_blocks(int64_t tokens, int64_t hidden, int32_t block) {
-    const int64_t n = numel(tokens, hidden);
-    if (n < 0 || !valid_block(block) || n % block) return -1;
+    int64_t n = 0;
+    if (check_shape(tokens, hidden, block, &n) != TACO_OK) return -1;
     return n / block;
+}
+
+int64_t taco_packed_bytes(int64_t tokens, int64_t hidden, int32_t block) {
+    int64_t n = 0;
+    if (check_shape(tokens, hidden, block, &n) != TACO_OK) return -1;
+    return (n / block) * (block + 8);
 }
 
 taco_status taco_compress(const uint16_t *x_bf16, int64_t tokens, int64_t hidden, int32_t block,
                           float target_energy, uint8_t *codes_e4m3, float *alpha, float *scale,
                           hipStream_t stream) {
-    const int64_t n = numel(tokens, hidden);
-    if (n < 0) return TACO_ERR_SHAPE;
-    if (!valid_block(block)) return TACO_ERR_BLOCK;
-    if (n % block) return TACO_ERR_SHAPE;
-    if (!(target_energy > 0.0f) || !(target_energy <= TACO_MAX_TARGET_ENERGY)) return TACO_ERR_PARAM;
+    int64_t n = 0;
+    const taco_status st = check_shape(tokens, hidden, block, &n);
+    if (st != TACO_OK) return st;
+    if (!valid_tau(target_energy)) return TACO_ERR_PARAM;
     if (n == 0) return TACO_OK;
     if (!x_bf16 || !codes_e4m3 || !alpha || !scale) return TACO_ERR_NULL;
     if (!aligned(x_bf16, 16) || !aligned(codes_e4m3, 16) || !aligned(alpha, 4) || !aligned(scale, 4))
@@ -901,45 +996,66 @@ taco_status taco_compress(const uint16_t *x_bf16, int64_t tokens, int64_t hidden
         overlap(scale, nb, x_bf16, nx) || overlap(codes_e4m3, nc, alpha, nb) ||
         overlap(codes_e4m3, nc, scale, nb) || overlap(alpha, nb, scale, nb))
         return TACO_ERR_ALIAS;
-    switch (block) {
-        case 32: return compress_launch<32>(x_bf16, m, target_energy, codes_e4m3, alpha, scale, stream);
-        case 64: return compress_launch<64>(x_bf16, m, target_energy, codes_e4m3, alpha, scale, stream);
-        case 128: return compress_launch<128>(x_bf16, m, target_energy, codes_e4m3, alpha, scale, stream);
-        case 256: return compress_launch<256>(x_bf16, m, target_energy, codes_e4m3, alpha, scale, stream);
-        default: return compress_launch<512>(x_bf16, m, target_energy, codes_e4m3, alpha, scale, stream);
-    }
+    return for_block(block, CompressLaunch<Layout::kSide>{x_bf16, m, target_energy, codes_e4m3,
+                                                           alpha, scale, stream});
+}
+
+taco_status taco_compress_packed(const uint16_t *x_bf16, int64_t tokens, int64_t hidden,
+                                 int32_t block, float target_energy, uint8_t *payload,
+                                 hipStream_t stream) {
+    int64_t n = 0;
+    const taco_status st = check_shape(tokens, hidden, block, &n);
+    if (st != TACO_OK) return st;
+    if (!valid_tau(target_energy)) return TACO_ERR_PARAM;
+    if (n == 0) return TACO_OK;
+    if (!x_bf16 || !payload) return TACO_ERR_NULL;
+    if (!aligned(x_bf16, 16) || !aligned(payload, 16)) return TACO_ERR_ALIGN;
+    const int64_t m = n / block;
+    if (overlap(payload, (size_t)m * (size_t)(block + 8), x_bf16, (size_t)n * 2)) return TACO_ERR_ALIAS;
+    return for_block(block, CompressLaunch<Layout::kPacked>{
+        x_bf16, m, target_energy, payload, reinterpret_cast<float *>(payload + block),
+        reinterpret_cast<float *>(payload + block + 4), stream});
 }
 
 taco_status taco_decompress(const uint8_t *codes_e4m3, const float *alpha, const float *scale,
                             int64_t tokens, int64_t hidden, int32_t block, uint16_t *y_bf16,
                             hipStream_t stream) {
     int64_t m = 0;
-    taco_status st = check_receiver(codes_e4m3, alpha, scale, tokens, hidden, block, y_bf16, 2, &m);
+    const taco_status st = check_receiver(codes_e4m3, alpha, scale, tokens, hidden, block, y_bf16, 2, &m);
     if (st != TACO_OK || m == 0) return st;
-    constexpr Out O = Out::kBf16;
-    switch (block) {
-        case 32: return decompress_launch<32, O>(codes_e4m3, alpha, scale, m, y_bf16, nullptr, stream);
-        case 64: return decompress_launch<64, O>(codes_e4m3, alpha, scale, m, y_bf16, nullptr, stream);
-        case 128: return decompress_launch<128, O>(codes_e4m3, alpha, scale, m, y_bf16, nullptr, stream);
-        case 256: return decompress_launch<256, O>(codes_e4m3, alpha, scale, m, y_bf16, nullptr, stream);
-        default: return decompress_launch<512, O>(codes_e4m3, alpha, scale, m, y_bf16, nullptr, stream);
-    }
+    return for_block(block, DecompressLaunch<Out::kBf16, Layout::kSide>{
+        codes_e4m3, alpha, scale, m, y_bf16, nullptr, stream});
+}
+
+taco_status taco_decompress_packed(const uint8_t *payload, int64_t tokens, int64_t hidden,
+                                   int32_t block, uint16_t *y_bf16, hipStream_t stream) {
+    int64_t m = 0;
+    const taco_status st = check_receiver_packed(payload, tokens, hidden, block, y_bf16, 2, &m);
+    if (st != TACO_OK || m == 0) return st;
+    return for_block(block, DecompressLaunch<Out::kBf16, Layout::kPacked>{
+        payload, reinterpret_cast<const float *>(payload + block),
+        reinterpret_cast<const float *>(payload + block + 4), m, y_bf16, nullptr, stream});
 }
 
 taco_status taco_decompress_accumulate(const uint8_t *codes_e4m3, const float *alpha,
                                        const float *scale, int64_t tokens, int64_t hidden,
                                        int32_t block, float *acc_f32, hipStream_t stream) {
     int64_t m = 0;
-    taco_status st = check_receiver(codes_e4m3, alpha, scale, tokens, hidden, block, acc_f32, 4, &m);
+    const taco_status st = check_receiver(codes_e4m3, alpha, scale, tokens, hidden, block, acc_f32, 4, &m);
     if (st != TACO_OK || m == 0) return st;
-    constexpr Out O = Out::kAccumulate;
-    switch (block) {
-        case 32: return decompress_launch<32, O>(codes_e4m3, alpha, scale, m, nullptr, acc_f32, stream);
-        case 64: return decompress_launch<64, O>(codes_e4m3, alpha, scale, m, nullptr, acc_f32, stream);
-        case 128: return decompress_launch<128, O>(codes_e4m3, alpha, scale, m, nullptr, acc_f32, stream);
-        case 256: return decompress_launch<256, O>(codes_e4m3, alpha, scale, m, nullptr, acc_f32, stream);
-        default: return decompress_launch<512, O>(codes_e4m3, alpha, scale, m, nullptr, acc_f32, stream);
-    }
+    return for_block(block, DecompressLaunch<Out::kAccumulate, Layout::kSide>{
+        codes_e4m3, alpha, scale, m, nullptr, acc_f32, stream});
+}
+
+taco_status taco_decompress_accumulate_packed(const uint8_t *payload, int64_t tokens,
+                                              int64_t hidden, int32_t block, float *acc_f32,
+                                              hipStream_t stream) {
+    int64_t m = 0;
+    const taco_status st = check_receiver_packed(payload, tokens, hidden, block, acc_f32, 4, &m);
+    if (st != TACO_OK || m == 0) return st;
+    return for_block(block, DecompressLaunch<Out::kAccumulate, Layout::kPacked>{
+        payload, reinterpret_cast<const float *>(payload + block),
+        reinterpret_cast<const float *>(payload + block + 4), m, nullptr, acc_f32, stream});
 }
 
 taco_status taco_reduce_compress(const uint16_t *own_bf16, int32_t npayloads,
@@ -947,11 +1063,10 @@ taco_status taco_reduce_compress(const uint16_t *own_bf16, int32_t npayloads,
                                  const float *const *scale, int64_t tokens, int64_t hidden,
                                  int32_t block, float target_energy, uint8_t *out_codes,
                                  float *out_alpha, float *out_scale, hipStream_t stream) {
-    const int64_t n = numel(tokens, hidden);
-    if (n < 0) return TACO_ERR_SHAPE;
-    if (!valid_block(block)) return TACO_ERR_BLOCK;
-    if (n % block) return TACO_ERR_SHAPE;
-    if (!(target_energy > 0.0f) || !(target_energy <= TACO_MAX_TARGET_ENERGY)) return TACO_ERR_PARAM;
+    int64_t n = 0;
+    taco_status st = check_shape(tokens, hidden, block, &n);
+    if (st != TACO_OK) return st;
+    if (!valid_tau(target_energy)) return TACO_ERR_PARAM;
     if (npayloads < 0 || npayloads > TACO_MAX_PAYLOADS) return TACO_ERR_PARAM;
     if (npayloads == 0 && !own_bf16) return TACO_ERR_PARAM;
     if (n == 0) return TACO_OK;
@@ -963,36 +1078,48 @@ taco_status taco_reduce_compress(const uint16_t *own_bf16, int32_t npayloads,
     if (overlap(out_codes, nc, out_alpha, nb) || overlap(out_codes, nc, out_scale, nb) ||
         overlap(out_alpha, nb, out_scale, nb))
         return TACO_ERR_ALIAS;
+    const void *outs[3] = {out_codes, out_alpha, out_scale};
+    const size_t out_len[3] = {nc, nb, nb};
     if (own_bf16) {
         if (!aligned(own_bf16, 16)) return TACO_ERR_ALIGN;
-        const size_t no = (size_t)n * 2;
-        if (overlap(out_codes, nc, own_bf16, no) || overlap(out_alpha, nb, own_bf16, no) ||
-            overlap(out_scale, nb, own_bf16, no))
-            return TACO_ERR_ALIAS;
+        for (int o = 0; o < 3; ++o)
+            if (overlap(outs[o], out_len[o], own_bf16, (size_t)n * 2)) return TACO_ERR_ALIAS;
     }
     Payloads pay = {};
-    for (int p = 0; p < npayloads; ++p) {
-        const uint8_t *c = codes_e4m3[p];
-        const float *a = alpha[p], *sc = scale[p];
-        if (!c || !a || !sc) return TACO_ERR_NULL;
-        if (!aligned(c, 16) || !aligned(a, 4) || !aligned(sc, 4)) return TACO_ERR_ALIGN;
-        const void *ins[3] = {c, a, sc};
-        const size_t lens[3] = {nc, nb, nb};
-        for (int i = 0; i < 3; ++i)
-            if (overlap(out_codes, nc, ins[i], lens[i]) || overlap(out_alpha, nb, ins[i], lens[i]) ||
-                overlap(out_scale, nb, ins[i], lens[i]))
-                return TACO_ERR_ALIAS;
-        pay.codes[p] = c;
-        pay.alpha[p] = a;
-        pay.scale[p] = sc;
+    st = check_payloads(npayloads, codes_e4m3, alpha, scale, n, block, false, outs, out_len, 3, &pay);
+    if (st != TACO_OK) return st;
+    return for_block(block, ReduceLaunch<Layout::kSide>{npayloads, own_bf16, pay, m, target_energy,
+                                                         out_codes, out_alpha, out_scale, stream});
+}
+
+taco_status taco_reduce_compress_packed(const uint16_t *own_bf16, int32_t npayloads,
+                                        const uint8_t *const *payloads, int64_t tokens,
+                                        int64_t hidden, int32_t block, float target_energy,
+                                        uint8_t *out_payload, hipStream_t stream) {
+    int64_t n = 0;
+    taco_status st = check_shape(tokens, hidden, block, &n);
+    if (st != TACO_OK) return st;
+    if (!valid_tau(target_energy)) return TACO_ERR_PARAM;
+    if (npayloads < 0 || npayloads > TACO_MAX_PAYLOADS) return TACO_ERR_PARAM;
+    if (npayloads == 0 && !own_bf16) return TACO_ERR_PARAM;
+    if (n == 0) return TACO_OK;
+    if (!out_payload) return TACO_ERR_NULL;
+    if (npayloads > 0 && !payloads) return TACO_ERR_NULL;
+    const int64_t m = n / block;
+    if (!aligned(out_payload, 16)) return TACO_ERR_ALIGN;
+    const void *outs[1] = {out_payload};
+    const size_t out_len[1] = {(size_t)m * (size_t)(block + 8)};
+    if (own_bf16) {
+        if (!aligned(own_bf16, 16)) return TACO_ERR_ALIGN;
+        if (overlap(out_payload, out_len[0], own_bf16, (size_t)n * 2)) return TACO_ERR_ALIAS;
     }
-    switch (block) {
-        case 32: return reduce_dispatch<32>(npayloads, own_bf16, pay, m, target_energy, out_codes, out_alpha, out_scale, stream);
-        case 64: return reduce_dispatch<64>(npayloads, own_bf16, pay, m, target_energy, out_codes, out_alpha, out_scale, stream);
-        case 128: return reduce_dispatch<128>(npayloads, own_bf16, pay, m, target_energy, out_codes, out_alpha, out_scale, stream);
-        case 256: return reduce_dispatch<256>(npayloads, own_bf16, pay, m, target_energy, out_codes, out_alpha, out_scale, stream);
-        default: return reduce_dispatch<512>(npayloads, own_bf16, pay, m, target_energy, out_codes, out_alpha, out_scale, stream);
-    }
+    Payloads pay = {};
+    st = check_payloads(npayloads, payloads, nullptr, nullptr, n, block, true, outs, out_len, 1, &pay);
+    if (st != TACO_OK) return st;
+    return for_block(block, ReduceLaunch<Layout::kPacked>{
+        npayloads, own_bf16, pay, m, target_energy, out_payload,
+        reinterpret_cast<float *>(out_payload + block), reinterpret_cast<float *>(out_payload + block + 4),
+        stream});
 }
 
 taco_status taco_e4m3_encode(const float *x, int64_t n, uint8_t *codes, hipStream_t stream) {

@@ -151,6 +151,43 @@ taco_status taco_reduce_compress(const uint16_t *own_bf16, int32_t npayloads,
                                  float *out_alpha, float *out_scale, hipStream_t stream);
 
 /*
+ * Interleaved wire layout ([TACO] section 4.4.2: alpha_k and s_k are stored
+ * contiguously with block k's FP8 payload, so a single message carries the
+ * whole compressed tensor and a receiver finds the scalars by pointer
+ * arithmetic).  A payload is M records of block + 8 bytes: record k holds
+ * block k's block codes (same element order as x), then alpha_k and s_k as
+ * float32 (little-endian).  Payload buffers are 16-byte aligned.  The calls
+ * below compute exactly what their side-buffer counterparts compute; only the
+ * placement of codes, alpha and s differs.
+ *
+ * taco_packed_bytes: payload size M * (block + 8), or -1 for an invalid shape
+ * or block (same rules as taco_num_blocks).
+ */
+int64_t taco_packed_bytes(int64_t tokens, int64_t hidden, int32_t block);
+
+/* taco_compress writing one interleaved payload (must not overlap x). */
+taco_status taco_compress_packed(const uint16_t *x_bf16, int64_t tokens, int64_t hidden,
+                                 int32_t block, float target_energy, uint8_t *payload,
+                                 hipStream_t stream);
+
+/* taco_decompress reading one interleaved payload. */
+taco_status taco_decompress_packed(const uint8_t *payload, int64_t tokens, int64_t hidden,
+                                   int32_t block, uint16_t *y_bf16, hipStream_t stream);
+
+/* taco_decompress_accumulate reading one interleaved payload. */
+taco_status taco_decompress_accumulate_packed(const uint8_t *payload, int64_t tokens,
+                                              int64_t hidden, int32_t block, float *acc_f32,
+                                              hipStream_t stream);
+
+/* taco_reduce_compress with interleaved payloads: payloads is a HOST array of
+ * npayloads DEVICE pointers to payloads; the result is one interleaved
+ * payload (must not overlap own or any input payload). */
+taco_status taco_reduce_compress_packed(const uint16_t *own_bf16, int32_t npayloads,
+                                        const uint8_t *const *payloads, int64_t tokens,
+                                        int64_t hidden, int32_t block, float target_energy,
+                                        uint8_t *out_payload, hipStream_t stream);
+
+/*
  * The E4M3 conversions the kernels above use (Cvt_FP8 of [TACO] Eq. 10 and
  * Cvt_FP32 of Eq. 11), exposed element-wise so that they can be checked
  * exhaustively.  encode: round to nearest even, OCP E4M3FN; inputs of

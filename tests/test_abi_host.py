@@ -9,6 +9,17 @@ import pytest
 
 from conftest import ROOT
 
+# These tests pass fake device addresses and only ever expect validation
+# errors; on a machine with a GPU a validation slip would launch a kernel on
+# them, so the module runs only where no GPU is visible (counting devices
+# does not initialise the GPU).
+try:
+    import torch as _torch
+    if _torch.cuda.device_count() > 0:
+        pytest.skip("host-only validation tests (fake device pointers)", allow_module_level=True)
+except ImportError:  # pragma: no cover
+    pass
+
 HEADER = os.path.join(ROOT, "include", "taco.h")
 LIB = os.path.join(ROOT, "gradients_taco_compress_amd", "libtaco.so")
 
@@ -34,6 +45,12 @@ def lib():
     L.taco_decompress.argtypes = [P, P, P, I64, I64, I32, P, P]
     L.taco_decompress_accumulate.argtypes = [P, P, P, I64, I64, I32, P, P]
     L.taco_reduce_compress.argtypes = [P, I32, P, P, P, I64, I64, I32, F32, P, P, P, P]
+    L.taco_packed_bytes.argtypes = [I64, I64, I32]
+    L.taco_packed_bytes.restype = I64
+    L.taco_compress_packed.argtypes = [P, I64, I64, I32, F32, P, P]
+    L.taco_decompress_packed.argtypes = [P, I64, I64, I32, P, P]
+    L.taco_decompress_accumulate_packed.argtypes = [P, I64, I64, I32, P, P]
+    L.taco_reduce_compress_packed.argtypes = [P, I32, P, I64, I64, I32, F32, P, P]
     L.taco_e4m3_encode.argtypes = [P, I64, P, P]
     L.taco_e4m3_decode.argtypes = [P, I64, P, P]
     L.taco_status_string.argtypes = [ctypes.c_int]
@@ -43,7 +60,7 @@ def lib():
 
 def test_every_declared_function_is_exported(lib):
     names = declared_functions()
-    assert len(names) == 8, names
+    assert len(names) == 13, names
     for n in names:
         assert hasattr(lib, n), n
     out = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True).stdout
@@ -175,3 +192,43 @@ def test_reduce_compress_validation(lib):
     # Empty tensors: a no-op once the arguments that do not depend on N are valid.
     assert reduce_call(lib, tokens=0, out_codes=None, out_alpha=None, out_scale=None) == OK
     assert reduce_call(lib, own=None, npay=1, tokens=0) == OK   # own is optional
+
+
+def test_packed_validation(lib):
+    assert lib.taco_packed_bytes(4, 256, 128) == 8 * 136
+    assert lib.taco_packed_bytes(3, 96, 128) == -1
+    assert lib.taco_packed_bytes(4, 256, 100) == -1
+    cp = lambda **k: lib.taco_compress_packed(k.get("x", A), k.get("tokens", 4), 256,
+                                              k.get("block", 128), k.get("tau", 1.0),
+                                              k.get("out", 2 * A), None)
+    assert cp(tokens=-1) == SHAPE
+    assert cp(block=48) == BLOCK
+    assert cp(tau=-1.0) == PARAM
+    assert cp(x=None) == NULL
+    assert cp(out=None) == NULL
+    assert cp(out=2 * A + 8) == ALIGN
+    assert cp(out=A + 1024) == ALIAS
+    assert cp(tokens=0, x=None, out=None) == OK
+    for fn, elem in ((lib.taco_decompress_packed, 2), (lib.taco_decompress_accumulate_packed, 4)):
+        dp = lambda **k: fn(k.get("pay", A), k.get("tokens", 4), 256, k.get("block", 128),
+                            k.get("out", 2 * A), None)
+        assert dp(tokens=-3) == SHAPE
+        assert dp(block=96) == BLOCK
+        assert dp(pay=None) == NULL
+        assert dp(out=None) == NULL
+        assert dp(pay=A + 4) == ALIGN
+        assert dp(out=A + 8 * 136 - 16) == ALIAS
+        assert dp(tokens=0, pay=None, out=None) == OK
+    arr = ctypes.c_void_p * 8
+    rp = lambda own=A, npay=2, pays=(5 * A, 6 * A), out=2 * A, tokens=4: lib.taco_reduce_compress_packed(
+        own, npay, None if pays is None else ctypes.cast(arr(*pays), ctypes.c_void_p), tokens, 256,
+        128, 1.0, out, None)
+    assert rp(npay=9) == PARAM
+    assert rp(own=None, npay=0) == PARAM
+    assert rp(out=None) == NULL
+    assert rp(pays=None) == NULL
+    assert rp(pays=(5 * A, None)) == NULL
+    assert rp(pays=(5 * A, 6 * A + 8)) == ALIGN
+    assert rp(out=5 * A + 512) == ALIAS
+    assert rp(out=A + 64) == ALIAS
+    assert rp(tokens=0, out=None) == OK
