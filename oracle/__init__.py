@@ -61,12 +61,27 @@ def _load():
         lib.taco_oracle_fwht.restype = None
         lib.taco_oracle_ash_block.argtypes = [P, i32, f64, f64, P, P, P]
         lib.taco_oracle_compress.argtypes = [P, i64, i32, f64, f64, P, P, P]
-        lib.taco_oracle_reconstruct_f64.argtypes = [P, P, P, i64, i32, P]
-        lib.taco_oracle_decompress.argtypes = [P, P, P, i64, i32, P]
-        lib.taco_oracle_decompress_accumulate.argtypes = [P, P, P, i64, i32, P]
+        lib.taco_oracle_compress_fmt.argtypes = [P, i64, i32, f64, f64, i32, P, P, P]
+        lib.taco_oracle_reconstruct_f64.argtypes = [P, P, P, i64, i32, i32, P]
+        lib.taco_oracle_decompress.argtypes = [P, P, P, i64, i32, i32, P]
+        lib.taco_oracle_decompress_accumulate.argtypes = [P, P, P, i64, i32, i32, P]
         lib.taco_oracle_roundtrip_noquant.argtypes = [P, i32, f64, f64, P]
-        lib.taco_oracle_compress_f64.argtypes = [P, i64, i32, f64, f64, P, P, P]
-        lib.taco_oracle_reduce_compress.argtypes = [P, i32, P, P, P, i64, i32, f64, f64, P, P, P]
+        lib.taco_oracle_compress_f64.argtypes = [P, i64, i32, f64, f64, i32, P, P, P]
+        lib.taco_oracle_reduce_compress.argtypes = [P, i32, P, P, P, i64, i32, f64, f64, i32,
+                                                    P, P, P]
+        lib.taco_oracle_qmax.argtypes = [i32]
+        lib.taco_oracle_qmax.restype = f64
+        lib.taco_oracle_encode_array.argtypes = [i32, P, i64, P]
+        lib.taco_oracle_encode_array.restype = None
+        lib.taco_oracle_decode_array.argtypes = [i32, P, i64, P]
+        lib.taco_oracle_decode_array.restype = None
+        for name, arg, res in (("e5m2_decode", ctypes.c_uint8, f64),
+                               ("e5m2_encode", ctypes.c_float, ctypes.c_uint8),
+                               ("int8_decode", ctypes.c_uint8, f64),
+                               ("int8_encode", ctypes.c_float, ctypes.c_uint8)):
+            fn = getattr(lib, "taco_oracle_" + name)
+            fn.argtypes = [arg]
+            fn.restype = res
         _lib = lib
     return _lib
 
@@ -83,6 +98,41 @@ def _check(rc: int):
 
 
 # ---------------------------------------------------------------- codecs ----
+
+#: Code formats: E4M3 (the operator's), E5M2 (section 5.3.2 format ablation)
+#: and INT8 (section 6 fallback; section 2.3 / Eq. 1 quantiser).
+FORMATS = {"e4m3": 0, "e5m2": 1, "int8": 2}
+
+
+def _fmt(fmt: str) -> int:
+    try:
+        return FORMATS[fmt]
+    except KeyError:
+        raise ValueError(f"unknown code format {fmt!r} (one of {sorted(FORMATS)})") from None
+
+
+def qmax(fmt: str = "e4m3") -> float:
+    """Q_max of Eq. 9 for a code format."""
+    return float(_load().taco_oracle_qmax(_fmt(fmt)))
+
+
+def decode(codes, fmt: str = "e4m3") -> np.ndarray:
+    """Values (float64) of codes of a format."""
+    lib = _load()
+    c = np.ascontiguousarray(codes, dtype=np.uint8)
+    out = np.empty(c.shape, np.float64)
+    lib.taco_oracle_decode_array(_fmt(fmt), _ptr(c), c.size, _ptr(out))
+    return out
+
+
+def encode(values, fmt: str = "e4m3") -> np.ndarray:
+    """Nearest-even, saturating codes of float32 values in a format."""
+    lib = _load()
+    v = np.ascontiguousarray(values, dtype=np.float32)
+    out = np.empty(v.shape, np.uint8)
+    lib.taco_oracle_encode_array(_fmt(fmt), _ptr(v), v.size, _ptr(out))
+    return out
+
 
 def e4m3_decode(codes) -> np.ndarray:
     """Values (float64) of E4M3 codes."""
@@ -111,14 +161,16 @@ def double_to_bf16(values) -> np.ndarray:
     return out
 
 
-def encode_function_address() -> int:
-    """Address of the scalar C encoder (for the exhaustive test helper)."""
-    return ctypes.cast(_load().taco_oracle_e4m3_encode, ctypes.c_void_p).value
+def encode_function_address(fmt: str = "e4m3") -> int:
+    """Address of a scalar C encoder (for the exhaustive test helper)."""
+    _fmt(fmt)
+    return ctypes.cast(getattr(_load(), f"taco_oracle_{fmt}_encode"), ctypes.c_void_p).value
 
 
-def decode_function_address() -> int:
-    """Address of the scalar C decoder (for the exhaustive test helper)."""
-    return ctypes.cast(_load().taco_oracle_e4m3_decode, ctypes.c_void_p).value
+def decode_function_address(fmt: str = "e4m3") -> int:
+    """Address of a scalar C decoder (for the exhaustive test helper)."""
+    _fmt(fmt)
+    return ctypes.cast(getattr(_load(), f"taco_oracle_{fmt}_decode"), ctypes.c_void_p).value
 
 
 def fwht(v) -> np.ndarray:
@@ -146,7 +198,7 @@ def ash_block(x_bits, block: int, tau: float = 1.0, eps: float = EPS):
     return float(alpha[0]), gt, z
 
 
-def compress(x_bits, block: int, tau: float = 1.0, eps: float = EPS):
+def compress(x_bits, block: int, tau: float = 1.0, eps: float = EPS, fmt: str = "e4m3"):
     """Codes (uint8, same shape as x), alpha and s (float32, one per block)."""
     lib = _load()
     x = np.ascontiguousarray(x_bits, dtype=np.uint16)
@@ -156,11 +208,12 @@ def compress(x_bits, block: int, tau: float = 1.0, eps: float = EPS):
     codes = np.empty(x.shape, np.uint8)
     alpha = np.empty(n // block, np.float32)
     scale = np.empty(n // block, np.float32)
-    _check(lib.taco_oracle_compress(_ptr(x), n, block, tau, eps, _ptr(codes), _ptr(alpha), _ptr(scale)))
+    _check(lib.taco_oracle_compress_fmt(_ptr(x), n, block, tau, eps, _fmt(fmt), _ptr(codes),
+                                        _ptr(alpha), _ptr(scale)))
     return codes, alpha, scale
 
 
-def compress_f64(x, block: int, tau: float = 1.0, eps: float = EPS):
+def compress_f64(x, block: int, tau: float = 1.0, eps: float = EPS, fmt: str = "e4m3"):
     """Like compress() for a tensor of float64 values."""
     lib = _load()
     xv = np.ascontiguousarray(x, dtype=np.float64)
@@ -170,11 +223,13 @@ def compress_f64(x, block: int, tau: float = 1.0, eps: float = EPS):
     codes = np.empty(xv.shape, np.uint8)
     alpha = np.empty(n // block, np.float32)
     scale = np.empty(n // block, np.float32)
-    _check(lib.taco_oracle_compress_f64(_ptr(xv), n, block, tau, eps, _ptr(codes), _ptr(alpha), _ptr(scale)))
+    _check(lib.taco_oracle_compress_f64(_ptr(xv), n, block, tau, eps, _fmt(fmt), _ptr(codes),
+                                        _ptr(alpha), _ptr(scale)))
     return codes, alpha, scale
 
 
-def reduce_compress(own_bits, payloads, block: int, tau: float = 1.0, eps: float = EPS):
+def reduce_compress(own_bits, payloads, block: int, tau: float = 1.0, eps: float = EPS,
+                    fmt: str = "e4m3"):
     """Owner step: compress own + sum of the payloads' reconstructions.
     own_bits: bf16 bit patterns or None; payloads: list of (codes, alpha, scale)."""
     lib = _load()
@@ -198,40 +253,43 @@ def reduce_compress(own_bits, payloads, block: int, tau: float = 1.0, eps: float
     _check(lib.taco_oracle_reduce_compress(None if own is None else _ptr(own), len(pay),
                                            ctypes.cast(cp, ctypes.c_void_p), ctypes.cast(ap, ctypes.c_void_p),
                                            ctypes.cast(sp, ctypes.c_void_p), n, block, tau, eps,
-                                           _ptr(codes), _ptr(alpha), _ptr(scale)))
+                                           _fmt(fmt), _ptr(codes), _ptr(alpha), _ptr(scale)))
     return codes, alpha, scale
 
 
-def reconstruct_f64(codes, alpha, scale, block: int) -> np.ndarray:
+def reconstruct_f64(codes, alpha, scale, block: int, fmt: str = "e4m3") -> np.ndarray:
     """G' in float64 (before any output rounding), same shape as codes."""
     lib = _load()
     c = np.ascontiguousarray(codes, dtype=np.uint8)
     a = np.ascontiguousarray(alpha, dtype=np.float32)
     s = np.ascontiguousarray(scale, dtype=np.float32)
     out = np.empty(c.shape, np.float64)
-    _check(lib.taco_oracle_reconstruct_f64(_ptr(c), _ptr(a), _ptr(s), c.size, block, _ptr(out)))
+    _check(lib.taco_oracle_reconstruct_f64(_ptr(c), _ptr(a), _ptr(s), c.size, block, _fmt(fmt),
+                                           _ptr(out)))
     return out
 
 
-def decompress(codes, alpha, scale, block: int) -> np.ndarray:
+def decompress(codes, alpha, scale, block: int, fmt: str = "e4m3") -> np.ndarray:
     """bf16 bit patterns (uint16) of the reconstruction."""
     lib = _load()
     c = np.ascontiguousarray(codes, dtype=np.uint8)
     a = np.ascontiguousarray(alpha, dtype=np.float32)
     s = np.ascontiguousarray(scale, dtype=np.float32)
     y = np.empty(c.shape, np.uint16)
-    _check(lib.taco_oracle_decompress(_ptr(c), _ptr(a), _ptr(s), c.size, block, _ptr(y)))
+    _check(lib.taco_oracle_decompress(_ptr(c), _ptr(a), _ptr(s), c.size, block, _fmt(fmt), _ptr(y)))
     return y
 
 
-def decompress_accumulate(codes, alpha, scale, block: int, acc: np.ndarray) -> np.ndarray:
+def decompress_accumulate(codes, alpha, scale, block: int, acc: np.ndarray,
+                          fmt: str = "e4m3") -> np.ndarray:
     """acc (float32, updated in place and returned) += G'."""
     lib = _load()
     c = np.ascontiguousarray(codes, dtype=np.uint8)
     a = np.ascontiguousarray(alpha, dtype=np.float32)
     s = np.ascontiguousarray(scale, dtype=np.float32)
     assert acc.dtype == np.float32 and acc.flags["C_CONTIGUOUS"] and acc.size == c.size
-    _check(lib.taco_oracle_decompress_accumulate(_ptr(c), _ptr(a), _ptr(s), c.size, block, _ptr(acc)))
+    _check(lib.taco_oracle_decompress_accumulate(_ptr(c), _ptr(a), _ptr(s), c.size, block,
+                                                 _fmt(fmt), _ptr(acc)))
     return acc
 
 

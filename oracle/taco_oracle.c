@@ -32,6 +32,15 @@
  *  - The decompressed tensor is rounded once to bfloat16 (nearest, ties to
  *    even); the accumulate variant rounds G' once to float32 and adds it to
  *    the float32 accumulator with one float32 addition.
+ *  - Code formats other than E4M3 (section 5.3.2 format ablation; section 6,
+ *    the INT8 fallback for hardware without FP8): the pipeline is unchanged
+ *    and only Cvt_FP8 / Cvt_FP32 and Q_max change.
+ *      E5M2: OCP E5M2 (bias 15, S.11111.00 = infinity, S.11111.mm with
+ *            mm != 0 = NaN), Q_max = 57344, nearest-even, saturating.
+ *      INT8: the uniform quantiser of section 2.3 / Eq. 1 with the dual
+ *            scale as its step (Delta = s = max|Z| / 127, Q_max = 127):
+ *            q = round(Z / s), nearest with ties to even, clamped to
+ *            [-127, 127], stored as a two's complement byte.
  *
  * Build:  gcc -O2 -std=c11 -ffp-contract=off -fno-fast-math -fPIC -shared
  *         taco_oracle.c -o libtaco_oracle.so -lm
@@ -41,7 +50,14 @@
 #include <string.h>
 
 #define ORACLE_QMAX 448.0          /* largest finite OCP E4M3 value */
+#define ORACLE_E5M2_MAX 57344.0    /* largest finite OCP E5M2 value */
+#define ORACLE_INT8_MAX 127.0      /* symmetric INT8 range */
 #define ORACLE_MAX_BLOCK 4096
+
+/* Code formats (argument `fmt` below). */
+#define ORACLE_FMT_E4M3 0
+#define ORACLE_FMT_E5M2 1
+#define ORACLE_FMT_INT8 2
 
 /* ------------------------------------------------------------------------ */
 /* bfloat16 <-> double                                                        */
@@ -132,6 +148,111 @@ uint8_t taco_oracle_e4m3_encode(float v)
     return sign | (uint8_t)code;
 }
 
+/* ------------------------------------------------------------------------ */
+/* E5M2 codec (section 2.3 / Figure 3: 5 exponent bits, 2 mantissa bits)      */
+/* ------------------------------------------------------------------------ */
+
+/* Value of an E5M2 code: bias 15, exponent field 0 is subnormal (m * 2^-16),
+ * exponent field 31 is infinity (m = 0) or NaN. */
+double taco_oracle_e5m2_decode(uint8_t c)
+{
+    int s = c >> 7, e = (c >> 2) & 0x1F, m = c & 0x3;
+    double mag;
+    if (e == 0x1F)
+        mag = (m == 0) ? INFINITY : NAN;
+    else
+        mag = (e == 0) ? ldexp((double)m, -16) : ldexp(1.0 + m / 4.0, e - 15);
+    return s ? -mag : mag;
+}
+
+/* Nearest E5M2 code to v, ties to even mantissa, saturating to +-57344. */
+uint8_t taco_oracle_e5m2_encode(float v)
+{
+    if (isnan(v)) return 0x7F;
+    uint8_t sign = signbit(v) ? 0x80 : 0x00;
+    double a = fabs((double)v);
+    if (a >= ORACLE_E5M2_MAX) return sign | 0x7B;
+    int code;
+    if (a < ldexp(1.0, -14)) {
+        /* Subnormal range m * 2^-16; m = 4 is the smallest normal, code 0x04. */
+        code = (int)round_half_even(a / ldexp(1.0, -16));
+    } else {
+        int e;
+        frexp(a, &e);
+        int E = e - 1;                          /* a in [2^E, 2^(E+1)) */
+        double q = a / ldexp(1.0, E - 2);       /* in [4, 8), exact */
+        int mq = (int)round_half_even(q);       /* 4..8; 8 carries */
+        code = ((E + 15) << 2) + (mq - 4);
+    }
+    if (code > 0x7B) code = 0x7B;               /* 0x7C would be infinity */
+    return sign | (uint8_t)code;
+}
+
+/* ------------------------------------------------------------------------ */
+/* INT8 codec (section 2.3 and Eq. 1: round(x / Delta))                      */
+/* ------------------------------------------------------------------------ */
+
+/* Value of an INT8 code: the byte as a two's complement integer. */
+double taco_oracle_int8_decode(uint8_t c)
+{
+    return (double)(int8_t)c;
+}
+
+/* Nearest integer to v, ties to even, clamped to [-127, 127]. */
+uint8_t taco_oracle_int8_encode(float v)
+{
+    if (isnan(v)) return 0x00;
+    double a = fabs((double)v);
+    double r = (a >= ORACLE_INT8_MAX) ? ORACLE_INT8_MAX : round_half_even(a);
+    int q = (int)r;
+    if (signbit(v)) q = -q;
+    return (uint8_t)(int8_t)q;
+}
+
+/* Format dispatch: Q_max, Cvt (float -> code) and its inverse. */
+double taco_oracle_qmax(int fmt)
+{
+    switch (fmt) {
+    case ORACLE_FMT_E4M3: return ORACLE_QMAX;
+    case ORACLE_FMT_E5M2: return ORACLE_E5M2_MAX;
+    case ORACLE_FMT_INT8: return ORACLE_INT8_MAX;
+    default: return -1.0;
+    }
+}
+
+static uint8_t encode_fmt(float v, int fmt)
+{
+    switch (fmt) {
+    case ORACLE_FMT_E5M2: return taco_oracle_e5m2_encode(v);
+    case ORACLE_FMT_INT8: return taco_oracle_int8_encode(v);
+    default: return taco_oracle_e4m3_encode(v);
+    }
+}
+
+static double decode_fmt(uint8_t c, int fmt)
+{
+    switch (fmt) {
+    case ORACLE_FMT_E5M2: return taco_oracle_e5m2_decode(c);
+    case ORACLE_FMT_INT8: return taco_oracle_int8_decode(c);
+    default: return taco_oracle_e4m3_decode(c);
+    }
+}
+
+static int valid_fmt(int fmt)
+{
+    return fmt == ORACLE_FMT_E4M3 || fmt == ORACLE_FMT_E5M2 || fmt == ORACLE_FMT_INT8;
+}
+
+void taco_oracle_encode_array(int fmt, const float *v, int64_t n, uint8_t *out)
+{
+    for (int64_t i = 0; i < n; ++i) out[i] = encode_fmt(v[i], fmt);
+}
+
+void taco_oracle_decode_array(int fmt, const uint8_t *c, int64_t n, double *out)
+{
+    for (int64_t i = 0; i < n; ++i) out[i] = decode_fmt(c[i], fmt);
+}
+
 /* Element-wise array forms of the three conversions above. */
 void taco_oracle_e4m3_encode_array(const float *v, int64_t n, uint8_t *out)
 {
@@ -209,16 +330,16 @@ int taco_oracle_ash_block(const uint16_t *x, int B, double tau, double eps,
 }
 
 /* Eq. 9-10 for one block with its Z and alpha (Algorithm 1, sender side). */
-static void quantise_block(const double *Z, double a, int B, uint8_t *q,
+static void quantise_block(const double *Z, double a, int B, int fmt, uint8_t *q,
                            float *alpha_out, float *scale_out)
 {
     double zmax = 0.0;
     for (int j = 0; j < B; ++j) zmax = fmax(zmax, fabs(Z[j]));
-    double s = zmax / ORACLE_QMAX;                 /* Eq. 9 */
+    double s = zmax / taco_oracle_qmax(fmt);       /* Eq. 9 */
     for (int j = 0; j < B; ++j) {                  /* Eq. 10 */
         float v = (s > 0.0) ? (float)(Z[j] / s) : 0.0f;
         if (v == 0.0f) v = 0.0f;                   /* zero carries no sign */
-        q[j] = taco_oracle_e4m3_encode(v);
+        q[j] = encode_fmt(v, fmt);
     }
     *alpha_out = (float)a;
     *scale_out = (float)s;
@@ -226,31 +347,40 @@ static void quantise_block(const double *Z, double a, int B, uint8_t *q,
 
 /*
  * Compress a flattened tensor of n bf16 values (n a multiple of B) into
- * n E4M3 codes and n/B pairs (alpha_k, s_k), block by block.
+ * n codes of format fmt and n/B pairs (alpha_k, s_k), block by block.
  */
-int taco_oracle_compress(const uint16_t *x, int64_t n, int B, double tau,
-                         double eps, uint8_t *codes, float *alpha, float *scale)
+int taco_oracle_compress_fmt(const uint16_t *x, int64_t n, int B, double tau,
+                             double eps, int fmt, uint8_t *codes, float *alpha,
+                             float *scale)
 {
-    if (!valid_block(B) || n < 0 || n % B) return -1;
+    if (!valid_block(B) || !valid_fmt(fmt) || n < 0 || n % B) return -1;
     double Z[ORACLE_MAX_BLOCK];
     for (int64_t k = 0; k < n / B; ++k) {
         double a;
         taco_oracle_ash_block(x + k * B, B, tau, eps, &a, NULL, Z);
-        quantise_block(Z, a, B, codes + k * B, alpha + k, scale + k);
+        quantise_block(Z, a, B, fmt, codes + k * B, alpha + k, scale + k);
     }
     return 0;
 }
 
+int taco_oracle_compress(const uint16_t *x, int64_t n, int B, double tau,
+                         double eps, uint8_t *codes, float *alpha, float *scale)
+{
+    return taco_oracle_compress_fmt(x, n, B, tau, eps, ORACLE_FMT_E4M3, codes,
+                                    alpha, scale);
+}
+
 /* The same for a tensor given as doubles. */
 int taco_oracle_compress_f64(const double *x, int64_t n, int B, double tau,
-                             double eps, uint8_t *codes, float *alpha, float *scale)
+                             double eps, int fmt, uint8_t *codes, float *alpha,
+                             float *scale)
 {
-    if (!valid_block(B) || n < 0 || n % B) return -1;
+    if (!valid_block(B) || !valid_fmt(fmt) || n < 0 || n % B) return -1;
     double Z[ORACLE_MAX_BLOCK];
     for (int64_t k = 0; k < n / B; ++k) {
         double a;
         ash_block_f64(x + k * B, B, tau, eps, &a, NULL, Z);
-        quantise_block(Z, a, B, codes + k * B, alpha + k, scale + k);
+        quantise_block(Z, a, B, fmt, codes + k * B, alpha + k, scale + k);
     }
     return 0;
 }
@@ -261,10 +391,10 @@ int taco_oracle_compress_f64(const double *x, int64_t n, int B, double tau,
 
 /* Reconstruct one block G'_k in double from its codes and float32 scalars. */
 static void reconstruct_block(const uint8_t *q, float alpha, float s, int B,
-                              double *out)
+                              int fmt, double *out)
 {
     for (int j = 0; j < B; ++j)                    /* Eq. 11 */
-        out[j] = taco_oracle_e4m3_decode(q[j]) * (double)s;
+        out[j] = decode_fmt(q[j], fmt) * (double)s;
     taco_oracle_fwht(out, B);                      /* Eq. 12 */
     double c = 1.0 / sqrt((double)B);
     for (int j = 0; j < B; ++j) out[j] = out[j] * c / (double)alpha; /* Eq. 13 */
@@ -272,23 +402,24 @@ static void reconstruct_block(const uint8_t *q, float alpha, float s, int B,
 
 /* G' in double precision (no output rounding), for error analysis. */
 int taco_oracle_reconstruct_f64(const uint8_t *codes, const float *alpha,
-                                const float *scale, int64_t n, int B,
+                                const float *scale, int64_t n, int B, int fmt,
                                 double *out)
 {
-    if (!valid_block(B) || n < 0 || n % B) return -1;
+    if (!valid_block(B) || !valid_fmt(fmt) || n < 0 || n % B) return -1;
     for (int64_t k = 0; k < n / B; ++k)
-        reconstruct_block(codes + k * B, alpha[k], scale[k], B, out + k * B);
+        reconstruct_block(codes + k * B, alpha[k], scale[k], B, fmt, out + k * B);
     return 0;
 }
 
 /* Decompress to bf16 (round to nearest even, once). */
 int taco_oracle_decompress(const uint8_t *codes, const float *alpha,
-                           const float *scale, int64_t n, int B, uint16_t *y)
+                           const float *scale, int64_t n, int B, int fmt,
+                           uint16_t *y)
 {
-    if (!valid_block(B) || n < 0 || n % B) return -1;
+    if (!valid_block(B) || !valid_fmt(fmt) || n < 0 || n % B) return -1;
     double g[ORACLE_MAX_BLOCK];
     for (int64_t k = 0; k < n / B; ++k) {
-        reconstruct_block(codes + k * B, alpha[k], scale[k], B, g);
+        reconstruct_block(codes + k * B, alpha[k], scale[k], B, fmt, g);
         for (int j = 0; j < B; ++j)
             y[k * B + j] = taco_oracle_double_to_bf16(g[j]);
     }
@@ -298,12 +429,12 @@ int taco_oracle_decompress(const uint8_t *codes, const float *alpha,
 /* acc += G' in float32: G' rounded once to float32, then one float32 add. */
 int taco_oracle_decompress_accumulate(const uint8_t *codes, const float *alpha,
                                       const float *scale, int64_t n, int B,
-                                      float *acc)
+                                      int fmt, float *acc)
 {
-    if (!valid_block(B) || n < 0 || n % B) return -1;
+    if (!valid_block(B) || !valid_fmt(fmt) || n < 0 || n % B) return -1;
     double g[ORACLE_MAX_BLOCK];
     for (int64_t k = 0; k < n / B; ++k) {
-        reconstruct_block(codes + k * B, alpha[k], scale[k], B, g);
+        reconstruct_block(codes + k * B, alpha[k], scale[k], B, fmt, g);
         for (int j = 0; j < B; ++j) {
             float gf = (float)g[j];
             acc[k * B + j] = acc[k * B + j] + gf;
@@ -320,26 +451,28 @@ int taco_oracle_decompress_accumulate(const uint8_t *codes, const float *alpha,
  * The reduce-scatter phase ends in one local reduction of the received
  * payloads, and the reduced segment is compressed again for the all-gather:
  * X = own + sum_p G'_p (Eq. 11-13 per payload, summed in double; own may be
- * NULL for a pure sum), then (codes, alpha, s) of X by Eq. 5-10.
+ * NULL for a pure sum), then (codes, alpha, s) of X by Eq. 5-10.  Payloads
+ * and result share one code format.
  */
 int taco_oracle_reduce_compress(const uint16_t *own, int npay,
                                 const uint8_t *const *codes_in,
                                 const float *const *alpha_in,
                                 const float *const *scale_in, int64_t n, int B,
-                                double tau, double eps, uint8_t *codes,
+                                double tau, double eps, int fmt, uint8_t *codes,
                                 float *alpha, float *scale)
 {
-    if (!valid_block(B) || n < 0 || n % B || npay < 0) return -1;
+    if (!valid_block(B) || !valid_fmt(fmt) || n < 0 || n % B || npay < 0) return -1;
     double X[ORACLE_MAX_BLOCK], g[ORACLE_MAX_BLOCK], Z[ORACLE_MAX_BLOCK];
     for (int64_t k = 0; k < n / B; ++k) {
         for (int j = 0; j < B; ++j) X[j] = own ? bf16_to_double(own[k * B + j]) : 0.0;
         for (int p = 0; p < npay; ++p) {
-            reconstruct_block(codes_in[p] + k * B, alpha_in[p][k], scale_in[p][k], B, g);
+            reconstruct_block(codes_in[p] + k * B, alpha_in[p][k], scale_in[p][k], B,
+                              fmt, g);
             for (int j = 0; j < B; ++j) X[j] += g[j];
         }
         double a;
         ash_block_f64(X, B, tau, eps, &a, NULL, Z);
-        quantise_block(Z, a, B, codes + k * B, alpha + k, scale + k);
+        quantise_block(Z, a, B, fmt, codes + k * B, alpha + k, scale + k);
     }
     return 0;
 }

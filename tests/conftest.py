@@ -71,3 +71,25 @@ def torch_e4m3_table() -> np.ndarray:
     import torch
     codes = torch.arange(256, dtype=torch.int32).to(torch.uint8)
     return codes.view(torch.float8_e4m3fn).to(torch.float64).numpy()
+
+
+def exhaustive_check(encoder_address: int, values: np.ndarray, twos: bool, nan_lo: int):
+    """Run tests/helpers/code_exhaustive.c over all 2^31 non-negative binary32
+    patterns (and their negatives).  Returns (mismatches, first bad pattern)."""
+    lib = ctypes.CDLL(build_helper("code_exhaustive"))
+    lib.code_check_range.restype = ctypes.c_int64
+    lib.code_check_range.argtypes = [ctypes.c_uint64, ctypes.c_uint64, ctypes.c_void_p,
+                                     ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                     ctypes.c_int, ctypes.POINTER(ctypes.c_uint32)]
+    vals = np.ascontiguousarray(values, dtype=np.float64)
+    first = ctypes.c_uint32(0)
+    bad = lib.code_check_range(0, 1 << 31, encoder_address, vals.ctypes.data_as(ctypes.c_void_p),
+                               vals.size, int(twos), nan_lo, cpu_threads(), ctypes.byref(first))
+    return int(bad), int(first.value)
+
+
+def torch_e5m2_table() -> np.ndarray:
+    """Values of all 256 E5M2 codes from torch's float8_e5m2 decoder."""
+    import torch
+    codes = torch.arange(256, dtype=torch.int32).to(torch.uint8)
+    return codes.view(torch.float8_e5m2).to(torch.float64).numpy()

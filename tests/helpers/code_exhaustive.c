@@ -1,15 +1,19 @@
 /*
- * Exhaustive check of an E4M3 encoder over every binary32 bit pattern.
+ * Exhaustive check of an 8-bit code encoder (E4M3, E5M2 or INT8) over every
+ * binary32 bit pattern.
  *
  * The expected code is derived independently of the encoder under test: the
- * caller passes the 127 non-negative finite E4M3 values in code order (taken
- * from a library decoder), and each input is placed between two neighbours by
- * binary search; it must map to the nearer one, to the code with a zero
- * mantissa LSB on an exact tie, and to 0x7E (448) from 448 upwards.  Negative
- * inputs must give the positive input's code with the sign bit set; NaN must
- * give a NaN code.
+ * caller passes the nvals non-negative finite values of the format in code
+ * order (taken from a library decoder or written out), and each input is
+ * placed between two neighbours by binary search; it must map to the nearer
+ * one, to the even code index on an exact tie (the code whose mantissa, or
+ * integer, is even), and to the largest code from the largest value upwards.
+ * A negative input must give the positive input's code negated: the sign bit
+ * set (sign-magnitude formats) or the two's complement of the code (INT8).
+ * NaN must give a code >= nan_lo in its low seven bits (sign-magnitude), or
+ * code 0 (two's complement).
  *
- * Build: gcc -O2 -fPIC -shared -pthread e4m3_exhaustive.c -o libe4m3_exhaustive.so
+ * Build: gcc -O2 -fPIC -shared -pthread code_exhaustive.c -o libcode_exhaustive.so
  */
 #include <math.h>
 #include <pthread.h>
@@ -21,23 +25,25 @@ typedef uint8_t (*enc_fn)(float);
 typedef struct {
     uint64_t lo, hi;          /* non-negative patterns [lo, hi) */
     enc_fn enc;
-    const double *vals;       /* 127 ascending values, codes 0x00..0x7E */
+    const double *vals;       /* nvals ascending values, codes 0..nvals-1 */
+    int nvals, twos, nan_lo;
     int64_t bad;
     uint32_t first_bad;
 } job_t;
 
-static uint8_t expected(double v, const double *vals)
+static int expected(double v, const double *vals, int nvals)
 {
-    if (v >= vals[126]) return 0x7E;
-    int lo = 0, hi = 126;                 /* vals[lo] <= v < vals[hi] */
+    const int top = nvals - 1;
+    if (v >= vals[top]) return top;
+    int lo = 0, hi = top;                 /* vals[lo] <= v < vals[hi] */
     while (hi - lo > 1) {
         int mid = (lo + hi) / 2;
         if (vals[mid] <= v) lo = mid; else hi = mid;
     }
     double m = 0.5 * (vals[lo] + vals[hi]);   /* exact in double */
-    if (v < m) return (uint8_t)lo;
-    if (v > m) return (uint8_t)hi;
-    return (uint8_t)((lo % 2 == 0) ? lo : hi);
+    if (v < m) return lo;
+    if (v > m) return hi;
+    return (lo % 2 == 0) ? lo : hi;
 }
 
 static void *run(void *arg)
@@ -54,10 +60,12 @@ static void *run(void *arg)
         uint8_t gotn = J->enc(fn);
         int ok;
         if (isnan(f)) {
-            ok = ((got & 0x7F) == 0x7F) && ((gotn & 0x7F) == 0x7F);
+            ok = J->twos ? (got == 0 && gotn == 0)
+                         : ((got & 0x7F) >= J->nan_lo && (gotn & 0x7F) >= J->nan_lo);
         } else {
-            uint8_t e = expected((double)f, J->vals);
-            ok = (got == e) && (gotn == (uint8_t)(e | 0x80));
+            int e = expected((double)f, J->vals, J->nvals);
+            uint8_t en = J->twos ? (uint8_t)(-e) : (uint8_t)(e | 0x80);
+            ok = (got == (uint8_t)e) && (gotn == en);
         }
         if (!ok) {
             if (J->bad == 0) J->first_bad = u;
@@ -68,8 +76,8 @@ static void *run(void *arg)
 }
 
 /* Returns the number of failing non-negative patterns in [lo, hi). */
-int64_t e4m3_check_range(uint64_t lo, uint64_t hi, void *enc, const double *vals,
-                         int nthreads, uint32_t *first_bad)
+int64_t code_check_range(uint64_t lo, uint64_t hi, void *enc, const double *vals, int nvals,
+                         int twos, int nan_lo, int nthreads, uint32_t *first_bad)
 {
     if (nthreads < 1) nthreads = 1;
     if (nthreads > 64) nthreads = 64;
@@ -81,6 +89,9 @@ int64_t e4m3_check_range(uint64_t lo, uint64_t hi, void *enc, const double *vals
         jobs[t].hi = lo + (hi - lo) * (uint64_t)(t + 1) / (uint64_t)nthreads;
         jobs[t].enc = (enc_fn)enc;
         jobs[t].vals = vals;
+        jobs[t].nvals = nvals;
+        jobs[t].twos = twos;
+        jobs[t].nan_lo = nan_lo;
         jobs[t].bad = 0;
         jobs[t].first_bad = 0;
     }
@@ -90,9 +101,8 @@ int64_t e4m3_check_range(uint64_t lo, uint64_t hi, void *enc, const double *vals
     run(&jobs[0]);
     int64_t bad = 0;
     *first_bad = 0;
-    for (int t = 0; t < nthreads; ++t) {
-        if (t > 0 && created[t]) pthread_join(th[t], NULL);
-    }
+    for (int t = 1; t < nthreads; ++t)
+        if (created[t]) pthread_join(th[t], NULL);
     for (int t = 0; t < nthreads; ++t) {
         if (jobs[t].bad && bad == 0) *first_bad = jobs[t].first_bad;
         bad += jobs[t].bad;

@@ -11,7 +11,7 @@ import math
 import numpy as np
 import pytest
 
-from conftest import build_helper, cpu_threads, read_golden, torch_e4m3_table
+from conftest import exhaustive_check, read_golden, torch_e4m3_table
 
 
 def test_decode_known_values(oracle_mod):
@@ -86,18 +86,11 @@ def test_encode_matches_torch_on_random_values(oracle_mod):
 
 def test_encode_exhaustive_every_float32(oracle_mod):
     """All 2^31 non-negative binary32 patterns (and their negatives)."""
-    lib = ctypes.CDLL(build_helper("e4m3_exhaustive"))
-    lib.e4m3_check_range.restype = ctypes.c_int64
-    lib.e4m3_check_range.argtypes = [ctypes.c_uint64, ctypes.c_uint64, ctypes.c_void_p,
-                                     ctypes.c_void_p, ctypes.c_int,
-                                     ctypes.POINTER(ctypes.c_uint32)]
     table = torch_e4m3_table()[:127].astype(np.float64).copy()   # library decoder
     assert np.all(np.diff(table) > 0) and table[126] == 448.0
-    first = ctypes.c_uint32(0)
-    bad = lib.e4m3_check_range(0, 1 << 31, oracle_mod.encode_function_address(),
-                               table.ctypes.data_as(ctypes.c_void_p), cpu_threads(),
-                               ctypes.byref(first))
-    assert bad == 0, f"{bad} mismatches, first pattern 0x{first.value:08x}"
+    bad, first = exhaustive_check(oracle_mod.encode_function_address("e4m3"), table,
+                                  twos=False, nan_lo=0x7F)
+    assert bad == 0, f"{bad} mismatches, first pattern 0x{first:08x}"
 
 
 def test_quantisation_error_within_eq3_bound(oracle_mod):
