@@ -19,7 +19,8 @@ the dominant kernel and the CPU oracle's rate on the same workload.
 
 ``NAME:owner`` times the fused owner step of the two-shot all-reduce
 (``taco_reduce_compress`` of an own partial plus three payloads) instead;
-``NAME:packed`` the round trip through the interleaved wire layout.
+``NAME:packed`` the round trip through the interleaved wire layout;
+``NAME:e5m2`` and ``NAME:int8`` the round trip with E5M2 or INT8 codes.
 """
 from __future__ import annotations
 
@@ -37,7 +38,7 @@ METRIC = "compress+decompress GB/s of bf16 input and % of MI355X HBM peak"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E peak (AMD specification), GB/s
 MALL_BYTES = 256 << 20
 ROTATE_BYTES = 2 * MALL_BYTES
-KERNEL_SRC = os.path.join(ROOT, "gradients_taco_compress_amd", "csrc", "taco.hip")
+KERNEL_DIR = os.path.join(ROOT, "gradients_taco_compress_amd", "csrc")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 
 
@@ -76,8 +77,14 @@ def algorithmic_bytes(op: str, n: int, block: int) -> float:
 
 
 def kernel_hash() -> str:
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """sha256[:16] over the library's sources (file names and contents, sorted)."""
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(KERNEL_DIR)):
+        if name.endswith((".hip", ".hpp")):
+            h.update(name.encode())
+            with open(os.path.join(KERNEL_DIR, name), "rb") as f:
+                h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def traffic_for(kernel: str, workload: str, block: int):
@@ -126,7 +133,7 @@ def make_graph(torch, fn, use_graph: bool):
 
 
 def roundtrip_case(torch, taco, synth, name: str, block: int, steps: int, warmup: int,
-                   use_graph: bool):
+                   use_graph: bool, fmt: str = "e4m3"):
     import numpy as np
     r = synth.WORKLOADS[name]
     n = r.numel
@@ -147,16 +154,16 @@ def roundtrip_case(torch, taco, synth, name: str, block: int, steps: int, warmup
 
     def run_compress():
         for x, codes, alpha, scale, _ in sets:
-            taco.compress(x, block=block, codes=codes, alpha=alpha, scale=scale)
+            taco.compress(x, block=block, codes=codes, alpha=alpha, scale=scale, fmt=fmt)
 
     def run_decompress():
         for _, codes, alpha, scale, y in sets:
-            taco.decompress(codes, alpha, scale, block=block, out=y)
+            taco.decompress(codes, alpha, scale, block=block, out=y, fmt=fmt)
 
     def run_steps():
         for x, codes, alpha, scale, y in sets:
-            taco.compress(x, block=block, codes=codes, alpha=alpha, scale=scale)
-            taco.decompress(codes, alpha, scale, block=block, out=y)
+            taco.compress(x, block=block, codes=codes, alpha=alpha, scale=scale, fmt=fmt)
+            taco.decompress(codes, alpha, scale, block=block, out=y, fmt=fmt)
 
     for _ in range(max(1, warmup // nsets)):
         run_steps()
@@ -172,7 +179,7 @@ def roundtrip_case(torch, taco, synth, name: str, block: int, steps: int, warmup
     t_c = timer.time(comp_fn, reps) / k
     t_d = timer.time(dec_fn, reps) / k
     return {"n": n, "block": block, "steps": k, "t_step": t_steps / k, "t_compress": t_c,
-            "t_decompress": t_d, "sets": nsets, "rows": r.rows, "cols": r.cols,
+            "t_decompress": t_d, "sets": nsets, "rows": r.rows, "cols": r.cols, "format": fmt,
             "bytes_step": algorithmic_bytes("compress", n, block)
             + algorithmic_bytes("decompress", n, block),
             "input_bytes_step": 2.0 * n, "kernels": {"compress": t_c, "decompress": t_d}}
@@ -351,7 +358,8 @@ def record(res, name: str, args, cpu=None):
     op = kern if kern != "reduce_compress" else f"reduce_compress:{res['npayloads']}"
     kbytes = algorithmic_bytes(op, res["n"], res["block"])
     achieved = kbytes / dur / 1e9
-    traffic = traffic_for(kern, name, res["block"])
+    fmt = res.get("format", "e4m3")
+    traffic = traffic_for(kern if fmt == "e4m3" else f"{kern}[{fmt}]", name, res["block"])
     rec = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -366,7 +374,7 @@ def record(res, name: str, args, cpu=None):
         "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": name, "tokens": res["rows"], "hidden": res["cols"],
-                   "block": res["block"], "target_energy": 1.0,
+                   "block": res["block"], "target_energy": 1.0, "format": fmt,
                    "step": ("4x compress + 4x decompress_accumulate" if "t_accumulate" in res
                             else f"reduce_compress of own + {res['npayloads']} payloads"
                             if "npayloads" in res
@@ -419,7 +427,9 @@ def main():
                  ("qwen7b_act_16384x3584", 128), ("qwen7b_act_16384x3584", 256),
                  ("grad_8192x8192", 256), ("gpt175b_hidden_32768x12288", 256),
                  ("gpt175b_hidden_32768x12288:owner", 256),
-                 ("gpt2.7b_rowpar_8192x2560:packed", 128)]
+                 ("gpt2.7b_rowpar_8192x2560:packed", 128),
+                 ("gpt2.7b_rowpar_8192x2560:e5m2", 128),
+                 ("gpt2.7b_rowpar_8192x2560:int8", 128)]
     else:
         name = args.workload or synth.DEFAULT_WORKLOAD
         block = args.block or synth.WORKLOADS[name.split(":")[0]].blocks[0]
@@ -436,6 +446,10 @@ def main():
         elif name.endswith(":packed"):
             name = name.split(":")[0]
             res = packed_case(torch, taco, synth, name, block, steps, args.warmup, use_graph)
+        elif name.endswith((":e5m2", ":int8")):
+            name, fmt = name.split(":")
+            res = roundtrip_case(torch, taco, synth, name, block, steps, args.warmup, use_graph,
+                                 fmt)
         elif acc:
             res = accumulate_case(torch, taco, synth, name, block, steps, args.warmup, use_graph)
         else:

@@ -8,16 +8,19 @@ the library has not been built (``python -m gradients_taco_compress_amd.build``)
 Two layers:
 
 * ``taco_compress``, ``taco_decompress``, ``taco_decompress_accumulate``,
-  ``taco_reduce_compress``, their ``*_packed`` forms, ``taco_packed_bytes``,
-  ``taco_e4m3_encode``, ``taco_e4m3_decode``, ``taco_num_blocks``,
-  ``taco_status_string``: the C ABI of ``include/taco.h``
-  with the same names and arguments (device pointers as ints, stream handle
-  as int, pointer arrays as sequences of ints).
+  ``taco_reduce_compress``, their ``*_packed`` forms, the ``*_fmt`` forms of
+  all eight (with a code format), ``taco_packed_bytes``, ``taco_encode``,
+  ``taco_decode``, ``taco_e4m3_encode``, ``taco_e4m3_decode``,
+  ``taco_num_blocks``, ``taco_status_string``: the C ABI of
+  ``include/taco.h`` with the same names and arguments (device pointers as
+  ints, stream handle as int, pointer arrays as sequences of ints, formats
+  as the ints of ``FORMATS``).
 * ``compress``, ``decompress``, ``decompress_accumulate``, ``reduce_compress``,
-  their ``*_packed`` forms on interleaved payloads, ``e4m3_encode``,
-  ``e4m3_decode``: the same calls on torch tensors,
+  their ``*_packed`` forms on interleaved payloads, ``encode``, ``decode``,
+  ``e4m3_encode``, ``e4m3_decode``: the same calls on torch tensors,
   allocating outputs when none are given and launching on torch's current
-  stream.
+  stream.  ``fmt`` names the code format ("e4m3", "e5m2" or "int8"); E4M3
+  goes through the entry points without a format.
 """
 from __future__ import annotations
 
@@ -29,6 +32,9 @@ LIB_PATH = os.path.join(PKG, "libtaco.so")
 
 #: Values fixed by the library (see include/taco.h).
 QMAX = 448.0
+#: Code formats (taco_format) and their Q_max.
+FORMATS = {"e4m3": 0, "e5m2": 1, "int8": 2}
+QMAX_OF = {"e4m3": 448.0, "e5m2": 57344.0, "int8": 127.0}
 EPS = 1e-20
 BLOCKS = (32, 64, 128, 256, 512)
 DEFAULT_TARGET_ENERGY = 1.0
@@ -36,6 +42,7 @@ DEFAULT_TARGET_ENERGY = 1.0
 STATUS = {
     0: "TACO_OK", 1: "TACO_ERR_NULL", 2: "TACO_ERR_SHAPE", 3: "TACO_ERR_BLOCK",
     4: "TACO_ERR_PARAM", 5: "TACO_ERR_ALIGN", 6: "TACO_ERR_ALIAS", 7: "TACO_ERR_HIP",
+    8: "TACO_ERR_FORMAT",
 }
 
 
@@ -77,6 +84,23 @@ _lib.taco_e4m3_encode.argtypes = [_P, _I64, _P, _P]
 _lib.taco_e4m3_encode.restype = ctypes.c_int
 _lib.taco_e4m3_decode.argtypes = [_P, _I64, _P, _P]
 _lib.taco_e4m3_decode.restype = ctypes.c_int
+_lib.taco_compress_fmt.argtypes = [_P, _I64, _I64, _I32, _F32, _I32, _P, _P, _P, _P]
+_lib.taco_decompress_fmt.argtypes = [_P, _P, _P, _I64, _I64, _I32, _I32, _P, _P]
+_lib.taco_decompress_accumulate_fmt.argtypes = [_P, _P, _P, _I64, _I64, _I32, _I32, _P, _P]
+_lib.taco_reduce_compress_fmt.argtypes = [_P, _I32, _P, _P, _P, _I64, _I64, _I32, _F32, _I32,
+                                          _P, _P, _P, _P]
+_lib.taco_compress_packed_fmt.argtypes = [_P, _I64, _I64, _I32, _F32, _I32, _P, _P]
+_lib.taco_decompress_packed_fmt.argtypes = [_P, _I64, _I64, _I32, _I32, _P, _P]
+_lib.taco_decompress_accumulate_packed_fmt.argtypes = [_P, _I64, _I64, _I32, _I32, _P, _P]
+_lib.taco_reduce_compress_packed_fmt.argtypes = [_P, _I32, _P, _I64, _I64, _I32, _F32, _I32,
+                                                 _P, _P]
+_lib.taco_encode.argtypes = [_I32, _P, _I64, _P, _P]
+_lib.taco_decode.argtypes = [_I32, _P, _I64, _P, _P]
+for _name in ("compress_fmt", "decompress_fmt", "decompress_accumulate_fmt",
+              "reduce_compress_fmt", "compress_packed_fmt", "decompress_packed_fmt",
+              "decompress_accumulate_packed_fmt", "reduce_compress_packed_fmt", "encode",
+              "decode"):
+    getattr(_lib, "taco_" + _name).restype = ctypes.c_int
 _lib.taco_status_string.argtypes = [ctypes.c_int]
 _lib.taco_status_string.restype = ctypes.c_char_p
 
@@ -85,7 +109,11 @@ EXPORTS = ("taco_num_blocks", "taco_compress", "taco_decompress",
            "taco_decompress_accumulate", "taco_reduce_compress", "taco_packed_bytes",
            "taco_compress_packed", "taco_decompress_packed", "taco_decompress_accumulate_packed",
            "taco_reduce_compress_packed", "taco_e4m3_encode", "taco_e4m3_decode",
-           "taco_status_string")
+           "taco_status_string", "taco_compress_fmt", "taco_decompress_fmt",
+           "taco_decompress_accumulate_fmt", "taco_reduce_compress_fmt",
+           "taco_compress_packed_fmt", "taco_decompress_packed_fmt",
+           "taco_decompress_accumulate_packed_fmt", "taco_reduce_compress_packed_fmt",
+           "taco_encode", "taco_decode")
 
 #: Most payloads one taco_reduce_compress call sums.
 MAX_PAYLOADS = 8
@@ -163,6 +191,68 @@ def taco_reduce_compress_packed(own_bf16: int, npayloads: int, payloads, tokens:
                                             target_energy, out_payload, stream)
 
 
+def taco_compress_fmt(x_bf16: int, tokens: int, hidden: int, block: int, target_energy: float,
+                      format: int, codes: int, alpha: int, scale: int, stream: int) -> int:
+    return _lib.taco_compress_fmt(x_bf16, tokens, hidden, block, target_energy, format, codes,
+                                  alpha, scale, stream)
+
+
+def taco_decompress_fmt(codes: int, alpha: int, scale: int, tokens: int, hidden: int, block: int,
+                        format: int, y_bf16: int, stream: int) -> int:
+    return _lib.taco_decompress_fmt(codes, alpha, scale, tokens, hidden, block, format, y_bf16,
+                                    stream)
+
+
+def taco_decompress_accumulate_fmt(codes: int, alpha: int, scale: int, tokens: int, hidden: int,
+                                   block: int, format: int, acc_f32: int, stream: int) -> int:
+    return _lib.taco_decompress_accumulate_fmt(codes, alpha, scale, tokens, hidden, block, format,
+                                               acc_f32, stream)
+
+
+def taco_reduce_compress_fmt(own_bf16: int, npayloads: int, codes, alpha, scale, tokens: int,
+                             hidden: int, block: int, target_energy: float, format: int,
+                             out_codes: int, out_alpha: int, out_scale: int, stream: int) -> int:
+    arrs = [None if a is None else _ptr_array(a) for a in (codes, alpha, scale)]
+    args = [None if a is None else ctypes.cast(a, ctypes.c_void_p) for a in arrs]
+    return _lib.taco_reduce_compress_fmt(own_bf16, npayloads, args[0], args[1], args[2], tokens,
+                                         hidden, block, target_energy, format, out_codes,
+                                         out_alpha, out_scale, stream)
+
+
+def taco_compress_packed_fmt(x_bf16: int, tokens: int, hidden: int, block: int,
+                             target_energy: float, format: int, payload: int,
+                             stream: int) -> int:
+    return _lib.taco_compress_packed_fmt(x_bf16, tokens, hidden, block, target_energy, format,
+                                         payload, stream)
+
+
+def taco_decompress_packed_fmt(payload: int, tokens: int, hidden: int, block: int, format: int,
+                               y_bf16: int, stream: int) -> int:
+    return _lib.taco_decompress_packed_fmt(payload, tokens, hidden, block, format, y_bf16, stream)
+
+
+def taco_decompress_accumulate_packed_fmt(payload: int, tokens: int, hidden: int, block: int,
+                                          format: int, acc_f32: int, stream: int) -> int:
+    return _lib.taco_decompress_accumulate_packed_fmt(payload, tokens, hidden, block, format,
+                                                      acc_f32, stream)
+
+
+def taco_reduce_compress_packed_fmt(own_bf16: int, npayloads: int, payloads, tokens: int,
+                                    hidden: int, block: int, target_energy: float, format: int,
+                                    out_payload: int, stream: int) -> int:
+    arr = None if payloads is None else ctypes.cast(_ptr_array(payloads), ctypes.c_void_p)
+    return _lib.taco_reduce_compress_packed_fmt(own_bf16, npayloads, arr, tokens, hidden, block,
+                                                target_energy, format, out_payload, stream)
+
+
+def taco_encode(format: int, x: int, n: int, codes: int, stream: int) -> int:
+    return _lib.taco_encode(format, x, n, codes, stream)
+
+
+def taco_decode(format: int, codes: int, n: int, out: int, stream: int) -> int:
+    return _lib.taco_decode(format, codes, n, out, stream)
+
+
 def taco_e4m3_encode(x: int, n: int, codes: int, stream: int) -> int:
     return _lib.taco_e4m3_encode(x, n, codes, stream)
 
@@ -208,17 +298,32 @@ def _check(status: int, what: str):
         raise TacoError(status, what)
 
 
+def _format(fmt: str) -> int:
+    try:
+        return FORMATS[fmt]
+    except KeyError:
+        raise ValueError(f"unknown code format {fmt!r} (one of {sorted(FORMATS)})") from None
+
+
+def _compress_call(fmt, x, tokens, hidden, block, tau, codes, alpha, scale, stream):
+    if fmt == "e4m3":
+        return taco_compress(x, tokens, hidden, block, tau, codes, alpha, scale, stream)
+    return taco_compress_fmt(x, tokens, hidden, block, tau, _format(fmt), codes, alpha, scale,
+                             stream)
+
+
 def compress(x, block: int = 256, target_energy: float = DEFAULT_TARGET_ENERGY,
-             codes=None, alpha=None, scale=None, stream=None):
+             codes=None, alpha=None, scale=None, stream=None, fmt: str = "e4m3"):
     """Compress a bf16 tensor [..., hidden]: returns (codes uint8 same shape,
     alpha float32 [M], scale float32 [M])."""
     torch = _torch()
+    _format(fmt)
     _need(x, torch.bfloat16, "x")
     tokens, hidden = _shape2(x)
     m = taco_num_blocks(tokens, hidden, block)
     if m < 0:   # let the library name the validation error
-        _check(taco_compress(x.data_ptr(), tokens, hidden, block, float(target_energy),
-                             0, 0, 0, _stream(stream)), "taco_compress")
+        _check(_compress_call(fmt, x.data_ptr(), tokens, hidden, block, float(target_energy),
+                              0, 0, 0, _stream(stream)), "taco_compress")
     if codes is None:
         codes = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
     if alpha is None:
@@ -230,8 +335,8 @@ def compress(x, block: int = 256, target_energy: float = DEFAULT_TARGET_ENERGY,
     _need(scale, torch.float32, "scale")
     if codes.numel() != x.numel() or alpha.numel() < m or scale.numel() < m:
         raise ValueError("output buffers are too small")
-    _check(taco_compress(x.data_ptr(), tokens, hidden, block, float(target_energy),
-                         codes.data_ptr(), alpha.data_ptr(), scale.data_ptr(), _stream(stream)),
+    _check(_compress_call(fmt, x.data_ptr(), tokens, hidden, block, float(target_energy),
+                          codes.data_ptr(), alpha.data_ptr(), scale.data_ptr(), _stream(stream)),
            "taco_compress")
     return codes, alpha, scale
 
@@ -248,39 +353,54 @@ def _receiver_args(codes, alpha, scale, block):
     return tokens, hidden
 
 
-def decompress(codes, alpha, scale, block: int = 256, out=None, stream=None):
+def decompress(codes, alpha, scale, block: int = 256, out=None, stream=None, fmt: str = "e4m3"):
     """Reconstruct a bf16 tensor with the shape of ``codes``."""
     torch = _torch()
+    f = _format(fmt)
     tokens, hidden = _receiver_args(codes, alpha, scale, block)
     if out is None:
         out = torch.empty(codes.shape, dtype=torch.bfloat16, device=codes.device)
     _need(out, torch.bfloat16, "out")
     if out.numel() != codes.numel():
         raise ValueError("out must have as many elements as codes")
-    _check(taco_decompress(codes.data_ptr(), alpha.data_ptr(), scale.data_ptr(), tokens, hidden,
-                           block, out.data_ptr(), _stream(stream)), "taco_decompress")
+    if fmt == "e4m3":
+        st = taco_decompress(codes.data_ptr(), alpha.data_ptr(), scale.data_ptr(), tokens, hidden,
+                             block, out.data_ptr(), _stream(stream))
+    else:
+        st = taco_decompress_fmt(codes.data_ptr(), alpha.data_ptr(), scale.data_ptr(), tokens,
+                                 hidden, block, f, out.data_ptr(), _stream(stream))
+    _check(st, "taco_decompress")
     return out
 
 
-def decompress_accumulate(codes, alpha, scale, acc, block: int = 256, stream=None):
+def decompress_accumulate(codes, alpha, scale, acc, block: int = 256, stream=None,
+                          fmt: str = "e4m3"):
     """acc (float32, same number of elements as codes) += reconstruction."""
     torch = _torch()
+    f = _format(fmt)
     tokens, hidden = _receiver_args(codes, alpha, scale, block)
     _need(acc, torch.float32, "acc")
     if acc.numel() != codes.numel():
         raise ValueError("acc must have as many elements as codes")
-    _check(taco_decompress_accumulate(codes.data_ptr(), alpha.data_ptr(), scale.data_ptr(), tokens,
-                                      hidden, block, acc.data_ptr(), _stream(stream)),
-           "taco_decompress_accumulate")
+    if fmt == "e4m3":
+        st = taco_decompress_accumulate(codes.data_ptr(), alpha.data_ptr(), scale.data_ptr(),
+                                        tokens, hidden, block, acc.data_ptr(), _stream(stream))
+    else:
+        st = taco_decompress_accumulate_fmt(codes.data_ptr(), alpha.data_ptr(), scale.data_ptr(),
+                                            tokens, hidden, block, f, acc.data_ptr(),
+                                            _stream(stream))
+    _check(st, "taco_decompress_accumulate")
     return acc
 
 
 def reduce_compress(own, payloads, block: int = 256, target_energy: float = DEFAULT_TARGET_ENERGY,
-                    codes=None, alpha=None, scale=None, stream=None):
+                    codes=None, alpha=None, scale=None, stream=None, fmt: str = "e4m3"):
     """Owner step: compress own + the sum of the payloads' reconstructions.
     own: bf16 tensor or None; payloads: list of (codes, alpha, scale) as
-    returned by compress().  Returns (codes, alpha, scale)."""
+    returned by compress() with the same format.  Returns (codes, alpha,
+    scale)."""
     torch = _torch()
+    f = _format(fmt)
     ref = own if own is not None else (payloads[0][0] if payloads else None)
     if ref is None:
         raise ValueError("need own or at least one payload")
@@ -311,13 +431,17 @@ def reduce_compress(own, payloads, block: int = 256, target_energy: float = DEFA
     if codes.numel() != ref.numel() or alpha.numel() < m or scale.numel() < m:
         raise ValueError("output buffers are too small")
     n = len(payloads)
-    _check(taco_reduce_compress(0 if own is None else own.data_ptr(), n,
-                                [c.data_ptr() for c, _, _ in payloads] if n else None,
-                                [a.data_ptr() for _, a, _ in payloads] if n else None,
-                                [s.data_ptr() for _, _, s in payloads] if n else None,
-                                tokens, hidden, block, float(target_energy), codes.data_ptr(),
-                                alpha.data_ptr(), scale.data_ptr(), _stream(stream)),
-           "taco_reduce_compress")
+    args = (0 if own is None else own.data_ptr(), n,
+            [c.data_ptr() for c, _, _ in payloads] if n else None,
+            [a.data_ptr() for _, a, _ in payloads] if n else None,
+            [s.data_ptr() for _, _, s in payloads] if n else None,
+            tokens, hidden, block, float(target_energy))
+    outs = (codes.data_ptr(), alpha.data_ptr(), scale.data_ptr(), _stream(stream))
+    if fmt == "e4m3":
+        st = taco_reduce_compress(*args, *outs)
+    else:
+        st = taco_reduce_compress_fmt(*args, f, *outs)
+    _check(st, "taco_reduce_compress")
     return codes, alpha, scale
 
 
@@ -329,9 +453,10 @@ def _packed_len(tokens, hidden, block):
 
 
 def compress_packed(x, block: int = 256, target_energy: float = DEFAULT_TARGET_ENERGY,
-                    payload=None, stream=None):
+                    payload=None, stream=None, fmt: str = "e4m3"):
     """Compress a bf16 tensor into one interleaved payload (uint8, 1-D)."""
     torch = _torch()
+    f = _format(fmt)
     _need(x, torch.bfloat16, "x")
     tokens, hidden = _shape2(x)
     nb = _packed_len(tokens, hidden, block)
@@ -340,14 +465,21 @@ def compress_packed(x, block: int = 256, target_energy: float = DEFAULT_TARGET_E
     _need(payload, torch.uint8, "payload")
     if payload.numel() < nb:
         raise ValueError("payload buffer is too small")
-    _check(taco_compress_packed(x.data_ptr(), tokens, hidden, block, float(target_energy),
-                                payload.data_ptr(), _stream(stream)), "taco_compress_packed")
+    if fmt == "e4m3":
+        st = taco_compress_packed(x.data_ptr(), tokens, hidden, block, float(target_energy),
+                                  payload.data_ptr(), _stream(stream))
+    else:
+        st = taco_compress_packed_fmt(x.data_ptr(), tokens, hidden, block, float(target_energy),
+                                      f, payload.data_ptr(), _stream(stream))
+    _check(st, "taco_compress_packed")
     return payload
 
 
-def decompress_packed(payload, shape, block: int = 256, out=None, stream=None):
+def decompress_packed(payload, shape, block: int = 256, out=None, stream=None,
+                      fmt: str = "e4m3"):
     """Reconstruct a bf16 tensor of the given shape from an interleaved payload."""
     torch = _torch()
+    f = _format(fmt)
     _need(payload, torch.uint8, "payload")
     hidden = shape[-1]
     tokens = 1
@@ -358,29 +490,41 @@ def decompress_packed(payload, shape, block: int = 256, out=None, stream=None):
     if out is None:
         out = torch.empty(shape, dtype=torch.bfloat16, device=payload.device)
     _need(out, torch.bfloat16, "out")
-    _check(taco_decompress_packed(payload.data_ptr(), tokens, hidden, block, out.data_ptr(),
-                                  _stream(stream)), "taco_decompress_packed")
+    if fmt == "e4m3":
+        st = taco_decompress_packed(payload.data_ptr(), tokens, hidden, block, out.data_ptr(),
+                                    _stream(stream))
+    else:
+        st = taco_decompress_packed_fmt(payload.data_ptr(), tokens, hidden, block, f,
+                                        out.data_ptr(), _stream(stream))
+    _check(st, "taco_decompress_packed")
     return out
 
 
-def decompress_accumulate_packed(payload, acc, block: int = 256, stream=None):
+def decompress_accumulate_packed(payload, acc, block: int = 256, stream=None, fmt: str = "e4m3"):
     """acc (float32) += reconstruction of an interleaved payload."""
     torch = _torch()
+    f = _format(fmt)
     _need(payload, torch.uint8, "payload")
     _need(acc, torch.float32, "acc")
     tokens, hidden = _shape2(acc)
     if payload.numel() < _packed_len(tokens, hidden, block):
         raise ValueError("payload is too small for acc's shape")
-    _check(taco_decompress_accumulate_packed(payload.data_ptr(), tokens, hidden, block,
-                                             acc.data_ptr(), _stream(stream)),
-           "taco_decompress_accumulate_packed")
+    if fmt == "e4m3":
+        st = taco_decompress_accumulate_packed(payload.data_ptr(), tokens, hidden, block,
+                                               acc.data_ptr(), _stream(stream))
+    else:
+        st = taco_decompress_accumulate_packed_fmt(payload.data_ptr(), tokens, hidden, block, f,
+                                                   acc.data_ptr(), _stream(stream))
+    _check(st, "taco_decompress_accumulate_packed")
     return acc
 
 
 def reduce_compress_packed(own, payloads, shape=None, block: int = 256,
-                           target_energy: float = DEFAULT_TARGET_ENERGY, out=None, stream=None):
+                           target_energy: float = DEFAULT_TARGET_ENERGY, out=None, stream=None,
+                           fmt: str = "e4m3"):
     """Owner step on interleaved payloads: returns one interleaved payload."""
     torch = _torch()
+    f = _format(fmt)
     if own is not None:
         _need(own, torch.bfloat16, "own")
         shape = own.shape
@@ -400,10 +544,14 @@ def reduce_compress_packed(own, payloads, shape=None, block: int = 256,
         out = torch.empty(nb, dtype=torch.uint8, device=dev)
     _need(out, torch.uint8, "out")
     n = len(payloads)
-    _check(taco_reduce_compress_packed(0 if own is None else own.data_ptr(), n,
-                                       [p.data_ptr() for p in payloads] if n else None,
-                                       tokens, hidden, block, float(target_energy), out.data_ptr(),
-                                       _stream(stream)), "taco_reduce_compress_packed")
+    args = (0 if own is None else own.data_ptr(), n,
+            [p.data_ptr() for p in payloads] if n else None, tokens, hidden, block,
+            float(target_energy))
+    if fmt == "e4m3":
+        st = taco_reduce_compress_packed(*args, out.data_ptr(), _stream(stream))
+    else:
+        st = taco_reduce_compress_packed_fmt(*args, f, out.data_ptr(), _stream(stream))
+    _check(st, "taco_reduce_compress_packed")
     return out
 
 
@@ -428,4 +576,29 @@ def e4m3_decode(codes, out=None, stream=None):
     _need(out, torch.float32, "out")
     _check(taco_e4m3_decode(codes.data_ptr(), codes.numel(), out.data_ptr(), _stream(stream)),
            "taco_e4m3_decode")
+    return out
+
+
+def encode(x, fmt: str = "e4m3", out=None, stream=None):
+    """Element-wise codes of a float32 tensor in a format (the kernels' conversion)."""
+    torch = _torch()
+    f = _format(fmt)
+    _need(x, torch.float32, "x")
+    if out is None:
+        out = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    _need(out, torch.uint8, "out")
+    _check(taco_encode(f, x.data_ptr(), x.numel(), out.data_ptr(), _stream(stream)), "taco_encode")
+    return out
+
+
+def decode(codes, fmt: str = "e4m3", out=None, stream=None):
+    """Element-wise float32 values of codes in a format (the kernels' conversion)."""
+    torch = _torch()
+    f = _format(fmt)
+    _need(codes, torch.uint8, "codes")
+    if out is None:
+        out = torch.empty(codes.shape, dtype=torch.float32, device=codes.device)
+    _need(out, torch.float32, "out")
+    _check(taco_decode(f, codes.data_ptr(), codes.numel(), out.data_ptr(), _stream(stream)),
+           "taco_decode")
     return out

@@ -10,7 +10,13 @@ import sys
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-SRC = os.path.join(PKG, "csrc", "taco.hip")
+CSRC = os.path.join(PKG, "csrc")
+#: Translation units: one kernel set per code format, plus the C ABI.
+SOURCES = [os.path.join(CSRC, f) for f in
+           ("taco_abi.hip", "taco_e4m3.hip", "taco_e5m2.hip", "taco_int8.hip")]
+#: Every file the library is built from (sources and headers).
+ALL_FILES = SOURCES + [os.path.join(CSRC, "taco_kernels.hpp"),
+                       os.path.join(CSRC, "taco_internal.hpp")]
 HEADER = os.path.join(ROOT, "include", "taco.h")
 LIB = os.path.join(PKG, "libtaco.so")
 
@@ -21,29 +27,44 @@ FLAGS = [
     "-O3",
     "-std=c++17",
     "-fPIC",
-    "-shared",
     "-Wall",
     # No packed-FP32 instructions anywhere in the device code.
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
 ]
 
+# hipcc's host pass does not know the packed-fp32 feature and says so.
+_NOISE = "'-packed-fp32-ops' is not a recognized feature"
 
-def build(verbose: bool = False) -> str:
-    """Compile every source into LIB (always recompiles)."""
-    tmp = LIB + f".tmp{os.getpid()}"
-    cmd = [HIPCC, *FLAGS, "-I", os.path.join(ROOT, "include"), SRC, "-o", tmp]
+
+def _run(cmd, verbose: bool) -> None:
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
-    # hipcc's host pass does not know the packed-fp32 feature and says so;
-    # everything else is shown.
-    noise = "'-packed-fp32-ops' is not a recognized feature"
-    msgs = [ln for ln in (res.stdout + res.stderr).splitlines() if noise not in ln]
+    msgs = [ln for ln in (res.stdout + res.stderr).splitlines() if _NOISE not in ln]
     if res.returncode != 0:
         raise RuntimeError("hipcc failed:\n" + "\n".join(msgs))
     if msgs and verbose:
         print("\n".join(msgs))
-    os.replace(tmp, LIB)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source (in parallel) and link LIB; always recompiles."""
+    from concurrent.futures import ThreadPoolExecutor
+    tag = f".tmp{os.getpid()}"
+    objs = [os.path.join(CSRC, os.path.basename(src) + tag + ".o") for src in SOURCES]
+    try:
+        with ThreadPoolExecutor(max_workers=len(SOURCES)) as pool:
+            jobs = [pool.submit(_run, [HIPCC, *FLAGS, "-I", os.path.join(ROOT, "include"),
+                                       "-c", src, "-o", obj], verbose)
+                    for src, obj in zip(SOURCES, objs)]
+            for j in jobs:
+                j.result()
+        _run([HIPCC, "--offload-arch=gfx950", "-shared", *objs, "-o", LIB + tag], verbose)
+        os.replace(LIB + tag, LIB)
+    finally:
+        for path in objs + [LIB + tag]:
+            if os.path.exists(path):
+                os.remove(path)
     return LIB
 
 

@@ -1,0 +1,5 @@
+// libtaco kernels for E5M2 codes (one translation unit per code format keeps
+// each compilation small; see taco_kernels.hpp for the kernels).
+#include "taco_kernels.hpp"
+
+template struct taco_internal::Ops<taco_internal::Fmt::kE5M2>;

@@ -1,4 +1,6 @@
-// libtaco: the TACO compression operator as hand-written HIP for gfx950.
+// libtaco kernels: the TACO compression operator as hand-written HIP for
+// gfx950, templated on the code format.  Each taco_<format>.hip includes this
+// file and instantiates Ops<format>; the C ABI (taco_abi.hip) calls those.
 //
 // Operator: [TACO] = the page "TACO: Efficient Communication Compression of
 // Intermediate Tensors for Scalable Tensor-Parallel LLM Training", section
@@ -31,22 +33,27 @@
 //    the kernel rotates the raw block R = H x, reduces sum x^2 and max |R|,
 //    and quantises v = R * (Q / max|R|).  alpha and s are computed once per
 //    block from the two reductions.
-//  * Stores: packed E4M3 (v_cvt_pk_fp8_f32, OCP E4M3FN on gfx950, round to
-//    nearest even), 8 codes per lane per chunk; alpha / s as float32
-//    side-buffers.  Decompress decodes with v_cvt_pk_f32_fp8 and rounds to
-//    bf16 with v_cvt_pk_bf16_f32.
+//  * Stores: 8 codes per lane per chunk; alpha / s as float32.  E4M3 and E5M2
+//    use the hardware conversions (v_cvt_pk_fp8_f32 / v_cvt_pk_bf8_f32, OCP
+//    formats on gfx950, round to nearest even); INT8 rounds with one float
+//    addition (see Codec<Fmt::kInt8>).  Decompress decodes, rotates and
+//    rounds to bf16 with v_cvt_pk_bf16_f32.
 //  * Grid-stride loop over wave-steps (one step per wave by default, so a
 //    large tensor launches tens of thousands of work-groups); when a wave
 //    has several steps, the next step's loads are issued before the current
 //    step is processed.  Loads and stores are non-temporal: every byte is
 //    streamed once.
 
+#pragma once
+
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <math.h>
 
 #include "taco.h"
+#include "taco_internal.hpp"
 
+namespace taco_internal {
 namespace {
 
 typedef float f2v __attribute__((ext_vector_type(2)));
@@ -110,14 +117,12 @@ struct Geo {
     static_assert((LPB == 4 || LPB == 8) && EPL >= 8, "lane layout");
 };
 
-// Where block k's codes, alpha and s live.
+// Where block k's codes, alpha and s live (Layout):
 //  kSide:   codes[k*B .. k*B+B), alpha[k], scale[k] (three buffers).
 //  kPacked: one record of B + 8 bytes per block ([TACO] section 4.4.2, the
 //           zero-copy metadata layout): the block's codes, then alpha_k and
 //           s_k as float32; `alpha` and `scale` point at record 0's
 //           scalars, so block k's are alpha[k * kScalarStride].
-enum class Layout { kSide, kPacked };
-
 template <int B, Layout L>
 struct Wire {
     static constexpr int64_t kRecord = (L == Layout::kPacked) ? B + 8 : B;     // bytes
@@ -349,30 +354,97 @@ __device__ __forceinline__ Quot quotient(float q, float m) {
     return {hi, lo};
 }
 
-// Packs 8 values into 8 E4M3 codes (little-endian: element j in byte j).
-// The argument of the conversion is v * (hi + lo) with a single final
-// rounding, i.e. float32 of v * Q / m almost always correctly rounded; the
-// +0 addend of the inner fma maps an exact zero of either sign to +0 (code
-// 0x00).
+// Code formats: Q_max of Eq. 9 and the conversions of Eq. 10 (pack8: the
+// codes of 8 float32 values) and Eq. 11 (decode8: the values of 8 codes).
+// Codes are little-endian, element j in byte j.  encode8 gives the codes of
+// v * Q / m for 8 values, given Q / m as hi + lo: the argument of the
+// conversion is v * (hi + lo) with a single final rounding, i.e. float32 of
+// v * Q / m almost always correctly rounded; the +0 addend of the inner fma
+// maps an exact zero of either sign to +0.
+template <Fmt F>
+struct Codec;
+
+template <Fmt F>
 __device__ __forceinline__ u2v encode8(const float *v, Quot r) {
     float q[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) q[j] = fmaf(v[j], r.hi, fmaf(v[j], r.lo, 0.0f));
-    int lo = __builtin_amdgcn_cvt_pk_fp8_f32(q[0], q[1], 0, false);
-    lo = __builtin_amdgcn_cvt_pk_fp8_f32(q[2], q[3], lo, true);
-    int hi = __builtin_amdgcn_cvt_pk_fp8_f32(q[4], q[5], 0, false);
-    hi = __builtin_amdgcn_cvt_pk_fp8_f32(q[6], q[7], hi, true);
-    return (u2v){(uint32_t)lo, (uint32_t)hi};
+    return Codec<F>::pack8(q);
 }
 
-__device__ __forceinline__ void decode8(const u2v c, float *v) {
-    f2v a = __builtin_amdgcn_cvt_pk_f32_fp8((int)c.x, false);
-    f2v b = __builtin_amdgcn_cvt_pk_f32_fp8((int)c.x, true);
-    f2v d = __builtin_amdgcn_cvt_pk_f32_fp8((int)c.y, false);
-    f2v e = __builtin_amdgcn_cvt_pk_f32_fp8((int)c.y, true);
-    v[0] = a.x; v[1] = a.y; v[2] = b.x; v[3] = b.y;
-    v[4] = d.x; v[5] = d.y; v[6] = e.x; v[7] = e.y;
-}
+// OCP E4M3 ("E4M3FN"), the operator's format ([TACO] section 4.3).
+template <>
+struct Codec<Fmt::kE4M3> {
+    static constexpr float kQmax = TACO_QMAX;
+    static __device__ __forceinline__ u2v pack8(const float *q) {
+        int lo = __builtin_amdgcn_cvt_pk_fp8_f32(q[0], q[1], 0, false);
+        lo = __builtin_amdgcn_cvt_pk_fp8_f32(q[2], q[3], lo, true);
+        int hi = __builtin_amdgcn_cvt_pk_fp8_f32(q[4], q[5], 0, false);
+        hi = __builtin_amdgcn_cvt_pk_fp8_f32(q[6], q[7], hi, true);
+        return (u2v){(uint32_t)lo, (uint32_t)hi};
+    }
+    static __device__ __forceinline__ void decode8(const u2v c, float *v) {
+        f2v a = __builtin_amdgcn_cvt_pk_f32_fp8((int)c.x, false);
+        f2v b = __builtin_amdgcn_cvt_pk_f32_fp8((int)c.x, true);
+        f2v d = __builtin_amdgcn_cvt_pk_f32_fp8((int)c.y, false);
+        f2v e = __builtin_amdgcn_cvt_pk_f32_fp8((int)c.y, true);
+        v[0] = a.x; v[1] = a.y; v[2] = b.x; v[3] = b.y;
+        v[4] = d.x; v[5] = d.y; v[6] = e.x; v[7] = e.y;
+    }
+};
+
+// OCP E5M2 ([TACO] section 5.3.2 format ablation; section 2.3 / Figure 3).
+template <>
+struct Codec<Fmt::kE5M2> {
+    static constexpr float kQmax = TACO_E5M2_MAX;
+    static __device__ __forceinline__ u2v pack8(const float *q) {
+        int lo = __builtin_amdgcn_cvt_pk_bf8_f32(q[0], q[1], 0, false);
+        lo = __builtin_amdgcn_cvt_pk_bf8_f32(q[2], q[3], lo, true);
+        int hi = __builtin_amdgcn_cvt_pk_bf8_f32(q[4], q[5], 0, false);
+        hi = __builtin_amdgcn_cvt_pk_bf8_f32(q[6], q[7], hi, true);
+        return (u2v){(uint32_t)lo, (uint32_t)hi};
+    }
+    static __device__ __forceinline__ void decode8(const u2v c, float *v) {
+        f2v a = __builtin_amdgcn_cvt_pk_f32_bf8((int)c.x, false);
+        f2v b = __builtin_amdgcn_cvt_pk_f32_bf8((int)c.x, true);
+        f2v d = __builtin_amdgcn_cvt_pk_f32_bf8((int)c.y, false);
+        f2v e = __builtin_amdgcn_cvt_pk_f32_bf8((int)c.y, true);
+        v[0] = a.x; v[1] = a.y; v[2] = b.x; v[3] = b.y;
+        v[4] = d.x; v[5] = d.y; v[6] = e.x; v[7] = e.y;
+    }
+};
+
+// Symmetric INT8 with the dual scale as its step ([TACO] section 6 fallback;
+// quantiser of section 2.3 / Eq. 1): q = round(Z / s) in [-127, 127] as a
+// two's complement byte.  For |q| < 2^22, float32 q + 1.5 * 2^23 rounds q to
+// the nearest integer, ties to even, in one addition, and the low byte of
+// the sum's bit pattern is that integer's two's complement byte.  Arguments
+// never exceed 127 in magnitude (Z / s <= Q_max), so no clamp is needed.
+template <>
+struct Codec<Fmt::kInt8> {
+    static constexpr float kQmax = TACO_INT8_MAX;
+    static __device__ __forceinline__ u2v pack8(const float *q) {
+        uint32_t w[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) w[j] = __float_as_uint(q[j] + 0x1.8p23f);
+        // v_perm_b32 byte selectors: 0-3 pick bytes of the second operand,
+        // 4-7 bytes of the first, 0x0c gives a zero byte.
+        const uint32_t lo = __builtin_amdgcn_perm(w[1], w[0], 0x0c0c0400u) |
+                            __builtin_amdgcn_perm(w[3], w[2], 0x04000c0cu);
+        const uint32_t hi = __builtin_amdgcn_perm(w[5], w[4], 0x0c0c0400u) |
+                            __builtin_amdgcn_perm(w[7], w[6], 0x04000c0cu);
+        return (u2v){lo, hi};
+    }
+    static __device__ __forceinline__ void decode8(const u2v c, float *v) {
+        // (the bit-field extract builtin returns its sign-extended field as
+        // an unsigned value: convert it as a signed one)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            v[j] = (float)(int32_t)__builtin_amdgcn_sbfe(c.x, 8 * j, 8);
+            v[4 + j] = (float)(int32_t)__builtin_amdgcn_sbfe(c.y, 8 * j, 8);
+        }
+    }
+};
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
     bf2v r = __builtin_convertvector((f2v){a, b}, bf2v);   // round to nearest even
@@ -405,7 +477,7 @@ constexpr float kOutUnshift = 0x1p-64f;
 
 // ----------------------------------------------------------- compress -----
 
-template <int B, Layout L>
+template <int B, Fmt F, Layout L>
 __global__ __launch_bounds__(kGroup) void compress_kernel(
     const uint16_t *__restrict__ x, int64_t nblocks, float tau,
     uint8_t *__restrict__ codes, float *__restrict__ alpha, float *__restrict__ scale) {
@@ -418,8 +490,9 @@ __global__ __launch_bounds__(kGroup) void compress_kernel(
     const float sg2 = (lane & 2) ? -1.0f : 1.0f;
     const float sg8 = (lane & 8) ? -1.0f : 1.0f;
     const float lane_sign = (__popc(t) & 1) ? -1.0f : 1.0f;
+    using C = Codec<F>;
     // 1 / (sqrt(B) * Q_max), rounded once.
-    constexpr float kScaleFactor = (float)(inv_sqrt(B) / 448.0);
+    constexpr float kScaleFactor = (float)(inv_sqrt(B) / (double)C::kQmax);
     constexpr float kInvB = 1.0f / (float)B;
 
     const int64_t nsteps = (nblocks + G::BPW - 1) / G::BPW;
@@ -494,14 +567,14 @@ __global__ __launch_bounds__(kGroup) void compress_kernel(
             m *= kTinyShift;
         }
         // [TACO] Eq. 10: Z / s = Q * R / max|R|.
-        Quot r = quotient(TACO_QMAX, m);
+        Quot r = quotient(C::kQmax, m);
         r.hi = (m > 0.0f) ? r.hi * lane_sign : 0.0f;
         r.lo = (m > 0.0f) ? r.lo * lane_sign : 0.0f;
 
         if (active) {
             uint8_t *cq = codes + blk * W::kRecord + 8 * t;
 #pragma unroll
-            for (int k = 0; k < G::CH; ++k) st8(cq + k * G::SPAN, encode8(&v[8 * k], r));
+            for (int k = 0; k < G::CH; ++k) st8(cq + k * G::SPAN, encode8<F>(&v[8 * k], r));
             if (t == 0) {
                 alpha[blk * W::kScalarStride] = a * unshift;
                 scale[blk * W::kScalarStride] = s;
@@ -512,9 +585,7 @@ __global__ __launch_bounds__(kGroup) void compress_kernel(
 
 // --------------------------------------------------------- decompress -----
 
-enum class Out { kBf16, kAccumulate };
-
-template <int B, Out MODE, Layout L>
+template <int B, Fmt F, Out MODE, Layout L>
 __global__ __launch_bounds__(kGroup) void decompress_kernel(
     const uint8_t *__restrict__ codes, const float *__restrict__ alpha,
     const float *__restrict__ scale, int64_t nblocks, uint16_t *__restrict__ y,
@@ -528,6 +599,7 @@ __global__ __launch_bounds__(kGroup) void decompress_kernel(
     const float sg2 = (lane & 2) ? -1.0f : 1.0f;
     const float sg8 = (lane & 8) ? -1.0f : 1.0f;
     const float lane_sign = (__popc(t) & 1) ? -1.0f : 1.0f;
+    using C = Codec<F>;
     // 1 / sqrt(B), rounded once.
     constexpr float kInvSqrtB = (float)inv_sqrt(B);
 
@@ -552,7 +624,7 @@ __global__ __launch_bounds__(kGroup) void decompress_kernel(
     for (int64_t step = wave0; step < nsteps; step += nwaves) {
         float v[G::EPL];
 #pragma unroll
-        for (int k = 0; k < G::CH; ++k) decode8(buf[k], &v[8 * k]);   // Eq. 11 (before * s)
+        for (int k = 0; k < G::CH; ++k) C::decode8(buf[k], &v[8 * k]);   // Eq. 11 (before * s)
         float a = a_buf, s = s_buf;
         pin_values(v);
         asm volatile("" : "+v"(a), "+v"(s));
@@ -607,13 +679,6 @@ __global__ __launch_bounds__(kGroup) void decompress_kernel(
 
 // ------------------------------------------------------ owner step -------
 
-// Device pointers of the received payloads, passed by value.
-struct Payloads {
-    const uint8_t *codes[TACO_MAX_PAYLOADS];
-    const float *alpha[TACO_MAX_PAYLOADS];
-    const float *scale[TACO_MAX_PAYLOADS];
-};
-
 // Owner step of the two-shot all-reduce ([TACO] section 4.4.2): compress
 // X = own + sum_p G'_p without materialising X.  With H H = B I,
 // H G'_p = sqrt(B) (s_p / alpha_p) decode(q_p), so
@@ -621,7 +686,7 @@ struct Payloads {
 // one transform (of own) plus one multiply-add per payload element, all in
 // the rotated domain.  The block energy follows from Parseval,
 // sum X^2 = sum (H X)^2 / B, and Eq. 6-10 proceed as in compress_kernel.
-template <int B, int P, Layout L>
+template <int B, Fmt F, int P, Layout L>
 __global__ __launch_bounds__(kGroup) void reduce_compress_kernel(
     const uint16_t *__restrict__ own, Payloads pay, int64_t nblocks, float tau,
     uint8_t *__restrict__ codes, float *__restrict__ alpha, float *__restrict__ scale) {
@@ -634,7 +699,8 @@ __global__ __launch_bounds__(kGroup) void reduce_compress_kernel(
     const float sg2 = (lane & 2) ? -1.0f : 1.0f;
     const float sg8 = (lane & 8) ? -1.0f : 1.0f;
     const float lane_sign = (__popc(t) & 1) ? -1.0f : 1.0f;
-    constexpr float kScaleFactor = (float)(inv_sqrt(B) / 448.0);
+    using C = Codec<F>;
+    constexpr float kScaleFactor = (float)(inv_sqrt(B) / (double)C::kQmax);
     // sqrt(B) = kSqrtBHi + kSqrtBLo to about 2^-48.
     constexpr float kSqrtBHi = (float)(1.0 / inv_sqrt(B));
     constexpr float kSqrtBLo = (float)(1.0 / inv_sqrt(B) - (double)kSqrtBHi);
@@ -697,7 +763,7 @@ __global__ __launch_bounds__(kGroup) void reduce_compress_kernel(
             const float chs = ch * lane_sign, cls = cl * lane_sign;
             float d[G::EPL];
 #pragma unroll
-            for (int k = 0; k < G::CH; ++k) decode8(qc[p][k], &d[8 * k]);
+            for (int k = 0; k < G::CH; ++k) C::decode8(qc[p][k], &d[8 * k]);
 #pragma unroll
             for (int i = 0; i < G::EPL; ++i) v[i] = fmaf(d[i], cls, fmaf(d[i], chs, v[i]));
         }
@@ -737,7 +803,7 @@ __global__ __launch_bounds__(kGroup) void reduce_compress_kernel(
         }
         // As in compress_kernel, v holds lane_sign * (H X), so r carries the
         // lane sign too.
-        Quot r = quotient(TACO_QMAX, m);
+        Quot r = quotient(C::kQmax, m);
         r.hi = (m > 0.0f) ? r.hi * lane_sign : 0.0f;
         r.lo = (m > 0.0f) ? r.lo * lane_sign : 0.0f;
 
@@ -745,7 +811,7 @@ __global__ __launch_bounds__(kGroup) void reduce_compress_kernel(
         if (blk < nblocks) {
             uint8_t *cq = codes + blk * W::kRecord + 8 * t;
 #pragma unroll
-            for (int k = 0; k < G::CH; ++k) st8(cq + k * G::SPAN, encode8(&v[8 * k], r));
+            for (int k = 0; k < G::CH; ++k) st8(cq + k * G::SPAN, encode8<F>(&v[8 * k], r));
             if (t == 0) {
                 alpha[blk * W::kScalarStride] = a * unshift;
                 scale[blk * W::kScalarStride] = s;
@@ -756,60 +822,44 @@ __global__ __launch_bounds__(kGroup) void reduce_compress_kernel(
 
 // ------------------------------------------------------------- codec ------
 
-__global__ __launch_bounds__(kGroup) void e4m3_encode_kernel(const float *__restrict__ x, int64_t n,
-                                                             uint8_t *__restrict__ codes) {
+// Element-wise conversions through the same pack8 / decode8 the operator
+// uses (the operator's own scaling, and with it the mapping of -0 to +0,
+// is not part of the conversion).
+template <Fmt F>
+__global__ __launch_bounds__(kGroup) void encode_kernel(const float *__restrict__ x, int64_t n,
+                                                        uint8_t *__restrict__ codes) {
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i * 4 < n; i += stride) {
-        const int64_t e = i * 4;
-        float q[4];
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i * 8 < n; i += stride) {
+        const int64_t e = i * 8;
+        float q[8];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) q[j] = (e + j < n) ? x[e + j] : 0.0f;
-        int w = __builtin_amdgcn_cvt_pk_fp8_f32(q[0], q[1], 0, false);
-        w = __builtin_amdgcn_cvt_pk_fp8_f32(q[2], q[3], w, true);
+        for (int j = 0; j < 8; ++j) q[j] = (e + j < n) ? x[e + j] : 0.0f;
+        const u2v w = Codec<F>::pack8(q);
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-            if (e + j < n) codes[e + j] = (uint8_t)((uint32_t)w >> (8 * j));
+        for (int j = 0; j < 8; ++j)
+            if (e + j < n) codes[e + j] = (uint8_t)(w[j / 4] >> (8 * (j % 4)));
     }
 }
 
-__global__ __launch_bounds__(kGroup) void e4m3_decode_kernel(const uint8_t *__restrict__ codes,
-                                                             int64_t n, float *__restrict__ out) {
+template <Fmt F>
+__global__ __launch_bounds__(kGroup) void decode_kernel(const uint8_t *__restrict__ codes,
+                                                        int64_t n, float *__restrict__ out) {
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i * 4 < n; i += stride) {
-        const int64_t e = i * 4;
-        uint32_t w = 0;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i * 8 < n; i += stride) {
+        const int64_t e = i * 8;
+        u2v w = {0u, 0u};
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-            if (e + j < n) w |= (uint32_t)codes[e + j] << (8 * j);
-        f2v a = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
-        f2v b = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
-        const float r[4] = {a.x, a.y, b.x, b.y};
+        for (int j = 0; j < 8; ++j)
+            if (e + j < n) w[j / 4] |= (uint32_t)codes[e + j] << (8 * (j % 4));
+        float r[8];
+        Codec<F>::decode8(w, r);
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < 8; ++j)
             if (e + j < n) out[e + j] = r[j];
     }
 }
 
 // -------------------------------------------------------------- host ------
-
-bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
-
-bool overlap(const void *a, size_t na, const void *b, size_t nb) {
-    if (na == 0 || nb == 0) return false;
-    const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
-    return a0 < b0 + nb && b0 < a0 + na;
-}
-
-bool valid_block(int32_t block) {
-    return block == 32 || block == 64 || block == 128 || block == 256 || block == 512;
-}
-
-// N = tokens * hidden, or -1 on a bad shape (negative, zero hidden, overflow).
-int64_t numel(int64_t tokens, int64_t hidden) {
-    if (tokens < 0 || hidden <= 0) return -1;
-    if (tokens > 0 && hidden > (INT64_C(1) << 60) / tokens) return -1;
-    return tokens * hidden;
-}
 
 // Grid: each wave takes TACO_STEPS_PER_WAVE wave-steps (grid-stride), so
 // large tensors launch many work-groups, which keeps every compute unit
@@ -844,32 +894,32 @@ taco_status for_block(int32_t block, F &&f) {
 template <int B>
 int64_t steps_of(int64_t nblocks) { return (nblocks + Geo<B>::BPW - 1) / Geo<B>::BPW; }
 
-template <Layout L>
+template <Fmt F, Layout L>
 struct CompressLaunch {
     const uint16_t *x; int64_t m; float tau; uint8_t *codes; float *alpha; float *scale;
     hipStream_t stream;
     template <int B> taco_status run() const {
-        return launch(reinterpret_cast<const void *>(&compress_kernel<B, L>), grid_for(steps_of<B>(m)),
-                      stream, x, m, tau, codes, alpha, scale);
+        return launch(reinterpret_cast<const void *>(&compress_kernel<B, F, L>),
+                      grid_for(steps_of<B>(m)), stream, x, m, tau, codes, alpha, scale);
     }
 };
 
-template <Out MODE, Layout L>
+template <Fmt F, Out MODE, Layout L>
 struct DecompressLaunch {
     const uint8_t *codes; const float *alpha; const float *scale; int64_t m; uint16_t *y;
     float *acc; hipStream_t stream;
     template <int B> taco_status run() const {
-        return launch(reinterpret_cast<const void *>(&decompress_kernel<B, MODE, L>),
+        return launch(reinterpret_cast<const void *>(&decompress_kernel<B, F, MODE, L>),
                       grid_for(steps_of<B>(m)), stream, codes, alpha, scale, m, y, acc);
     }
 };
 
-template <Layout L>
+template <Fmt F, Layout L>
 struct ReduceLaunch {
     int npay; const uint16_t *own; Payloads pay; int64_t m; float tau; uint8_t *codes;
     float *alpha; float *scale; hipStream_t stream;
     template <int B, int P> taco_status go() const {
-        return launch(reinterpret_cast<const void *>(&reduce_compress_kernel<B, P, L>),
+        return launch(reinterpret_cast<const void *>(&reduce_compress_kernel<B, F, P, L>),
                       grid_for(steps_of<B>(m)), stream, own, pay, m, tau, codes, alpha, scale);
     }
     template <int B> taco_status run() const {
@@ -887,277 +937,67 @@ struct ReduceLaunch {
     }
 };
 
-// Shape, block and element count checks shared by every entry point.
-taco_status check_shape(int64_t tokens, int64_t hidden, int32_t block, int64_t *n_out) {
-    const int64_t n = numel(tokens, hidden);
-    if (n < 0) return TACO_ERR_SHAPE;
-    if (!valid_block(block)) return TACO_ERR_BLOCK;
-    if (n % block) return TACO_ERR_SHAPE;
-    *n_out = n;
-    return TACO_OK;
-}
-
-bool valid_tau(float tau) { return tau > 0.0f && tau <= TACO_MAX_TARGET_ENERGY; }
-
-// Shared validation of the decompress-side calls (side-buffer layout).
-taco_status check_receiver(const uint8_t *codes, const float *alpha, const float *scale,
-                           int64_t tokens, int64_t hidden, int32_t block, const void *out,
-                           size_t out_elem, int64_t *nblocks_out) {
-    int64_t n = 0;
-    const taco_status st = check_shape(tokens, hidden, block, &n);
-    if (st != TACO_OK) return st;
-    *nblocks_out = n / block;
-    if (n == 0) return TACO_OK;
-    if (!codes || !alpha || !scale || !out) return TACO_ERR_NULL;
-    if (!aligned(codes, 16) || !aligned(out, 16) || !aligned(alpha, 4) || !aligned(scale, 4))
-        return TACO_ERR_ALIGN;
-    const size_t nb = (size_t)(n / block) * sizeof(float);
-    const size_t no = (size_t)n * out_elem;
-    if (overlap(out, no, codes, (size_t)n) || overlap(out, no, alpha, nb) || overlap(out, no, scale, nb))
-        return TACO_ERR_ALIAS;
-    return TACO_OK;
-}
-
-// Shared validation of the decompress-side calls (interleaved layout).
-taco_status check_receiver_packed(const uint8_t *payload, int64_t tokens, int64_t hidden,
-                                  int32_t block, const void *out, size_t out_elem,
-                                  int64_t *nblocks_out) {
-    int64_t n = 0;
-    const taco_status st = check_shape(tokens, hidden, block, &n);
-    if (st != TACO_OK) return st;
-    *nblocks_out = n / block;
-    if (n == 0) return TACO_OK;
-    if (!payload || !out) return TACO_ERR_NULL;
-    if (!aligned(payload, 16) || !aligned(out, 16)) return TACO_ERR_ALIGN;
-    if (overlap(out, (size_t)n * out_elem, payload, (size_t)(n / block) * (size_t)(block + 8)))
-        return TACO_ERR_ALIAS;
-    return TACO_OK;
-}
-
-// Validation of the owner step's payloads; fills pay.  `bytes` is the size
-// of one payload (codes + scalars as laid out), `packed` selects how the
-// scalar pointers are derived.
-taco_status check_payloads(int npay, const uint8_t *const *codes, const float *const *alpha,
-                           const float *const *scale, int64_t n, int32_t block, bool packed,
-                           const void *const *outs, const size_t *out_len, int nouts,
-                           Payloads *pay) {
-    const size_t nc = (size_t)n, nb = (size_t)(n / block) * sizeof(float);
-    for (int p = 0; p < npay; ++p) {
-        const uint8_t *c = codes[p];
-        const float *a = packed ? (c ? reinterpret_cast<const float *>(c + block) : nullptr) : alpha[p];
-        const float *sc = packed ? (c ? reinterpret_cast<const float *>(c + block + 4) : nullptr) : scale[p];
-        if (!c || !a || !sc) return TACO_ERR_NULL;
-        if (!aligned(c, 16) || !aligned(a, 4) || !aligned(sc, 4)) return TACO_ERR_ALIGN;
-        const void *ins[3] = {c, a, sc};
-        const size_t lens[3] = {packed ? (size_t)(n / block) * (size_t)(block + 8) : nc,
-                                packed ? 0 : nb, packed ? 0 : nb};
-        for (int i = 0; i < 3; ++i)
-            for (int o = 0; o < nouts; ++o)
-                if (overlap(outs[o], out_len[o], ins[i], lens[i])) return TACO_ERR_ALIAS;
-        pay->codes[p] = c;
-        pay->alpha[p] = a;
-        pay->scale[p] = sc;
-    }
-    return TACO_OK;
+unsigned codec_grid(int64_t n) {
+    const int64_t items = (n + 7) / 8;
+    const int64_t need = (items + kGroup - 1) / kGroup;
+    return (unsigned)(need < 65536 ? need : 65536);
 }
 
 }  // namespace
 
-// ---------------------------------------------------------------- C ABI ---
+// ------------------------------------------------- per-format entry -------
 
-extern "C" {
-
-int64_t taco_num_blocks(int64_t tokens, int64_t hidden, int32_t block) {
-    int64_t n = 0;
-    if (check_shape(tokens, hidden, block, &n) != TACO_OK) return -1;
-    return n / block;
+template <Fmt F>
+taco_status Ops<F>::compress(Layout layout, int32_t block, const uint16_t *x, int64_t nblocks,
+                             float tau, uint8_t *codes, float *alpha, float *scale,
+                             hipStream_t stream) {
+    if (layout == Layout::kPacked)
+        return for_block(block, CompressLaunch<F, Layout::kPacked>{x, nblocks, tau, codes, alpha,
+                                                                    scale, stream});
+    return for_block(block, CompressLaunch<F, Layout::kSide>{x, nblocks, tau, codes, alpha, scale,
+                                                              stream});
 }
 
-int64_t taco_packed_bytes(int64_t tokens, int64_t hidden, int32_t block) {
-    int64_t n = 0;
-    if (check_shape(tokens, hidden, block, &n) != TACO_OK) return -1;
-    return (n / block) * (block + 8);
-}
-
-taco_status taco_compress(const uint16_t *x_bf16, int64_t tokens, int64_t hidden, int32_t block,
-                          float target_energy, uint8_t *codes_e4m3, float *alpha, float *scale,
-                          hipStream_t stream) {
-    int64_t n = 0;
-    const taco_status st = check_shape(tokens, hidden, block, &n);
-    if (st != TACO_OK) return st;
-    if (!valid_tau(target_energy)) return TACO_ERR_PARAM;
-    if (n == 0) return TACO_OK;
-    if (!x_bf16 || !codes_e4m3 || !alpha || !scale) return TACO_ERR_NULL;
-    if (!aligned(x_bf16, 16) || !aligned(codes_e4m3, 16) || !aligned(alpha, 4) || !aligned(scale, 4))
-        return TACO_ERR_ALIGN;
-    const int64_t m = n / block;
-    const size_t nx = (size_t)n * 2, nc = (size_t)n, nb = (size_t)m * sizeof(float);
-    if (overlap(codes_e4m3, nc, x_bf16, nx) || overlap(alpha, nb, x_bf16, nx) ||
-        overlap(scale, nb, x_bf16, nx) || overlap(codes_e4m3, nc, alpha, nb) ||
-        overlap(codes_e4m3, nc, scale, nb) || overlap(alpha, nb, scale, nb))
-        return TACO_ERR_ALIAS;
-    return for_block(block, CompressLaunch<Layout::kSide>{x_bf16, m, target_energy, codes_e4m3,
-                                                           alpha, scale, stream});
-}
-
-taco_status taco_compress_packed(const uint16_t *x_bf16, int64_t tokens, int64_t hidden,
-                                 int32_t block, float target_energy, uint8_t *payload,
-                                 hipStream_t stream) {
-    int64_t n = 0;
-    const taco_status st = check_shape(tokens, hidden, block, &n);
-    if (st != TACO_OK) return st;
-    if (!valid_tau(target_energy)) return TACO_ERR_PARAM;
-    if (n == 0) return TACO_OK;
-    if (!x_bf16 || !payload) return TACO_ERR_NULL;
-    if (!aligned(x_bf16, 16) || !aligned(payload, 16)) return TACO_ERR_ALIGN;
-    const int64_t m = n / block;
-    if (overlap(payload, (size_t)m * (size_t)(block + 8), x_bf16, (size_t)n * 2)) return TACO_ERR_ALIAS;
-    return for_block(block, CompressLaunch<Layout::kPacked>{
-        x_bf16, m, target_energy, payload, reinterpret_cast<float *>(payload + block),
-        reinterpret_cast<float *>(payload + block + 4), stream});
-}
-
-taco_status taco_decompress(const uint8_t *codes_e4m3, const float *alpha, const float *scale,
-                            int64_t tokens, int64_t hidden, int32_t block, uint16_t *y_bf16,
-                            hipStream_t stream) {
-    int64_t m = 0;
-    const taco_status st = check_receiver(codes_e4m3, alpha, scale, tokens, hidden, block, y_bf16, 2, &m);
-    if (st != TACO_OK || m == 0) return st;
-    return for_block(block, DecompressLaunch<Out::kBf16, Layout::kSide>{
-        codes_e4m3, alpha, scale, m, y_bf16, nullptr, stream});
-}
-
-taco_status taco_decompress_packed(const uint8_t *payload, int64_t tokens, int64_t hidden,
-                                   int32_t block, uint16_t *y_bf16, hipStream_t stream) {
-    int64_t m = 0;
-    const taco_status st = check_receiver_packed(payload, tokens, hidden, block, y_bf16, 2, &m);
-    if (st != TACO_OK || m == 0) return st;
-    return for_block(block, DecompressLaunch<Out::kBf16, Layout::kPacked>{
-        payload, reinterpret_cast<const float *>(payload + block),
-        reinterpret_cast<const float *>(payload + block + 4), m, y_bf16, nullptr, stream});
-}
-
-taco_status taco_decompress_accumulate(const uint8_t *codes_e4m3, const float *alpha,
-                                       const float *scale, int64_t tokens, int64_t hidden,
-                                       int32_t block, float *acc_f32, hipStream_t stream) {
-    int64_t m = 0;
-    const taco_status st = check_receiver(codes_e4m3, alpha, scale, tokens, hidden, block, acc_f32, 4, &m);
-    if (st != TACO_OK || m == 0) return st;
-    return for_block(block, DecompressLaunch<Out::kAccumulate, Layout::kSide>{
-        codes_e4m3, alpha, scale, m, nullptr, acc_f32, stream});
-}
-
-taco_status taco_decompress_accumulate_packed(const uint8_t *payload, int64_t tokens,
-                                              int64_t hidden, int32_t block, float *acc_f32,
-                                              hipStream_t stream) {
-    int64_t m = 0;
-    const taco_status st = check_receiver_packed(payload, tokens, hidden, block, acc_f32, 4, &m);
-    if (st != TACO_OK || m == 0) return st;
-    return for_block(block, DecompressLaunch<Out::kAccumulate, Layout::kPacked>{
-        payload, reinterpret_cast<const float *>(payload + block),
-        reinterpret_cast<const float *>(payload + block + 4), m, nullptr, acc_f32, stream});
-}
-
-taco_status taco_reduce_compress(const uint16_t *own_bf16, int32_t npayloads,
-                                 const uint8_t *const *codes_e4m3, const float *const *alpha,
-                                 const float *const *scale, int64_t tokens, int64_t hidden,
-                                 int32_t block, float target_energy, uint8_t *out_codes,
-                                 float *out_alpha, float *out_scale, hipStream_t stream) {
-    int64_t n = 0;
-    taco_status st = check_shape(tokens, hidden, block, &n);
-    if (st != TACO_OK) return st;
-    if (!valid_tau(target_energy)) return TACO_ERR_PARAM;
-    if (npayloads < 0 || npayloads > TACO_MAX_PAYLOADS) return TACO_ERR_PARAM;
-    if (npayloads == 0 && !own_bf16) return TACO_ERR_PARAM;
-    if (n == 0) return TACO_OK;
-    if (!out_codes || !out_alpha || !out_scale) return TACO_ERR_NULL;
-    if (npayloads > 0 && (!codes_e4m3 || !alpha || !scale)) return TACO_ERR_NULL;
-    const int64_t m = n / block;
-    const size_t nc = (size_t)n, nb = (size_t)m * sizeof(float);
-    if (!aligned(out_codes, 16) || !aligned(out_alpha, 4) || !aligned(out_scale, 4)) return TACO_ERR_ALIGN;
-    if (overlap(out_codes, nc, out_alpha, nb) || overlap(out_codes, nc, out_scale, nb) ||
-        overlap(out_alpha, nb, out_scale, nb))
-        return TACO_ERR_ALIAS;
-    const void *outs[3] = {out_codes, out_alpha, out_scale};
-    const size_t out_len[3] = {nc, nb, nb};
-    if (own_bf16) {
-        if (!aligned(own_bf16, 16)) return TACO_ERR_ALIGN;
-        for (int o = 0; o < 3; ++o)
-            if (overlap(outs[o], out_len[o], own_bf16, (size_t)n * 2)) return TACO_ERR_ALIAS;
+template <Fmt F>
+taco_status Ops<F>::decompress(Layout layout, Out mode, int32_t block, const uint8_t *codes,
+                               const float *alpha, const float *scale, int64_t nblocks,
+                               uint16_t *y, float *acc, hipStream_t stream) {
+    if (layout == Layout::kPacked) {
+        if (mode == Out::kAccumulate)
+            return for_block(block, DecompressLaunch<F, Out::kAccumulate, Layout::kPacked>{
+                                        codes, alpha, scale, nblocks, y, acc, stream});
+        return for_block(block, DecompressLaunch<F, Out::kBf16, Layout::kPacked>{
+                                    codes, alpha, scale, nblocks, y, acc, stream});
     }
-    Payloads pay = {};
-    st = check_payloads(npayloads, codes_e4m3, alpha, scale, n, block, false, outs, out_len, 3, &pay);
-    if (st != TACO_OK) return st;
-    return for_block(block, ReduceLaunch<Layout::kSide>{npayloads, own_bf16, pay, m, target_energy,
-                                                         out_codes, out_alpha, out_scale, stream});
+    if (mode == Out::kAccumulate)
+        return for_block(block, DecompressLaunch<F, Out::kAccumulate, Layout::kSide>{
+                                    codes, alpha, scale, nblocks, y, acc, stream});
+    return for_block(block, DecompressLaunch<F, Out::kBf16, Layout::kSide>{
+                                codes, alpha, scale, nblocks, y, acc, stream});
 }
 
-taco_status taco_reduce_compress_packed(const uint16_t *own_bf16, int32_t npayloads,
-                                        const uint8_t *const *payloads, int64_t tokens,
-                                        int64_t hidden, int32_t block, float target_energy,
-                                        uint8_t *out_payload, hipStream_t stream) {
-    int64_t n = 0;
-    taco_status st = check_shape(tokens, hidden, block, &n);
-    if (st != TACO_OK) return st;
-    if (!valid_tau(target_energy)) return TACO_ERR_PARAM;
-    if (npayloads < 0 || npayloads > TACO_MAX_PAYLOADS) return TACO_ERR_PARAM;
-    if (npayloads == 0 && !own_bf16) return TACO_ERR_PARAM;
-    if (n == 0) return TACO_OK;
-    if (!out_payload) return TACO_ERR_NULL;
-    if (npayloads > 0 && !payloads) return TACO_ERR_NULL;
-    const int64_t m = n / block;
-    if (!aligned(out_payload, 16)) return TACO_ERR_ALIGN;
-    const void *outs[1] = {out_payload};
-    const size_t out_len[1] = {(size_t)m * (size_t)(block + 8)};
-    if (own_bf16) {
-        if (!aligned(own_bf16, 16)) return TACO_ERR_ALIGN;
-        if (overlap(out_payload, out_len[0], own_bf16, (size_t)n * 2)) return TACO_ERR_ALIAS;
-    }
-    Payloads pay = {};
-    st = check_payloads(npayloads, payloads, nullptr, nullptr, n, block, true, outs, out_len, 1, &pay);
-    if (st != TACO_OK) return st;
-    return for_block(block, ReduceLaunch<Layout::kPacked>{
-        npayloads, own_bf16, pay, m, target_energy, out_payload,
-        reinterpret_cast<float *>(out_payload + block), reinterpret_cast<float *>(out_payload + block + 4),
-        stream});
+template <Fmt F>
+taco_status Ops<F>::reduce_compress(Layout layout, int32_t block, int npay, const uint16_t *own,
+                                    const Payloads &pay, int64_t nblocks, float tau,
+                                    uint8_t *codes, float *alpha, float *scale,
+                                    hipStream_t stream) {
+    if (layout == Layout::kPacked)
+        return for_block(block, ReduceLaunch<F, Layout::kPacked>{npay, own, pay, nblocks, tau,
+                                                                  codes, alpha, scale, stream});
+    return for_block(block, ReduceLaunch<F, Layout::kSide>{npay, own, pay, nblocks, tau, codes,
+                                                            alpha, scale, stream});
 }
 
-taco_status taco_e4m3_encode(const float *x, int64_t n, uint8_t *codes, hipStream_t stream) {
-    if (n < 0) return TACO_ERR_SHAPE;
-    if (n == 0) return TACO_OK;
-    if (!x || !codes) return TACO_ERR_NULL;
-    if (!aligned(x, 16) || !aligned(codes, 16)) return TACO_ERR_ALIGN;
-    if (overlap(codes, (size_t)n, x, (size_t)n * 4)) return TACO_ERR_ALIAS;
-    const int64_t items = (n + 3) / 4;
-    const int64_t need = (items + kGroup - 1) / kGroup;
-    const unsigned grid = (unsigned)(need < 65536 ? need : 65536);
-    return launch(reinterpret_cast<const void *>(&e4m3_encode_kernel), grid, stream, x, n, codes);
+template <Fmt F>
+taco_status Ops<F>::encode(const float *x, int64_t n, uint8_t *codes, hipStream_t stream) {
+    return launch(reinterpret_cast<const void *>(&encode_kernel<F>), codec_grid(n), stream, x, n,
+                  codes);
 }
 
-taco_status taco_e4m3_decode(const uint8_t *codes, int64_t n, float *out, hipStream_t stream) {
-    if (n < 0) return TACO_ERR_SHAPE;
-    if (n == 0) return TACO_OK;
-    if (!codes || !out) return TACO_ERR_NULL;
-    if (!aligned(out, 16) || !aligned(codes, 16)) return TACO_ERR_ALIGN;
-    if (overlap(out, (size_t)n * 4, codes, (size_t)n)) return TACO_ERR_ALIAS;
-    const int64_t items = (n + 3) / 4;
-    const int64_t need = (items + kGroup - 1) / kGroup;
-    const unsigned grid = (unsigned)(need < 65536 ? need : 65536);
-    return launch(reinterpret_cast<const void *>(&e4m3_decode_kernel), grid, stream, codes, n, out);
+template <Fmt F>
+taco_status Ops<F>::decode(const uint8_t *codes, int64_t n, float *out, hipStream_t stream) {
+    return launch(reinterpret_cast<const void *>(&decode_kernel<F>), codec_grid(n), stream, codes,
+                  n, out);
 }
 
-const char *taco_status_string(taco_status status) {
-    switch (status) {
-        case TACO_OK: return "ok";
-        case TACO_ERR_NULL: return "a required pointer is NULL";
-        case TACO_ERR_SHAPE: return "bad shape: tokens < 0, hidden <= 0, or N not a multiple of the block";
-        case TACO_ERR_BLOCK: return "block size must be 32, 64, 128, 256 or 512";
-        case TACO_ERR_PARAM: return "target energy must be finite and in (0, 1e20], and the payload count in 0..8 (0 only with own data)";
-        case TACO_ERR_ALIGN: return "tensors must be 16-byte aligned, alpha and scale 4-byte aligned";
-        case TACO_ERR_ALIAS: return "an output buffer overlaps an input or another output";
-        case TACO_ERR_HIP: return "the HIP runtime refused the kernel launch";
-    }
-    return "unknown status";
-}
-
-}  // extern "C"
+}  // namespace taco_internal

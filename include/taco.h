@@ -69,6 +69,27 @@ extern "C" {
  * parallelism up to 9 ranks). */
 #define TACO_MAX_PAYLOADS 8
 
+/* Code formats of Eq. 10-11.  E4M3 is the operator's; the other two keep
+ * Eq. 5-13 and change only the code and Q_max ([TACO] section 5.3.2 compares
+ * the three formats; section 6 describes the INT8 variant for hardware
+ * without FP8):
+ *   TACO_FORMAT_E4M3  OCP E4M3FN, Q_max = 448 (TACO_QMAX).
+ *   TACO_FORMAT_E5M2  OCP E5M2 (bias 15, with infinities), Q_max = 57344.
+ *   TACO_FORMAT_INT8  the uniform quantiser of [TACO] section 2.3 / Eq. 1 with
+ *                     the dual scale s as its step: q = round(Z / s), to
+ *                     nearest with ties to even, in [-127, 127], stored as a
+ *                     two's complement byte; Q_max = 127.
+ * Every format rounds the float32 value Z / s (as E4M3 does), and exact
+ * zeros encode as 0x00. */
+typedef enum {
+    TACO_FORMAT_E4M3 = 0,
+    TACO_FORMAT_E5M2 = 1,
+    TACO_FORMAT_INT8 = 2
+} taco_format;
+
+#define TACO_E5M2_MAX 57344.0f
+#define TACO_INT8_MAX 127.0f
+
 typedef enum {
     TACO_OK = 0,
     TACO_ERR_NULL = 1,   /* a required pointer is NULL                          */
@@ -79,7 +100,8 @@ typedef enum {
     TACO_ERR_ALIGN = 5,  /* a tensor is not 16-byte aligned, or alpha / scale
                             not 4-byte aligned                                  */
     TACO_ERR_ALIAS = 6,  /* an output buffer overlaps an input or another output */
-    TACO_ERR_HIP = 7     /* the HIP runtime refused the launch                  */
+    TACO_ERR_HIP = 7,    /* the HIP runtime refused the launch                  */
+    TACO_ERR_FORMAT = 8  /* format is not one of the taco_format values         */
 } taco_status;
 
 /* Number of blocks M = tokens * hidden / block, or -1 if the shape or block
@@ -188,6 +210,45 @@ taco_status taco_reduce_compress_packed(const uint16_t *own_bf16, int32_t npaylo
                                         uint8_t *out_payload, hipStream_t stream);
 
 /*
+ * The calls above with a code format (taco_format): the same operations,
+ * validation and layouts, with codes of that format and its Q_max.  The
+ * format is checked first (TACO_ERR_FORMAT, also for N == 0).  Payloads of
+ * one format must be decoded, accumulated and reduced with the same format.
+ * The calls without a format are these with TACO_FORMAT_E4M3.
+ */
+taco_status taco_compress_fmt(const uint16_t *x_bf16, int64_t tokens, int64_t hidden,
+                              int32_t block, float target_energy, taco_format format,
+                              uint8_t *codes, float *alpha, float *scale, hipStream_t stream);
+taco_status taco_decompress_fmt(const uint8_t *codes, const float *alpha, const float *scale,
+                                int64_t tokens, int64_t hidden, int32_t block, taco_format format,
+                                uint16_t *y_bf16, hipStream_t stream);
+taco_status taco_decompress_accumulate_fmt(const uint8_t *codes, const float *alpha,
+                                           const float *scale, int64_t tokens, int64_t hidden,
+                                           int32_t block, taco_format format, float *acc_f32,
+                                           hipStream_t stream);
+taco_status taco_reduce_compress_fmt(const uint16_t *own_bf16, int32_t npayloads,
+                                     const uint8_t *const *codes, const float *const *alpha,
+                                     const float *const *scale, int64_t tokens, int64_t hidden,
+                                     int32_t block, float target_energy, taco_format format,
+                                     uint8_t *out_codes, float *out_alpha, float *out_scale,
+                                     hipStream_t stream);
+taco_status taco_compress_packed_fmt(const uint16_t *x_bf16, int64_t tokens, int64_t hidden,
+                                     int32_t block, float target_energy, taco_format format,
+                                     uint8_t *payload, hipStream_t stream);
+taco_status taco_decompress_packed_fmt(const uint8_t *payload, int64_t tokens, int64_t hidden,
+                                       int32_t block, taco_format format, uint16_t *y_bf16,
+                                       hipStream_t stream);
+taco_status taco_decompress_accumulate_packed_fmt(const uint8_t *payload, int64_t tokens,
+                                                  int64_t hidden, int32_t block,
+                                                  taco_format format, float *acc_f32,
+                                                  hipStream_t stream);
+taco_status taco_reduce_compress_packed_fmt(const uint16_t *own_bf16, int32_t npayloads,
+                                            const uint8_t *const *payloads, int64_t tokens,
+                                            int64_t hidden, int32_t block, float target_energy,
+                                            taco_format format, uint8_t *out_payload,
+                                            hipStream_t stream);
+
+/*
  * The E4M3 conversions the kernels above use (Cvt_FP8 of [TACO] Eq. 10 and
  * Cvt_FP32 of Eq. 11), exposed element-wise so that they can be checked
  * exhaustively.  encode: round to nearest even, OCP E4M3FN; inputs of
@@ -197,6 +258,14 @@ taco_status taco_reduce_compress_packed(const uint16_t *own_bf16, int32_t npaylo
  */
 taco_status taco_e4m3_encode(const float *x, int64_t n, uint8_t *codes, hipStream_t stream);
 taco_status taco_e4m3_decode(const uint8_t *codes, int64_t n, float *out, hipStream_t stream);
+
+/* The same for any format (taco_e4m3_* are these with TACO_FORMAT_E4M3).
+ * Encode contracts: |x| < 464 (E4M3), |x| < 61440 (E5M2), |x| < 127.5
+ * (INT8); larger inputs give unspecified codes. */
+taco_status taco_encode(taco_format format, const float *x, int64_t n, uint8_t *codes,
+                        hipStream_t stream);
+taco_status taco_decode(taco_format format, const uint8_t *codes, int64_t n, float *out,
+                        hipStream_t stream);
 
 /* Static description of a status code (never NULL). */
 const char *taco_status_string(taco_status status);

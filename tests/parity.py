@@ -1,9 +1,10 @@
 """Comparison of the HIP path against the oracle, with the tolerances of the
 contract:
 
-* E4M3 codes identical, except flips to the adjacent code where the oracle's
+* codes identical, except flips to the adjacent code where the oracle's
   argument Z/s sits at a rounding tie (within the float32 error the kernel's
-  evaluation order can carry), on at most 1e-5 of the elements;
+  evaluation order can carry), on at most 1e-5 of the elements (for every
+  code format: E4M3, E5M2 and INT8);
 * alpha and s within 1e-6 relative;
 * reconstructions within 1e-3 relative RMS of the oracle's reconstruction.
 """
@@ -18,6 +19,7 @@ FLIP_RATE = 1e-5
 SCALAR_RTOL = 1e-6
 RECON_RTOL = 1e-3
 QMAX = 448.0
+QMAX_OF = {"e4m3": 448.0, "e5m2": 57344.0, "int8": 127.0}
 U32 = 2.0 ** -24          # float32 unit roundoff
 
 # Flips and elements over every comparison of the session: the rate bound
@@ -45,36 +47,48 @@ def max_rel(a, b) -> float:
     return float(d.max()) if d.size else 0.0
 
 
-def _tie_ok(x_block, code_gpu, code_or, j, B) -> tuple[bool, str]:
-    """Is element j's flip a flip between adjacent codes at a rounding tie?"""
-    _, _, z = oracle.ash_block(x_block, B)
-    s64 = np.max(np.abs(z)) / QMAX
-    v = float(np.float32(z[j] / s64))
-    cg, co = int(code_gpu), int(code_or)
-    dg, do = oracle.e4m3_decode(np.array([cg, co], np.uint8))
+def _adjacent(cg: int, co: int, fmt: str) -> str:
+    """Empty if codes cg and co are neighbours in the format, else why not."""
+    dg, do = oracle.decode(np.array([cg, co], np.uint8), fmt)
+    if fmt == "int8":
+        return "" if abs(dg - do) <= 1 else f"codes {cg:#x} vs {co:#x} not adjacent"
     if (cg & 0x80) != (co & 0x80) and not (dg == 0 and do == 0):
         # Sign differs: only possible when both round to zero.
-        return False, f"sign flip {cg:#x} vs {co:#x} (v={v})"
+        return f"sign flip {cg:#x} vs {co:#x}"
     if abs((cg & 0x7F) - (co & 0x7F)) > 1:
-        return False, f"codes {cg:#x} vs {co:#x} not adjacent (v={v})"
+        return f"codes {cg:#x} vs {co:#x} not adjacent"
+    return ""
+
+
+def _tie_ok(x_block, code_gpu, code_or, j, B, fmt="e4m3") -> tuple[bool, str]:
+    """Is element j's flip a flip between adjacent codes at a rounding tie?"""
+    qmax = QMAX_OF[fmt]
+    _, _, z = oracle.ash_block(x_block, B)
+    s64 = np.max(np.abs(z)) / qmax
+    v = float(np.float32(z[j] / s64))
+    cg, co = int(code_gpu), int(code_or)
+    why = _adjacent(cg, co, fmt)
+    if why:
+        return False, f"{why} (v={v})"
+    dg, do = oracle.decode(np.array([cg, co], np.uint8), fmt)
     mid = 0.5 * (abs(dg) + abs(do))
     # Bound on the kernel's float32 error in v: the FWHT accumulates at most
     # log2(B) roundings of partial sums bounded by sum|x|, then two roundings
     # in the quotient and the product.
     xs = synth.bits_to_f32(x_block).astype(np.float64)
     m = np.max(np.abs(oracle.fwht(xs)))
-    bound = QMAX * np.log2(B) * U32 * np.sum(np.abs(xs)) / m + 4 * U32 * abs(v) if m > 0 else 0
+    bound = qmax * np.log2(B) * U32 * np.sum(np.abs(xs)) / m + 4 * U32 * abs(v) if m > 0 else 0
     if abs(abs(v) - mid) > bound:
         return False, f"not at a tie: |v|={abs(v)!r}, midpoint={mid!r}, bound={bound:.3g}"
     return True, ""
 
 
-def compare_compress(x_bits, B, codes, alpha, scale, tau=1.0, max_flip_checks=200):
+def compare_compress(x_bits, B, codes, alpha, scale, tau=1.0, max_flip_checks=200, fmt="e4m3"):
     """Check the GPU's (codes, alpha, scale) of x_bits against the oracle.
     Returns a dict of statistics; raises AssertionError on a violation."""
     x_bits = np.ascontiguousarray(x_bits).reshape(-1)
     codes = np.ascontiguousarray(codes).reshape(-1)
-    o_codes, o_alpha, o_scale = oracle.compress(x_bits, B, tau)
+    o_codes, o_alpha, o_scale = oracle.compress(x_bits, B, tau, fmt=fmt)
     o_codes = o_codes.reshape(-1)
     bad = np.nonzero(codes != o_codes)[0]
     n = x_bits.size
@@ -84,7 +98,7 @@ def compare_compress(x_bits, B, codes, alpha, scale, tau=1.0, max_flip_checks=20
         f"{bad.size} code mismatches in {n} elements (allowed {allowed_flips(n):.1f})"
     for i in bad[:max_flip_checks]:
         k, j = divmod(int(i), B)
-        ok, why = _tie_ok(x_bits[k * B:(k + 1) * B], codes[i], o_codes[i], j, B)
+        ok, why = _tie_ok(x_bits[k * B:(k + 1) * B], codes[i], o_codes[i], j, B, fmt)
         assert ok, f"element {i} (block {k}): {why}"
     ea = max_rel(alpha, o_alpha)
     es = max_rel(scale, o_scale)
@@ -94,12 +108,13 @@ def compare_compress(x_bits, B, codes, alpha, scale, tau=1.0, max_flip_checks=20
             "oracle": (o_codes, o_alpha, o_scale)}
 
 
-def compare_decompress(y_bits, o_codes, o_alpha, o_scale, B):
+def compare_decompress(y_bits, o_codes, o_alpha, o_scale, B, fmt="e4m3"):
     """GPU bf16 output y_bits (from the oracle's codes) against the oracle's
     bf16 output (relative RMS) and against its exact reconstruction
     (element-wise, one bf16 rounding plus the kernel's float32 error)."""
-    ref = oracle.reconstruct_f64(o_codes, o_alpha, o_scale, B).reshape(-1)
-    ref_bf16 = synth.bits_to_f32(oracle.decompress(o_codes, o_alpha, o_scale, B)).reshape(-1)
+    ref = oracle.reconstruct_f64(o_codes, o_alpha, o_scale, B, fmt=fmt).reshape(-1)
+    ref_bf16 = synth.bits_to_f32(oracle.decompress(o_codes, o_alpha, o_scale, B,
+                                                   fmt=fmt)).reshape(-1)
     y = synth.bits_to_f32(np.asarray(y_bits).reshape(-1)).astype(np.float64)
     r = rel_rms(y, ref_bf16)
     assert r <= RECON_RTOL, f"decompress rel RMS {r:.3g}"
@@ -113,21 +128,23 @@ def compare_decompress(y_bits, o_codes, o_alpha, o_scale, B):
     return {"rel_rms": r}
 
 
-def compare_reduce(own_bits, payloads, B, codes, alpha, scale, tau=1.0, max_flip_checks=200):
+def compare_reduce(own_bits, payloads, B, codes, alpha, scale, tau=1.0, max_flip_checks=200,
+                   fmt="e4m3"):
     """Check the GPU owner step (codes, alpha, scale of own + sum of payload
     reconstructions) against the oracle.  A flip must sit at an E4M3 tie
     within the float32 error of the kernel's rotated-domain sum:
     |err(H X)_j| <= 2^-23 (log2(B) |own|_1 + (P + 2) sum_p |c_p d_pj|),
     c_p = sqrt(B) s_p / alpha_p."""
     codes = np.ascontiguousarray(codes).reshape(-1)
-    o_codes, o_alpha, o_scale = oracle.reduce_compress(own_bits, payloads, B, tau)
+    qmax = QMAX_OF[fmt]
+    o_codes, o_alpha, o_scale = oracle.reduce_compress(own_bits, payloads, B, tau, fmt=fmt)
     o_codes = o_codes.reshape(-1)
     n = o_codes.size
     x = np.zeros(n)
     if own_bits is not None:
         x += synth.bits_to_f32(np.asarray(own_bits).reshape(-1)).astype(np.float64)
     for c, a, s in payloads:
-        x += oracle.reconstruct_f64(c, a, s, B).reshape(-1)
+        x += oracle.reconstruct_f64(c, a, s, B, fmt=fmt).reshape(-1)
     bad = np.nonzero(codes != o_codes)[0]
     TOTALS["flips"] += int(bad.size)
     TOTALS["n"] += int(n)
@@ -139,11 +156,11 @@ def compare_reduce(own_bits, payloads, B, codes, alpha, scale, tau=1.0, max_flip
         xb = x[k * B:(k + 1) * B]
         r = oracle.fwht(xb)
         m = np.max(np.abs(r))
-        v = float(np.float32(QMAX * r[j] / m))
+        v = float(np.float32(qmax * r[j] / m))
         cg, co = int(codes[i]), int(o_codes[i])
-        dg, do = oracle.e4m3_decode(np.array([cg, co], np.uint8))
-        assert (cg & 0x80) == (co & 0x80) or (dg == 0 and do == 0), (i, cg, co)
-        assert abs((cg & 0x7F) - (co & 0x7F)) <= 1, (i, cg, co)
+        dg, do = oracle.decode(np.array([cg, co], np.uint8), fmt)
+        why = _adjacent(cg, co, fmt)
+        assert not why, (i, why)
         own_l1 = 0.0
         if own_bits is not None:
             ob = synth.bits_to_f32(np.asarray(own_bits).reshape(-1)[k * B:(k + 1) * B])
@@ -151,10 +168,10 @@ def compare_reduce(own_bits, payloads, B, codes, alpha, scale, tau=1.0, max_flip
         pay_term = 0.0
         for c, a, s in payloads:
             cp = np.sqrt(B) * float(np.asarray(s).reshape(-1)[k]) / float(np.asarray(a).reshape(-1)[k])
-            dp = oracle.e4m3_decode(np.asarray(c).reshape(-1)[i:i + 1])[0]
+            dp = oracle.decode(np.asarray(c).reshape(-1)[i:i + 1], fmt)[0]
             pay_term += abs(cp * dp)
         err_r = 2.0 ** -23 * (np.log2(B) * own_l1 + (P + 2) * pay_term)
-        bound = QMAX * err_r / m + 4 * U32 * abs(v)
+        bound = qmax * err_r / m + 4 * U32 * abs(v)
         mid = 0.5 * (abs(dg) + abs(do))
         assert abs(abs(v) - mid) <= bound, f"element {i}: |v|={abs(v)}, mid={mid}, bound={bound:.3g}"
     ea = max_rel(alpha, o_alpha)

@@ -23,7 +23,8 @@ except ImportError:  # pragma: no cover
 HEADER = os.path.join(ROOT, "include", "taco.h")
 LIB = os.path.join(ROOT, "gradients_taco_compress_amd", "libtaco.so")
 
-OK, NULL, SHAPE, BLOCK, PARAM, ALIGN, ALIAS, HIP = range(8)
+OK, NULL, SHAPE, BLOCK, PARAM, ALIGN, ALIAS, HIP, FORMAT = range(9)
+E4M3, E5M2, INT8 = range(3)
 A = 1 << 20          # fake, 16-byte aligned "device" addresses: never dereferenced
 
 
@@ -53,6 +54,16 @@ def lib():
     L.taco_reduce_compress_packed.argtypes = [P, I32, P, I64, I64, I32, F32, P, P]
     L.taco_e4m3_encode.argtypes = [P, I64, P, P]
     L.taco_e4m3_decode.argtypes = [P, I64, P, P]
+    L.taco_compress_fmt.argtypes = [P, I64, I64, I32, F32, I32, P, P, P, P]
+    L.taco_decompress_fmt.argtypes = [P, P, P, I64, I64, I32, I32, P, P]
+    L.taco_decompress_accumulate_fmt.argtypes = [P, P, P, I64, I64, I32, I32, P, P]
+    L.taco_reduce_compress_fmt.argtypes = [P, I32, P, P, P, I64, I64, I32, F32, I32, P, P, P, P]
+    L.taco_compress_packed_fmt.argtypes = [P, I64, I64, I32, F32, I32, P, P]
+    L.taco_decompress_packed_fmt.argtypes = [P, I64, I64, I32, I32, P, P]
+    L.taco_decompress_accumulate_packed_fmt.argtypes = [P, I64, I64, I32, I32, P, P]
+    L.taco_reduce_compress_packed_fmt.argtypes = [P, I32, P, I64, I64, I32, F32, I32, P, P]
+    L.taco_encode.argtypes = [I32, P, I64, P, P]
+    L.taco_decode.argtypes = [I32, P, I64, P, P]
     L.taco_status_string.argtypes = [ctypes.c_int]
     L.taco_status_string.restype = ctypes.c_char_p
     return L
@@ -60,7 +71,7 @@ def lib():
 
 def test_every_declared_function_is_exported(lib):
     names = declared_functions()
-    assert len(names) == 13, names
+    assert len(names) == 23, names
     for n in names:
         assert hasattr(lib, n), n
     out = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True).stdout
@@ -79,8 +90,9 @@ def test_binding_names_match_header():
 
 
 def test_status_strings(lib):
-    for s in range(8):
+    for s in range(9):
         assert lib.taco_status_string(s)
+    assert b"format" in lib.taco_status_string(FORMAT)
     assert lib.taco_status_string(99) == b"unknown status"
 
 
@@ -232,3 +244,54 @@ def test_packed_validation(lib):
     assert rp(out=5 * A + 512) == ALIAS
     assert rp(out=A + 64) == ALIAS
     assert rp(tokens=0, out=None) == OK
+
+
+def test_format_validation(lib):
+    """A bad format is reported first (also for an empty tensor); with a
+    valid format every other check is the same as without one."""
+    arr = ctypes.c_void_p * 8
+    pays = ctypes.cast(arr(5 * A, 6 * A), ctypes.c_void_p)
+    calls = {
+        "compress": lambda f, **k: lib.taco_compress_fmt(
+            k.get("x", A), k.get("tokens", 4), 256, 128, 1.0, f, 2 * A, 3 * A, 4 * A, None),
+        "decompress": lambda f, **k: lib.taco_decompress_fmt(
+            k.get("x", A), 2 * A, 3 * A, k.get("tokens", 4), 256, 128, f, 4 * A, None),
+        "accumulate": lambda f, **k: lib.taco_decompress_accumulate_fmt(
+            k.get("x", A), 2 * A, 3 * A, k.get("tokens", 4), 256, 128, f, 4 * A, None),
+        # (own is optional: the probed pointer is the required output)
+        "reduce": lambda f, **k: lib.taco_reduce_compress_fmt(
+            A, 2, pays, pays, pays, k.get("tokens", 4), 256, 128, 1.0, f,
+            k.get("x", 2 * A), 3 * A, 4 * A, None),
+        "compress_packed": lambda f, **k: lib.taco_compress_packed_fmt(
+            k.get("x", A), k.get("tokens", 4), 256, 128, 1.0, f, 2 * A, None),
+        "decompress_packed": lambda f, **k: lib.taco_decompress_packed_fmt(
+            k.get("x", A), k.get("tokens", 4), 256, 128, f, 2 * A, None),
+        "accumulate_packed": lambda f, **k: lib.taco_decompress_accumulate_packed_fmt(
+            k.get("x", A), k.get("tokens", 4), 256, 128, f, 2 * A, None),
+        "reduce_packed": lambda f, **k: lib.taco_reduce_compress_packed_fmt(
+            A, 2, pays, k.get("tokens", 4), 256, 128, 1.0, f, k.get("x", 2 * A), None),
+        "encode": lambda f, **k: lib.taco_encode(f, k.get("x", A), 16 if k.get("tokens", 4)
+                                                 else 0, 2 * A, None),
+        "decode": lambda f, **k: lib.taco_decode(f, k.get("x", A), 16 if k.get("tokens", 4)
+                                                 else 0, 2 * A, None),
+    }
+    for name, call in calls.items():
+        for bad in (-1, 3, 255):
+            assert call(bad) == FORMAT, name
+            assert call(bad, tokens=0) == FORMAT, name
+        for f in (E4M3, E5M2, INT8):
+            assert call(f, x=None) == NULL, (name, f)
+            assert call(f, x=9 * A + 2) == ALIGN, (name, f)
+            assert call(f, tokens=0, x=None) == OK, (name, f)
+            if name not in ("encode", "decode"):
+                assert call(f, tokens=-1) == SHAPE, (name, f)
+
+
+def test_format_calls_match_e4m3_calls_on_errors(lib):
+    """The calls without a format behave as the E4M3 calls with one."""
+    # (only argument sets that fail validation: the pointers are fake)
+    for hidden, block, tau, want in ((96, 128, 1.0, SHAPE), (256, 100, 1.0, BLOCK),
+                                     (256, 128, -1.0, PARAM)):
+        a = lib.taco_compress(A, 3, hidden, block, tau, 2 * A, 3 * A, 4 * A, None)
+        b = lib.taco_compress_fmt(A, 3, hidden, block, tau, E4M3, 2 * A, 3 * A, 4 * A, None)
+        assert a == b == want
