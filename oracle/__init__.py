@@ -69,6 +69,8 @@ def _load():
         lib.taco_oracle_compress_f64.argtypes = [P, i64, i32, f64, f64, i32, P, P, P]
         lib.taco_oracle_reduce_compress.argtypes = [P, i32, P, P, P, i64, i32, f64, f64, i32,
                                                     P, P, P]
+        lib.taco_oracle_roundtrip_variant.argtypes = [P, i64, i32, i32, i32, f64, f64, P]
+        lib.taco_oracle_fidelity.argtypes = [P, P, i64, P]
         lib.taco_oracle_qmax.argtypes = [i32]
         lib.taco_oracle_qmax.restype = f64
         lib.taco_oracle_encode_array.argtypes = [i32, P, i64, P]
@@ -300,6 +302,38 @@ def roundtrip_noquant(x_bits, block: int, tau: float = 1.0, eps: float = EPS) ->
     out = np.empty(block, np.float64)
     _check(lib.taco_oracle_roundtrip_noquant(_ptr(x), block, tau, eps, _ptr(out)))
     return out
+
+
+# ------------------------------------------------- ablation variants ----
+
+#: Round-trip variants (see taco_oracle.c): the operator and the ablations the
+#: TACO paper compares it with.
+VARIANTS = {"taco": 0, "direct": 1, "ds": 2, "ash": 3, "hadamard": 4, "tensor": 5}
+
+
+def roundtrip_variant(x_bits, block: int, variant: str, fmt: str = "e4m3", tau: float = 1.0,
+                      eps: float = EPS) -> np.ndarray:
+    """x' (float64, same shape as x) of one ablation variant's round trip."""
+    lib = _load()
+    x = np.ascontiguousarray(x_bits, dtype=np.uint16)
+    if variant not in VARIANTS:
+        raise ValueError(f"unknown variant {variant!r} (one of {sorted(VARIANTS)})")
+    out = np.empty(x.shape, np.float64)
+    _check(lib.taco_oracle_roundtrip_variant(_ptr(x), x.size, block, VARIANTS[variant], _fmt(fmt),
+                                             tau, eps, _ptr(out)))
+    return out
+
+
+def fidelity(ref, got) -> dict:
+    """RelL2, Cos, MaxErr and MSE of got against ref (GIFT Eq. 21), in double."""
+    lib = _load()
+    r = np.ascontiguousarray(ref, dtype=np.float64).reshape(-1)
+    g = np.ascontiguousarray(got, dtype=np.float64).reshape(-1)
+    assert r.size == g.size and r.size > 0
+    out = np.empty(4, np.float64)
+    _check(lib.taco_oracle_fidelity(_ptr(r), _ptr(g), r.size, _ptr(out)))
+    return {"rel_l2": float(out[0]), "cos": float(out[1]), "max_err": float(out[2]),
+            "mse": float(out[3])}
 
 
 # ---------------------------------------------------- wire layout -------

@@ -478,6 +478,136 @@ int taco_oracle_reduce_compress(const uint16_t *own, int npay,
 }
 
 /* ------------------------------------------------------------------------ */
+/* Ablation variants and the fidelity metrics                                */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * The variants the TACO paper compares its operator with, each as a round
+ * trip x -> codes -> x' (every variant keeps the code format's Q_max):
+ *   0 TACO      ASH + DS: Eq. 5-13 (compress, then reconstruct).
+ *   1 DIRECT    direct cast of x, no scaling (section 4.2.1 "direct FP8
+ *               quantization"; the NVFP8 arm of section 5.2.2).
+ *   2 DS        dual scale only: per block s = max|x| / Q_max, q = Cvt(x / s),
+ *               x' = decode(q) s (section 5.2.2, DS in isolation).
+ *   3 ASH       adaptive scale and rotation, no post-rotation scale:
+ *               q = Cvt(Z) with Z of Eq. 8, x' = H decode(q) / sqrt(B) / alpha
+ *               (section 5.2.2, ASH alone).
+ *   4 HADAMARD  the standard rotation alone: Z = H x / sqrt(B), q = Cvt(Z),
+ *               x' = H decode(q) / sqrt(B) (sections 4.2.1 and 5.3.1).
+ *   5 TENSOR    one scale for the whole tensor: Delta = max|x| / Q_max,
+ *               q = Cvt(x / Delta), x' = decode(q) Delta (the uniform
+ *               quantiser of section 2.3 / Eq. 1 with INT8 codes; the same
+ *               per-tensor scaling with the FP8 formats).
+ * Cvt rounds the float32 value of its argument (saturating), as in Eq. 10;
+ * scalars that a receiver would use (alpha, s, Delta) are float32.  The
+ * output x' is in double (no output rounding).
+ */
+#define ORACLE_VARIANT_TACO 0
+#define ORACLE_VARIANT_DIRECT 1
+#define ORACLE_VARIANT_DS 2
+#define ORACLE_VARIANT_ASH 3
+#define ORACLE_VARIANT_HADAMARD 4
+#define ORACLE_VARIANT_TENSOR 5
+
+static uint8_t cvt_fmt(double v, int fmt)
+{
+    float f = (float)v;
+    if (f == 0.0f) f = 0.0f;                       /* zero carries no sign */
+    return encode_fmt(f, fmt);
+}
+
+int taco_oracle_roundtrip_variant(const uint16_t *x, int64_t n, int B, int variant,
+                                  int fmt, double tau, double eps, double *out)
+{
+    if (!valid_block(B) || !valid_fmt(fmt) || n < 0 || n % B) return -1;
+    if (variant < ORACLE_VARIANT_TACO || variant > ORACLE_VARIANT_TENSOR) return -1;
+    const double qmax = taco_oracle_qmax(fmt);
+    const double c = 1.0 / sqrt((double)B);
+    double tensor_max = 0.0;
+    for (int64_t i = 0; i < n; ++i) tensor_max = fmax(tensor_max, fabs(bf16_to_double(x[i])));
+    const float delta = (float)(tensor_max / qmax);
+    double G[ORACLE_MAX_BLOCK], Z[ORACLE_MAX_BLOCK];
+    uint8_t q[ORACLE_MAX_BLOCK];
+    for (int64_t k = 0; k < n / B; ++k) {
+        const uint16_t *xb = x + k * B;
+        double *ob = out + k * B;
+        for (int j = 0; j < B; ++j) G[j] = bf16_to_double(xb[j]);
+        switch (variant) {
+        case ORACLE_VARIANT_TACO: {
+            float a32, s32;
+            double a;
+            ash_block_f64(G, B, tau, eps, &a, NULL, Z);
+            quantise_block(Z, a, B, fmt, q, &a32, &s32);
+            reconstruct_block(q, a32, s32, B, fmt, ob);
+            break;
+        }
+        case ORACLE_VARIANT_DIRECT:
+            for (int j = 0; j < B; ++j) ob[j] = decode_fmt(cvt_fmt(G[j], fmt), fmt);
+            break;
+        case ORACLE_VARIANT_DS: {
+            double m = 0.0;
+            for (int j = 0; j < B; ++j) m = fmax(m, fabs(G[j]));
+            const double s = m / qmax;
+            const float s32 = (float)s;
+            for (int j = 0; j < B; ++j) {
+                double v = (s > 0.0) ? G[j] / s : 0.0;
+                ob[j] = decode_fmt(cvt_fmt(v, fmt), fmt) * (double)s32;
+            }
+            break;
+        }
+        case ORACLE_VARIANT_ASH: {
+            double a;
+            ash_block_f64(G, B, tau, eps, &a, NULL, Z);
+            const float a32 = (float)a;
+            for (int j = 0; j < B; ++j) ob[j] = decode_fmt(cvt_fmt(Z[j], fmt), fmt);
+            taco_oracle_fwht(ob, B);
+            for (int j = 0; j < B; ++j) ob[j] = ob[j] * c / (double)a32;
+            break;
+        }
+        case ORACLE_VARIANT_HADAMARD:
+            memcpy(Z, G, sizeof(double) * (size_t)B);
+            taco_oracle_fwht(Z, B);
+            for (int j = 0; j < B; ++j) ob[j] = decode_fmt(cvt_fmt(Z[j] * c, fmt), fmt);
+            taco_oracle_fwht(ob, B);
+            for (int j = 0; j < B; ++j) ob[j] *= c;
+            break;
+        default: /* ORACLE_VARIANT_TENSOR */
+            for (int j = 0; j < B; ++j) {
+                double v = (tensor_max > 0.0) ? G[j] / (tensor_max / qmax) : 0.0;
+                ob[j] = decode_fmt(cvt_fmt(v, fmt), fmt) * (double)delta;
+            }
+            break;
+        }
+    }
+    return 0;
+}
+
+/*
+ * Round-trip fidelity of x' against the reference x (n values), as the GIFT
+ * page defines it (Eq. 21): out[0] = RelL2 = |x' - x|_2 / |x|_2,
+ * out[1] = Cos = <x', x> / (|x'|_2 |x|_2), out[2] = MaxErr = |x' - x|_inf,
+ * out[3] = MSE = |x' - x|_2^2 / n.  Sums in double, in element order.
+ */
+int taco_oracle_fidelity(const double *ref, const double *got, int64_t n, double *out)
+{
+    if (n <= 0) return -1;
+    double se = 0.0, sr = 0.0, sg = 0.0, sd = 0.0, me = 0.0;
+    for (int64_t i = 0; i < n; ++i) {
+        double d = got[i] - ref[i];
+        se += d * d;
+        sr += ref[i] * ref[i];
+        sg += got[i] * got[i];
+        sd += got[i] * ref[i];
+        me = fmax(me, fabs(d));
+    }
+    out[0] = (sr > 0.0) ? sqrt(se) / sqrt(sr) : sqrt(se);
+    out[1] = (sr > 0.0 && sg > 0.0) ? sd / (sqrt(sg) * sqrt(sr)) : 0.0;
+    out[2] = me;
+    out[3] = se / (double)n;
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
 /* Self-check mode: the ASH round trip with quantisation left out            */
 /* ------------------------------------------------------------------------ */
 
