@@ -20,7 +20,9 @@ the dominant kernel and the CPU oracle's rate on the same workload.
 ``NAME:owner`` times the fused owner step of the two-shot all-reduce
 (``taco_reduce_compress`` of an own partial plus three payloads) instead;
 ``NAME:packed`` the round trip through the interleaved wire layout;
-``NAME:e5m2`` and ``NAME:int8`` the round trip with E5M2 or INT8 codes.
+``NAME:e5m2`` and ``NAME:int8`` the round trip with E5M2 or INT8 codes;
+``NAME:fidelity`` the fidelity study's fused round trip (``taco_roundtrip``,
+the operator's variant, error sums only).
 """
 from __future__ import annotations
 
@@ -73,6 +75,8 @@ def algorithmic_bytes(op: str, n: int, block: int) -> float:
         return n + side + 2.0 * n
     if op == "accumulate":
         return n + side + 8.0 * n
+    if op == "roundtrip":
+        return 2.0 * n
     raise ValueError(op)
 
 
@@ -234,6 +238,37 @@ def packed_case(torch, taco, synth, name: str, block: int, steps: int, warmup: i
             "input_bytes_step": 2.0 * n, "kernels": {"compress": t_c, "decompress": t_d}}
 
 
+def fidelity_case(torch, taco, synth, name: str, block: int, steps: int, warmup: int,
+                  use_graph: bool):
+    """taco_roundtrip of the operator's variant with error sums only: reads
+    the bf16 tensor once (plus a clearing launch of the 40-byte sums)."""
+    import numpy as np
+    r = synth.WORKLOADS[name]
+    n = r.numel
+    x0 = torch.from_numpy(synth.generate(r).view(np.int16)).cuda().view(torch.bfloat16)
+    nsets = max(1, -(-ROTATE_BYTES // (2 * n)))
+    sets = [(x0.clone(), torch.empty(taco.FIDELITY_SUMS_BYTES, dtype=torch.uint8, device="cuda"))
+            for _ in range(nsets)]
+    del x0
+
+    def run_steps():
+        for x, sums in sets:
+            taco.roundtrip(x, block=block, variant="taco", sums=sums)
+
+    for _ in range(max(1, warmup // nsets)):
+        run_steps()
+    torch.cuda.synchronize()
+    step_fn = make_graph(torch, run_steps, use_graph)
+    reps = max(1, -(-steps // nsets))
+    timer = Timer(torch)
+    step_fn()
+    k = reps * nsets
+    t = timer.time(step_fn, reps) / k
+    return {"n": n, "block": block, "steps": k, "t_step": t, "sets": nsets, "rows": r.rows,
+            "cols": r.cols, "fidelity": True, "bytes_step": 2.0 * n, "input_bytes_step": 2.0 * n,
+            "kernels": {"roundtrip": t}}
+
+
 def accumulate_case(torch, taco, synth, name: str, block: int, steps: int, warmup: int,
                     use_graph: bool):
     import numpy as np
@@ -379,6 +414,8 @@ def record(res, name: str, args, cpu=None):
                             else f"reduce_compress of own + {res['npayloads']} payloads"
                             if "npayloads" in res
                             else "compress_packed + decompress_packed" if res.get("packed")
+                            else "roundtrip with error sums (fidelity study)"
+                            if res.get("fidelity")
                             else "compress + decompress"),
                    "buffer_sets": res["sets"], "graph": not args.no_graph},
         "pct_hbm_peak": round(100.0 * res["bytes_step"] / t_step / 1e9 / HBM_PEAK_GBS, 2),
@@ -429,7 +466,8 @@ def main():
                  ("gpt175b_hidden_32768x12288:owner", 256),
                  ("gpt2.7b_rowpar_8192x2560:packed", 128),
                  ("gpt2.7b_rowpar_8192x2560:e5m2", 128),
-                 ("gpt2.7b_rowpar_8192x2560:int8", 128)]
+                 ("gpt2.7b_rowpar_8192x2560:int8", 128),
+                 ("gpt2.7b_rowpar_8192x2560:fidelity", 128)]
     else:
         name = args.workload or synth.DEFAULT_WORKLOAD
         block = args.block or synth.WORKLOADS[name.split(":")[0]].blocks[0]
@@ -446,6 +484,9 @@ def main():
         elif name.endswith(":packed"):
             name = name.split(":")[0]
             res = packed_case(torch, taco, synth, name, block, steps, args.warmup, use_graph)
+        elif name.endswith(":fidelity"):
+            name = name.split(":")[0]
+            res = fidelity_case(torch, taco, synth, name, block, steps, args.warmup, use_graph)
         elif name.endswith((":e5m2", ":int8")):
             name, fmt = name.split(":")
             res = roundtrip_case(torch, taco, synth, name, block, steps, args.warmup, use_graph,

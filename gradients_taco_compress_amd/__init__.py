@@ -11,13 +11,14 @@ Two layers:
   ``taco_reduce_compress``, their ``*_packed`` forms, the ``*_fmt`` forms of
   all eight (with a code format), ``taco_packed_bytes``, ``taco_encode``,
   ``taco_decode``, ``taco_e4m3_encode``, ``taco_e4m3_decode``,
-  ``taco_num_blocks``, ``taco_status_string``: the C ABI of
+  ``taco_roundtrip``, ``taco_num_blocks``, ``taco_status_string``: the C ABI of
   ``include/taco.h`` with the same names and arguments (device pointers as
   ints, stream handle as int, pointer arrays as sequences of ints, formats
   as the ints of ``FORMATS``).
 * ``compress``, ``decompress``, ``decompress_accumulate``, ``reduce_compress``,
   their ``*_packed`` forms on interleaved payloads, ``encode``, ``decode``,
-  ``e4m3_encode``, ``e4m3_decode``: the same calls on torch tensors,
+  ``e4m3_encode``, ``e4m3_decode``, ``roundtrip`` (with ``fidelity_metrics``):
+  the same calls on torch tensors,
   allocating outputs when none are given and launching on torch's current
   stream.  ``fmt`` names the code format ("e4m3", "e5m2" or "int8"); E4M3
   goes through the entry points without a format.
@@ -35,6 +36,8 @@ QMAX = 448.0
 #: Code formats (taco_format) and their Q_max.
 FORMATS = {"e4m3": 0, "e5m2": 1, "int8": 2}
 QMAX_OF = {"e4m3": 448.0, "e5m2": 57344.0, "int8": 127.0}
+#: Round-trip variants of the fidelity study (taco_variant).
+VARIANTS = {"taco": 0, "direct": 1, "ds": 2, "ash": 3, "hadamard": 4, "tensor": 5}
 EPS = 1e-20
 BLOCKS = (32, 64, 128, 256, 512)
 DEFAULT_TARGET_ENERGY = 1.0
@@ -94,6 +97,8 @@ _lib.taco_decompress_packed_fmt.argtypes = [_P, _I64, _I64, _I32, _I32, _P, _P]
 _lib.taco_decompress_accumulate_packed_fmt.argtypes = [_P, _I64, _I64, _I32, _I32, _P, _P]
 _lib.taco_reduce_compress_packed_fmt.argtypes = [_P, _I32, _P, _I64, _I64, _I32, _F32, _I32,
                                                  _P, _P]
+_lib.taco_roundtrip.argtypes = [_P, _I64, _I64, _I32, _F32, _I32, _I32, _P, _P, _P]
+_lib.taco_roundtrip.restype = ctypes.c_int
 _lib.taco_encode.argtypes = [_I32, _P, _I64, _P, _P]
 _lib.taco_decode.argtypes = [_I32, _P, _I64, _P, _P]
 for _name in ("compress_fmt", "decompress_fmt", "decompress_accumulate_fmt",
@@ -113,7 +118,7 @@ EXPORTS = ("taco_num_blocks", "taco_compress", "taco_decompress",
            "taco_decompress_accumulate_fmt", "taco_reduce_compress_fmt",
            "taco_compress_packed_fmt", "taco_decompress_packed_fmt",
            "taco_decompress_accumulate_packed_fmt", "taco_reduce_compress_packed_fmt",
-           "taco_encode", "taco_decode")
+           "taco_encode", "taco_decode", "taco_roundtrip")
 
 #: Most payloads one taco_reduce_compress call sums.
 MAX_PAYLOADS = 8
@@ -251,6 +256,12 @@ def taco_encode(format: int, x: int, n: int, codes: int, stream: int) -> int:
 
 def taco_decode(format: int, codes: int, n: int, out: int, stream: int) -> int:
     return _lib.taco_decode(format, codes, n, out, stream)
+
+
+def taco_roundtrip(x_bf16: int, tokens: int, hidden: int, block: int, target_energy: float,
+                   format: int, variant: int, y_bf16: int, sums: int, stream: int) -> int:
+    return _lib.taco_roundtrip(x_bf16, tokens, hidden, block, target_energy, format, variant,
+                               y_bf16, sums, stream)
 
 
 def taco_e4m3_encode(x: int, n: int, codes: int, stream: int) -> int:
@@ -602,3 +613,51 @@ def decode(codes, fmt: str = "e4m3", out=None, stream=None):
     _check(taco_decode(f, codes.data_ptr(), codes.numel(), out.data_ptr(), _stream(stream)),
            "taco_decode")
     return out
+
+
+#: Bytes of taco_fidelity_sums: the totals (four doubles, two floats) and
+#: the library's 64 slots of partial sums.
+FIDELITY_SUMS_BYTES = 40 + 4 * 64 * 8 + 2 * 64 * 4
+
+
+def roundtrip(x, block: int = 256, variant: str = "taco", fmt: str = "e4m3",
+              target_energy: float = DEFAULT_TARGET_ENERGY, want_output: bool = False,
+              sums=None, out=None, stream=None):
+    """One round trip of a fidelity-study variant over a bf16 tensor.
+    Returns (y or None, sums): y is the bf16 reconstruction (when wanted or
+    ``out`` is given), sums a uint8 device tensor holding taco_fidelity_sums
+    (read it with fidelity_metrics)."""
+    torch = _torch()
+    f = _format(fmt)
+    if variant not in VARIANTS:
+        raise ValueError(f"unknown variant {variant!r} (one of {sorted(VARIANTS)})")
+    _need(x, torch.bfloat16, "x")
+    tokens, hidden = _shape2(x)
+    if sums is None:
+        sums = torch.empty(FIDELITY_SUMS_BYTES, dtype=torch.uint8, device=x.device)
+    _need(sums, torch.uint8, "sums")
+    if sums.numel() < FIDELITY_SUMS_BYTES:
+        raise ValueError(f"sums must hold {FIDELITY_SUMS_BYTES} bytes")
+    if out is None and want_output:
+        out = torch.empty(x.shape, dtype=torch.bfloat16, device=x.device)
+    if out is not None:
+        _need(out, torch.bfloat16, "out")
+        if out.numel() != x.numel():
+            raise ValueError("out must have as many elements as x")
+    _check(taco_roundtrip(x.data_ptr(), tokens, hidden, block, float(target_energy), f,
+                          VARIANTS[variant], 0 if out is None else out.data_ptr(),
+                          sums.data_ptr(), _stream(stream)), "taco_roundtrip")
+    return out, sums
+
+
+def fidelity_metrics(sums, n: int) -> dict:
+    """RelL2, Cos, MaxErr and MSE (GIFT page, Eq. 21) of a round trip over n
+    elements, from its sums (synchronises with the device)."""
+    import struct
+    raw = bytes(sums[:40].cpu().numpy().tobytes())
+    se, sr, so, sd, me, tm = struct.unpack("<4d2f", raw)
+    return {"rel_l2": (se / sr) ** 0.5 if sr > 0 else se ** 0.5,
+            "cos": sd / (sr * so) ** 0.5 if sr > 0 and so > 0 else 0.0,
+            "max_err": me, "mse": se / n if n else 0.0,
+            "sum_sq_err": se, "sum_sq_ref": sr, "sum_sq_out": so, "sum_dot": sd,
+            "tensor_absmax": tm}

@@ -291,6 +291,29 @@ taco_status decode_any(taco_format format, const uint8_t *codes, int64_t n, floa
     return with_format(format, [&](auto ops) { return decltype(ops)::decode(codes, n, out, stream); });
 }
 
+taco_status roundtrip_any(const uint16_t *x, int64_t tokens, int64_t hidden, int32_t block,
+                          float tau, taco_format format, taco_variant variant, uint16_t *y,
+                          taco_fidelity_sums *sums, hipStream_t stream) {
+    if (!valid_format(format)) return TACO_ERR_FORMAT;
+    int64_t n = 0;
+    const taco_status st = check_shape(tokens, hidden, block, &n);
+    if (st != TACO_OK) return st;
+    if (!valid_tau(tau)) return TACO_ERR_PARAM;
+    if (variant < TACO_VARIANT_TACO || variant > TACO_VARIANT_TENSOR) return TACO_ERR_PARAM;
+    if (n == 0) return TACO_OK;
+    if (!sums || !x) return TACO_ERR_NULL;
+    if (!aligned(sums, 8)) return TACO_ERR_ALIGN;
+    const size_t ns = sizeof(taco_fidelity_sums);
+    if (!aligned(x, 16) || (y && !aligned(y, 16))) return TACO_ERR_ALIGN;
+    if (overlap(sums, ns, x, (size_t)n * 2) || (y && overlap(sums, ns, y, (size_t)n * 2)) ||
+        (y && overlap(y, (size_t)n * 2, x, (size_t)n * 2)))
+        return TACO_ERR_ALIAS;
+    const Variant v = static_cast<Variant>(static_cast<int>(variant));
+    return with_format(format, [&](auto ops) {
+        return decltype(ops)::roundtrip(v, block, x, n / block, tau, y, sums, stream);
+    });
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------- C ABI ---
@@ -446,13 +469,21 @@ taco_status taco_decode(taco_format format, const uint8_t *codes, int64_t n, flo
     return decode_any(format, codes, n, out, stream);
 }
 
+taco_status taco_roundtrip(const uint16_t *x_bf16, int64_t tokens, int64_t hidden,
+                           int32_t block, float target_energy, taco_format format,
+                           taco_variant variant, uint16_t *y_bf16, taco_fidelity_sums *sums,
+                           hipStream_t stream) {
+    return roundtrip_any(x_bf16, tokens, hidden, block, target_energy, format, variant, y_bf16,
+                         sums, stream);
+}
+
 const char *taco_status_string(taco_status status) {
     switch (status) {
         case TACO_OK: return "ok";
         case TACO_ERR_NULL: return "a required pointer is NULL";
         case TACO_ERR_SHAPE: return "bad shape: tokens < 0, hidden <= 0, or N not a multiple of the block";
         case TACO_ERR_BLOCK: return "block size must be 32, 64, 128, 256 or 512";
-        case TACO_ERR_PARAM: return "target energy must be finite and in (0, 1e20], and the payload count in 0..8 (0 only with own data)";
+        case TACO_ERR_PARAM: return "target energy must be finite and in (0, 1e20], the payload count in 0..8 (0 only with own data), and the variant a taco_variant value";
         case TACO_ERR_ALIGN: return "tensors must be 16-byte aligned, alpha and scale 4-byte aligned";
         case TACO_ERR_ALIAS: return "an output buffer overlaps an input or another output";
         case TACO_ERR_HIP: return "the HIP runtime refused the kernel launch";

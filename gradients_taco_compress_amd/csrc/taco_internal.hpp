@@ -19,6 +19,9 @@ enum class Layout { kSide, kPacked };
 // Decompress output: bf16 tensor, or float32 accumulator (acc += G').
 enum class Out { kBf16, kAccumulate };
 
+// Round-trip variants of the fidelity study (taco_variant of taco.h).
+enum class Variant { kTaco, kDirect, kDs, kAsh, kHadamard, kTensor };
+
 // Device pointers of the owner step's received payloads, passed by value to
 // the kernel.  For the interleaved layout, alpha[p] / scale[p] point at the
 // scalars of payload p's record 0.
@@ -44,6 +47,10 @@ struct Ops {
                                        const uint16_t *own, const Payloads &pay, int64_t nblocks,
                                        float tau, uint8_t *codes, float *alpha, float *scale,
                                        hipStream_t stream);
+    // Clears *sums, then (kTensor) finds max|x|, then runs the round trip.
+    static taco_status roundtrip(Variant variant, int32_t block, const uint16_t *x,
+                                 int64_t nblocks, float tau, uint16_t *y,
+                                 taco_fidelity_sums *sums, hipStream_t stream);
     static taco_status encode(const float *x, int64_t n, uint8_t *codes, hipStream_t stream);
     static taco_status decode(const uint8_t *codes, int64_t n, float *out, hipStream_t stream);
 };

@@ -462,8 +462,10 @@ constexpr double inv_sqrt(int b) {
 }
 
 // Blocks whose energy reaches this are rescaled by 2^-64 before squaring so
-// that sum x^2 stays finite for every bf16 input.
+// that sum x^2 stays finite for every bf16 input.  (kBigMax: the same for a
+// block maximum, before a plain rotation.)
 constexpr float kBigEnergy = 0x1p100f;
+constexpr float kBigMax = 0x1p100f;
 constexpr float kBigShift = 0x1p-64f;
 constexpr float kBigUnshift = 0x1p-64f;   // alpha of the original block = alpha' * 2^-64
 // Blocks with max|R| below this get R and max|R| scaled by 2^64 before
@@ -820,6 +822,309 @@ __global__ __launch_bounds__(kGroup) void reduce_compress_kernel(
     }
 }
 
+// ---------------------------------------------------- fidelity study -----
+
+// Saturating codes of 8 values (the ablation variants without a scale can
+// exceed Q_max): clamp to +-Q_max, map -0 to +0 (as encode8 does), convert.
+template <Fmt F>
+__device__ __forceinline__ u2v encode8_sat(const float *v, float factor) {
+    constexpr float Q = Codec<F>::kQmax;
+    float q[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) q[j] = fminf(fmaxf(fmaf(v[j], factor, 0.0f), -Q), Q);
+    return Codec<F>::pack8(q);
+}
+
+// Wave-level sum of a double (butterfly over the 64 lanes).
+__device__ __forceinline__ double wave_sum(double v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o /= 2) v += __shfl_xor(v, o, kWave);
+    return v;
+}
+__device__ __forceinline__ uint32_t wave_max_u(uint32_t v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o /= 2) v = max(v, (uint32_t)__shfl_xor((int)v, o, kWave));
+    return v;
+}
+
+// Clears the sums (one work-group).
+__global__ __launch_bounds__(kGroup) void fidelity_clear_kernel(taco_fidelity_sums *sums) {
+    const int i = threadIdx.x;
+    if (i < 4 * TACO_FIDELITY_SLOTS) (&sums->slot_sum[0][0])[i] = 0.0;
+    if (i < TACO_FIDELITY_SLOTS) {
+        sums->slot_max_err[i] = 0u;
+        sums->slot_absmax[i] = 0u;
+    }
+    if (i == 0) {
+        sums->sum_sq_err = 0.0;
+        sums->sum_sq_ref = 0.0;
+        sums->sum_sq_out = 0.0;
+        sums->sum_dot = 0.0;
+        sums->max_abs_err = 0.0f;
+        sums->tensor_absmax = 0.0f;
+    }
+}
+
+// max |x| of a bf16 tensor into the absmax slots (n a multiple of 8, 16-byte
+// aligned).  |bf16| as an integer orders like the value; the result is kept
+// as float32 bits.
+__global__ __launch_bounds__(kGroup) void absmax_kernel(const uint16_t *__restrict__ x,
+                                                        int64_t nchunks,
+                                                        taco_fidelity_sums *sums) {
+    uint32_t m = 0;
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < nchunks; i += stride) {
+        const u4v w = ld16(x + 8 * i);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) m = max(m, max(w[j] & 0x7FFFu, (w[j] >> 16) & 0x7FFFu));
+    }
+    m = wave_max_u(m);
+    __shared__ uint32_t part[kWavesPerGroup];
+    if ((threadIdx.x & (kWave - 1)) == 0) part[threadIdx.x >> 6] = m;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        uint32_t mm = 0;
+#pragma unroll
+        for (int w = 0; w < kWavesPerGroup; ++w) mm = max(mm, part[w]);
+        atomicMax(&sums->slot_absmax[blockIdx.x % TACO_FIDELITY_SLOTS], mm << 16);
+    }
+}
+
+// max over the absmax slots (every thread of the caller reads all slots).
+__device__ __forceinline__ float tensor_absmax_of(const taco_fidelity_sums *sums) {
+    uint32_t m = 0;
+    for (int i = 0; i < TACO_FIDELITY_SLOTS; ++i) m = max(m, sums->slot_absmax[i]);
+    return __uint_as_float(m);
+}
+
+// Totals from the slots (one wave; slot i in lane i, a fixed order).
+__global__ __launch_bounds__(kGroup) void fidelity_finish_kernel(taco_fidelity_sums *sums) {
+    const int lane = threadIdx.x;
+    if (lane >= kWave) return;
+    double t[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) t[q] = wave_sum(sums->slot_sum[q][lane]);
+    const uint32_t me = wave_max_u(sums->slot_max_err[lane]);
+    const uint32_t ma = wave_max_u(sums->slot_absmax[lane]);
+    if (lane == 0) {
+        sums->sum_sq_err = t[0];
+        sums->sum_sq_ref = t[1];
+        sums->sum_sq_out = t[2];
+        sums->sum_dot = t[3];
+        sums->max_abs_err = __uint_as_float(me);
+        sums->tensor_absmax = __uint_as_float(ma);
+    }
+}
+
+// One round trip of variant V per block, with the reconstruction error sums
+// (see taco_fidelity_sums).  Same lane layout as compress_kernel; the codes
+// of each chunk stay in registers.  The TACO variant repeats compress_kernel
+// and decompress_kernel operation for operation, so its output equals
+// decompress(compress(x)).  Grid-stride over wave-steps; each work-group
+// adds its sums with one atomic per quantity.
+template <int B, Fmt F, Variant V>
+__global__ __launch_bounds__(kGroup) void roundtrip_kernel(
+    const uint16_t *__restrict__ x, int64_t nblocks, float tau, uint16_t *__restrict__ y,
+    taco_fidelity_sums *sums) {
+    using G = Geo<B>;
+    using C = Codec<F>;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x >> 6;
+    const int t = lane_sub<G::LPB>(lane);
+    const int g = lane_slot<G::LPB>(lane);
+    const float sg1 = (lane & 1) ? -1.0f : 1.0f;
+    const float sg2 = (lane & 2) ? -1.0f : 1.0f;
+    const float sg8 = (lane & 8) ? -1.0f : 1.0f;
+    const float lane_sign = (__popc(t) & 1) ? -1.0f : 1.0f;
+    constexpr float kScaleFactor = (float)(inv_sqrt(B) / (double)C::kQmax);
+    constexpr float kInvSqrtB = (float)inv_sqrt(B);
+    constexpr float kInvB = 1.0f / (float)B;
+
+    // The whole tensor's max |x| (TENSOR variant; from absmax_kernel).
+    const float tmax = (V == Variant::kTensor) ? tensor_absmax_of(sums) : 0.0f;
+
+    double acc_e = 0.0, acc_r = 0.0, acc_o = 0.0, acc_d = 0.0;
+    uint32_t max_e = 0;
+
+    const int64_t nsteps = (nblocks + G::BPW - 1) / G::BPW;
+    const int64_t nwaves = (int64_t)gridDim.x * kWavesPerGroup;
+    for (int64_t step = (int64_t)blockIdx.x * kWavesPerGroup + wave; step < nsteps;
+         step += nwaves) {
+        // Slots past the last block re-read the last block; nothing of them
+        // is stored or summed.
+        const int64_t left = nblocks - step * G::BPW;
+        const int gl = (left >= G::BPW || g < left) ? g : (int)left - 1;
+        const uint16_t *p = x + step * (G::BPW * B) + (uint32_t)(gl * B + 8 * t);
+        const int64_t blk = step * G::BPW + g;
+        const bool active = blk < nblocks;
+        u4v buf[G::CH];
+#pragma unroll
+        for (int k = 0; k < G::CH; ++k) buf[k] = ld16(p + k * G::SPAN);
+        float xin[G::EPL], v[G::EPL];
+#pragma unroll
+        for (int k = 0; k < G::CH; ++k) unpack8(buf[k], &xin[8 * k]);
+#pragma unroll
+        for (int i = 0; i < G::EPL; ++i) v[i] = xin[i];
+
+        u2v q[G::CH];
+        float f = 1.0f;            // output factor applied after decoding
+        bool rotate_back = false;  // inverse transform after decoding
+        bool two_step = false;     // TACO: apply (2^64 f) then 2^-64, as decompress does
+        float fs = 0.0f;
+
+        if (V == Variant::kTaco || V == Variant::kAsh) {
+            // Eq. 6-7 as in compress_kernel (including its huge-block path).
+#if TACO_DOT2_ENERGY
+            float energy = energy_packed<G::CH>(buf);
+#else
+            float energy = sum_squares<G::EPL>(v);
+#endif
+            energy = block_sum<G::LPB>(energy);
+            float unshift = 1.0f;
+            if (__builtin_expect(energy >= kBigEnergy, 0)) {
+#pragma unroll
+                for (int i = 0; i < G::EPL; ++i) v[i] *= kBigShift;
+                energy = block_sum<G::LPB>(sum_squares<G::EPL>(v));
+                unshift = kBigUnshift;
+            }
+            const float a = tau * __builtin_amdgcn_rsqf(energy * kInvB + TACO_EPS);
+            fwht_block<G::LPB, G::EPL>(v, sg1, sg2, sg8);
+            rotate_back = true;
+            if (V == Variant::kTaco) {
+                float m = block_max<G::LPB>(max_abs<G::EPL>(v));
+                const float s = a * m * kScaleFactor;
+                if (__builtin_expect(m < kTinyMax && m > 0.0f, 0)) {
+#pragma unroll
+                    for (int i = 0; i < G::EPL; ++i) v[i] *= kTinyShift;
+                    m *= kTinyShift;
+                }
+                Quot r = quotient(C::kQmax, m);
+                r.hi = (m > 0.0f) ? r.hi * lane_sign : 0.0f;
+                r.lo = (m > 0.0f) ? r.lo * lane_sign : 0.0f;
+#pragma unroll
+                for (int k = 0; k < G::CH; ++k) q[k] = encode8<F>(&v[8 * k], r);
+                // decompress_kernel's output factor from the stored alpha, s.
+                const float at = a * unshift;
+                f = ((s * kInvSqrtB) / at) * lane_sign;
+                if (__builtin_expect(s > 0.0f && fabsf(f) < kTinyOut, 0)) {
+                    two_step = true;
+                    fs = (((s * kOutShift) * kInvSqrtB) / at) * lane_sign;
+                }
+            } else {
+                // Z = alpha R / sqrt(B) with R = H x (lane-signed), codes of Z.
+                const float za = a * kInvSqrtB * lane_sign;
+#pragma unroll
+                for (int k = 0; k < G::CH; ++k) q[k] = encode8_sat<F>(&v[8 * k], za);
+                f = (kInvSqrtB / (a * unshift)) * lane_sign;
+            }
+        } else if (V == Variant::kHadamard) {
+            // Blocks whose rotated values could overflow float32 are rotated
+            // as x 2^-64 (exact); the codes of Z = 2^64 R' / sqrt(B) then
+            // saturate as Z's would.
+            float zf = kInvSqrtB * lane_sign;
+            if (__builtin_expect(block_max<G::LPB>(max_abs<G::EPL>(v)) >= kBigMax, 0)) {
+#pragma unroll
+                for (int i = 0; i < G::EPL; ++i) v[i] *= kBigShift;
+                zf *= kTinyShift;
+            }
+            fwht_block<G::LPB, G::EPL>(v, sg1, sg2, sg8);
+            rotate_back = true;
+#pragma unroll
+            for (int k = 0; k < G::CH; ++k) q[k] = encode8_sat<F>(&v[8 * k], zf);
+            f = kInvSqrtB * lane_sign;
+        } else if (V == Variant::kDirect) {
+#pragma unroll
+            for (int k = 0; k < G::CH; ++k) q[k] = encode8_sat<F>(&v[8 * k], 1.0f);
+        } else {
+            // DS (block max) or TENSOR (tensor max): codes of x Q / m, x' = decode * (m / Q).
+            float m = (V == Variant::kDs) ? block_max<G::LPB>(max_abs<G::EPL>(v)) : tmax;
+            const float s = m / C::kQmax;
+            if (__builtin_expect(m < kTinyMax && m > 0.0f, 0)) {
+#pragma unroll
+                for (int i = 0; i < G::EPL; ++i) v[i] *= kTinyShift;
+                m *= kTinyShift;
+            }
+            Quot r = quotient(C::kQmax, m);
+            r.hi = (m > 0.0f) ? r.hi : 0.0f;
+            r.lo = (m > 0.0f) ? r.lo : 0.0f;
+#pragma unroll
+            for (int k = 0; k < G::CH; ++k) q[k] = encode8<F>(&v[8 * k], r);
+            f = s;
+        }
+
+        // Receiver side: decode, rotate back, scale.
+#pragma unroll
+        for (int k = 0; k < G::CH; ++k) C::decode8(q[k], &v[8 * k]);
+        if (rotate_back) fwht_block<G::LPB, G::EPL>(v, sg1, sg2, sg8);
+        if (V == Variant::kTaco && two_step) {
+#pragma unroll
+            for (int i = 0; i < G::EPL; ++i) v[i] = (v[i] * fs) * kOutUnshift;
+        } else if (V != Variant::kDirect) {
+#pragma unroll
+            for (int i = 0; i < G::EPL; ++i) v[i] *= f;
+        }
+
+        if (active) {
+            if (y) {
+                const int64_t e0 = blk * B + 8 * t;
+#pragma unroll
+                for (int k = 0; k < G::CH; ++k) {
+                    const float *w = &v[8 * k];
+                    const u4v o = {pack_bf16x2(w[0], w[1]), pack_bf16x2(w[2], w[3]),
+                                   pack_bf16x2(w[4], w[5]), pack_bf16x2(w[6], w[7])};
+                    st16(y + e0 + k * G::SPAN, o);
+                }
+            }
+            float se = 0.0f, sr = 0.0f, so = 0.0f, sd = 0.0f, me = 0.0f;
+#pragma unroll
+            for (int i = 0; i < G::EPL; ++i) {
+                const float d = v[i] - xin[i];
+                se = fmaf(d, d, se);
+                sr = fmaf(xin[i], xin[i], sr);
+                so = fmaf(v[i], v[i], so);
+                sd = fmaf(v[i], xin[i], sd);
+                me = fmaxf(me, fabsf(d));
+            }
+            acc_e += (double)se;
+            acc_r += (double)sr;
+            acc_o += (double)so;
+            acc_d += (double)sd;
+            max_e = max(max_e, __float_as_uint(me));
+        }
+    }
+
+    // Work-group totals: waves reduce, wave 0 adds them with atomics.
+    __shared__ double part[kWavesPerGroup][4];
+    __shared__ uint32_t part_max[kWavesPerGroup];
+    acc_e = wave_sum(acc_e);
+    acc_r = wave_sum(acc_r);
+    acc_o = wave_sum(acc_o);
+    acc_d = wave_sum(acc_d);
+    max_e = wave_max_u(max_e);
+    if (lane == 0) {
+        part[wave][0] = acc_e;
+        part[wave][1] = acc_r;
+        part[wave][2] = acc_o;
+        part[wave][3] = acc_d;
+        part_max[wave] = max_e;
+    }
+    __syncthreads();
+    const int slot = blockIdx.x % TACO_FIDELITY_SLOTS;
+    if (wave == 0 && lane < 5) {
+        if (lane < 4) {
+            double tsum = 0.0;
+#pragma unroll
+            for (int w = 0; w < kWavesPerGroup; ++w) tsum += part[w][lane];
+            atomicAdd(&sums->slot_sum[lane][slot], tsum);
+        } else {
+            uint32_t mm = 0;
+#pragma unroll
+            for (int w = 0; w < kWavesPerGroup; ++w) mm = max(mm, part_max[w]);
+            atomicMax(&sums->slot_max_err[slot], mm);
+        }
+    }
+}
+
 // ------------------------------------------------------------- codec ------
 
 // Element-wise conversions through the same pack8 / decode8 the operator
@@ -986,6 +1291,61 @@ taco_status Ops<F>::reduce_compress(Layout layout, int32_t block, int npay, cons
                                                                   codes, alpha, scale, stream});
     return for_block(block, ReduceLaunch<F, Layout::kSide>{npay, own, pay, nblocks, tau, codes,
                                                             alpha, scale, stream});
+}
+
+template <Fmt F, Variant V>
+struct RoundtripLaunch {
+    const uint16_t *x; int64_t m; float tau; uint16_t *y; taco_fidelity_sums *sums;
+    hipStream_t stream;
+    template <int B> taco_status run() const {
+        // Capped grid: 2048 groups of 4 waves fill every wave slot, and each
+        // group adds its totals with one atomic per quantity into one of
+        // the 64 slots (32 groups per slot).
+        unsigned grid = grid_for(steps_of<B>(m));
+        grid = grid < 2048u ? grid : 2048u;
+        return launch(reinterpret_cast<const void *>(&roundtrip_kernel<B, F, V>), grid, stream,
+                      x, m, tau, y, sums);
+    }
+};
+
+template <Fmt F>
+taco_status roundtrip_variant(Variant variant, int32_t block, const uint16_t *x, int64_t nblocks,
+                              float tau, uint16_t *y, taco_fidelity_sums *sums,
+                              hipStream_t stream) {
+    switch (variant) {
+        case Variant::kTaco:
+            return for_block(block, RoundtripLaunch<F, Variant::kTaco>{x, nblocks, tau, y, sums, stream});
+        case Variant::kDirect:
+            return for_block(block, RoundtripLaunch<F, Variant::kDirect>{x, nblocks, tau, y, sums, stream});
+        case Variant::kDs:
+            return for_block(block, RoundtripLaunch<F, Variant::kDs>{x, nblocks, tau, y, sums, stream});
+        case Variant::kAsh:
+            return for_block(block, RoundtripLaunch<F, Variant::kAsh>{x, nblocks, tau, y, sums, stream});
+        case Variant::kHadamard:
+            return for_block(block, RoundtripLaunch<F, Variant::kHadamard>{x, nblocks, tau, y, sums, stream});
+        case Variant::kTensor:
+            return for_block(block, RoundtripLaunch<F, Variant::kTensor>{x, nblocks, tau, y, sums, stream});
+    }
+    return TACO_ERR_PARAM;
+}
+
+template <Fmt F>
+taco_status Ops<F>::roundtrip(Variant variant, int32_t block, const uint16_t *x, int64_t nblocks,
+                              float tau, uint16_t *y, taco_fidelity_sums *sums,
+                              hipStream_t stream) {
+    taco_status st = launch(reinterpret_cast<const void *>(&fidelity_clear_kernel), 1u, stream,
+                            sums);
+    if (st != TACO_OK || nblocks == 0) return st;
+    if (variant == Variant::kTensor) {
+        const int64_t nchunks = nblocks * block / 8;
+        const int64_t need = (nchunks + kGroup - 1) / kGroup;
+        const unsigned grid = (unsigned)(need < 1024 ? need : 1024);
+        st = launch(reinterpret_cast<const void *>(&absmax_kernel), grid, stream, x, nchunks, sums);
+        if (st != TACO_OK) return st;
+    }
+    st = roundtrip_variant<F>(variant, block, x, nblocks, tau, y, sums, stream);
+    if (st != TACO_OK) return st;
+    return launch(reinterpret_cast<const void *>(&fidelity_finish_kernel), 1u, stream, sums);
 }
 
 template <Fmt F>

@@ -249,6 +249,71 @@ taco_status taco_reduce_compress_packed_fmt(const uint16_t *own_bf16, int32_t np
                                             hipStream_t stream);
 
 /*
+ * Fidelity study: round trips of the operator and of the variants [TACO]
+ * compares it with, measured against the input.
+ *   TACO_VARIANT_TACO      the operator: ASH + DS, Eq. 5-13 (compress, then
+ *                          decompress, in one pass; codes stay in registers).
+ *   TACO_VARIANT_DIRECT    direct cast of x to codes, no scaling (section
+ *                          4.2.1 direct FP8 quantization; the NVFP8 arm of
+ *                          section 5.2.2); saturating at +-Q_max.
+ *   TACO_VARIANT_DS        dual scale alone: per block s = max|x| / Q_max,
+ *                          no rotation (section 5.2.2, DS in isolation).
+ *   TACO_VARIANT_ASH       Eq. 6-8 without the post-rotation scale: codes of
+ *                          Z itself, saturating (section 5.2.2, ASH alone).
+ *   TACO_VARIANT_HADAMARD  the standard rotation alone, Z = H x / sqrt(B),
+ *                          saturating (sections 4.2.1 and 5.3.1).
+ *   TACO_VARIANT_TENSOR    one scale for the whole tensor, max|x| / Q_max (the
+ *                          quantiser of section 2.3 / Eq. 1 with INT8 codes).
+ * Every variant uses the code format given (and its Q_max).
+ */
+typedef enum {
+    TACO_VARIANT_TACO = 0,
+    TACO_VARIANT_DIRECT = 1,
+    TACO_VARIANT_DS = 2,
+    TACO_VARIANT_ASH = 3,
+    TACO_VARIANT_HADAMARD = 4,
+    TACO_VARIANT_TENSOR = 5
+} taco_variant;
+
+/* Sums a round trip accumulates, in device memory (8-byte aligned; the
+ * caller allocates sizeof(taco_fidelity_sums) bytes).  With n elements, x
+ * the input and x' the float32 reconstruction (before any output rounding),
+ * the metrics of the GIFT page's Eq. 21 ("GIFT: Geometry-Informed
+ * Low-precision Gradient Communication for LLM Pretraining") are
+ * RelL2 = sqrt(sum_sq_err / sum_sq_ref),
+ * Cos = sum_dot / sqrt(sum_sq_ref * sum_sq_out), MaxErr = max_abs_err and
+ * MSE = sum_sq_err / n.  Per-block partial sums are float32; work-groups add
+ * them in double, with atomics, into TACO_FIDELITY_SLOTS slots (so the last
+ * bits of a total vary between runs); the totals are the slots' sum. */
+#define TACO_FIDELITY_SLOTS 64
+typedef struct {
+    double sum_sq_err;    /* sum (x' - x)^2 */
+    double sum_sq_ref;    /* sum x^2 */
+    double sum_sq_out;    /* sum x'^2 */
+    double sum_dot;       /* sum x' x */
+    float max_abs_err;    /* max |x' - x| */
+    float tensor_absmax;  /* max |x| (TACO_VARIANT_TENSOR only; else 0) */
+    /* Written by the library before the totals above (contents unspecified
+     * for the caller). */
+    double slot_sum[4][TACO_FIDELITY_SLOTS];
+    uint32_t slot_max_err[TACO_FIDELITY_SLOTS];
+    uint32_t slot_absmax[TACO_FIDELITY_SLOTS];
+} taco_fidelity_sums;
+
+/*
+ * One round trip of a variant over a bf16 tensor (shape, block and
+ * target_energy as in taco_compress; target_energy is used by the TACO and
+ * ASH variants).  sums (required, device) is overwritten with this call's
+ * sums; y_bf16 (optional, NULL for none) receives x' rounded to bf16.
+ * sums must not overlap x or y.  A bad variant is TACO_ERR_PARAM.  As
+ * everywhere, N == 0 is a no-op (sums is then not written).
+ */
+taco_status taco_roundtrip(const uint16_t *x_bf16, int64_t tokens, int64_t hidden,
+                           int32_t block, float target_energy, taco_format format,
+                           taco_variant variant, uint16_t *y_bf16, taco_fidelity_sums *sums,
+                           hipStream_t stream);
+
+/*
  * The E4M3 conversions the kernels above use (Cvt_FP8 of [TACO] Eq. 10 and
  * Cvt_FP32 of Eq. 11), exposed element-wise so that they can be checked
  * exhaustively.  encode: round to nearest even, OCP E4M3FN; inputs of

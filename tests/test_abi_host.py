@@ -62,6 +62,7 @@ def lib():
     L.taco_decompress_packed_fmt.argtypes = [P, I64, I64, I32, I32, P, P]
     L.taco_decompress_accumulate_packed_fmt.argtypes = [P, I64, I64, I32, I32, P, P]
     L.taco_reduce_compress_packed_fmt.argtypes = [P, I32, P, I64, I64, I32, F32, I32, P, P]
+    L.taco_roundtrip.argtypes = [P, I64, I64, I32, F32, I32, I32, P, P, P]
     L.taco_encode.argtypes = [I32, P, I64, P, P]
     L.taco_decode.argtypes = [I32, P, I64, P, P]
     L.taco_status_string.argtypes = [ctypes.c_int]
@@ -71,7 +72,7 @@ def lib():
 
 def test_every_declared_function_is_exported(lib):
     names = declared_functions()
-    assert len(names) == 23, names
+    assert len(names) == 24, names
     for n in names:
         assert hasattr(lib, n), n
     out = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True).stdout
@@ -295,3 +296,27 @@ def test_format_calls_match_e4m3_calls_on_errors(lib):
         a = lib.taco_compress(A, 3, hidden, block, tau, 2 * A, 3 * A, 4 * A, None)
         b = lib.taco_compress_fmt(A, 3, hidden, block, tau, E4M3, 2 * A, 3 * A, 4 * A, None)
         assert a == b == want
+
+
+def test_roundtrip_validation(lib):
+    rt = lambda **k: lib.taco_roundtrip(k.get("x", A), k.get("tokens", 4), k.get("hidden", 256),
+                                        k.get("block", 128), k.get("tau", 1.0),
+                                        k.get("fmt", E4M3), k.get("variant", 0),
+                                        k.get("y", 2 * A), k.get("sums", 3 * A), None)
+    assert rt(fmt=7) == FORMAT
+    assert rt(fmt=7, tokens=0) == FORMAT
+    assert rt(tokens=-1) == SHAPE
+    assert rt(hidden=96, tokens=3) == SHAPE
+    assert rt(block=48) == BLOCK
+    assert rt(tau=0.0) == PARAM
+    for bad in (-1, 6, 99):
+        assert rt(variant=bad) == PARAM
+    assert rt(sums=None) == NULL
+    assert rt(x=None) == NULL
+    assert rt(sums=3 * A + 4) == ALIGN
+    assert rt(x=A + 8) == ALIGN
+    assert rt(y=2 * A + 2) == ALIGN
+    assert rt(sums=A + 64) == ALIAS            # inside x
+    assert rt(sums=2 * A + 512) == ALIAS       # inside y
+    assert rt(y=A + 1024) == ALIAS             # y overlaps x
+    assert rt(tokens=0, x=None, y=None, sums=None) == OK   # empty: nothing written
