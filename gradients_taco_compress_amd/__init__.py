@@ -55,6 +55,17 @@ class TacoError(RuntimeError):
         super().__init__(f"{what}: {STATUS.get(status, status)} ({taco_status_string(status)})")
 
 
+# libtaco.so names the HIP runtime by its soname (libamdhip64.so.7).  torch
+# ships its own copy of that runtime and loads it by another name, so which
+# copy the library binds to depends on load order: loading torch first makes
+# libtaco use torch's runtime, for which torch's device pointers and stream
+# handles are valid.  (Loaded the other way round, the process holds two HIP
+# runtimes and every launch on a torch stream fails.)
+try:
+    import torch as _torch_first  # noqa: F401
+except ImportError:  # pragma: no cover - the C ABI itself needs no torch
+    pass
+
 if not os.path.exists(LIB_PATH):
     raise ImportError(
         f"libtaco.so is not built ({LIB_PATH} missing); run "
