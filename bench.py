@@ -6,8 +6,8 @@ One step = one pass of the whole operator over one batch of synthetic input:
 round-trip workloads, or four ``taco_compress`` + four
 ``taco_decompress_accumulate`` calls for the four-payload workload.
 Inputs are resident in HBM before timing starts.  Buffer sets are rotated so
-that consecutive steps touch more than 512 MB (twice the 256 MB Infinity
-Cache) and each step streams from HBM.  The timed steps are replayed from a
+that every timed graph loads more than 1 GiB per replay (four times the
+256 MB Infinity Cache) and each kernel streams its inputs from HBM.  The timed steps are replayed from a
 HIP graph so that host launch overhead does not gap the GPU.
 
 Prints one JSON line (rank 0, the only rank): the headline metric is input
@@ -39,7 +39,19 @@ sys.path.insert(0, ROOT)
 METRIC = "compress+decompress GB/s of bf16 input and % of MI355X HBM peak"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E peak (AMD specification), GB/s
 MALL_BYTES = 256 << 20
-ROTATE_BYTES = 2 * MALL_BYTES
+# Buffer sets rotate so that every timed graph LOADS at least this much per
+# replay (four times the 256 MB Infinity Cache): data that cached loads leave
+# in the cache is long evicted when it is read again, so every kernel
+# streams its inputs from HBM.
+ROTATE_LOAD_BYTES = 4 * MALL_BYTES
+MAX_SET_BYTES = 12 << 30
+
+
+def rotation_sets(min_load_bytes: int, set_bytes: int) -> int:
+    """Buffer sets so that the smallest per-set load, repeated, reaches
+    ROTATE_LOAD_BYTES (capped by device memory)."""
+    nsets = max(1, -(-ROTATE_LOAD_BYTES // max(1, min_load_bytes)))
+    return max(1, min(nsets, MAX_SET_BYTES // max(1, set_bytes)))
 KERNEL_DIR = os.path.join(ROOT, "gradients_taco_compress_amd", "csrc")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 
@@ -145,7 +157,7 @@ def roundtrip_case(torch, taco, synth, name: str, block: int, steps: int, warmup
     x0 = torch.from_numpy(x_bits.view(np.int16)).cuda().view(torch.bfloat16)
     m = n // block
     per_set = 2 * n + n + 8 * m + 2 * n
-    nsets = max(1, -(-ROTATE_BYTES // per_set))
+    nsets = rotation_sets(n + 8 * m, per_set)        # the codes are the smallest input
     sets = []
     for _ in range(nsets):
         x = x0.clone()
@@ -200,7 +212,7 @@ def packed_case(torch, taco, synth, name: str, block: int, steps: int, warmup: i
     x0 = torch.from_numpy(synth.generate(r).view(np.int16)).cuda().view(torch.bfloat16)
     nbytes = taco.taco_packed_bytes(r.rows, r.cols, block)
     per_set = 2 * n + nbytes + 2 * n
-    nsets = max(1, -(-ROTATE_BYTES // per_set))
+    nsets = rotation_sets(nbytes, per_set)
     sets = [(x0.clone(), torch.empty(nbytes, dtype=torch.uint8, device="cuda"),
              torch.empty((r.rows, r.cols), dtype=torch.bfloat16, device="cuda")) for _ in range(nsets)]
     del x0
@@ -246,7 +258,7 @@ def fidelity_case(torch, taco, synth, name: str, block: int, steps: int, warmup:
     r = synth.WORKLOADS[name]
     n = r.numel
     x0 = torch.from_numpy(synth.generate(r).view(np.int16)).cuda().view(torch.bfloat16)
-    nsets = max(1, -(-ROTATE_BYTES // (2 * n)))
+    nsets = rotation_sets(2 * n, 2 * n)
     sets = [(x0.clone(), torch.empty(taco.FIDELITY_SUMS_BYTES, dtype=torch.uint8, device="cuda"))
             for _ in range(nsets)]
     del x0
