@@ -593,6 +593,130 @@ __global__ __launch_bounds__(kGroup) void compress_kernel(
     }
 }
 
+// Compress into the interleaved layout, staged through LDS.  A record is
+// B + 8 bytes, so a wave-step's 8 records are not a whole number of 128-byte
+// lines and its code stores would straddle lines.  Here each wave assembles
+// R = 16 consecutive records (16 (B + 8) bytes: always a multiple of 128,
+// since B / 8 + 1 is odd) in its own LDS region and writes them with
+// 16-byte stores, each store instruction covering whole lines.  The
+// arithmetic is compress_kernel's, step for step.
+template <int B, Fmt F>
+__global__ __launch_bounds__(kGroup) void compress_packed_kernel(
+    const uint16_t *__restrict__ x, int64_t nblocks, float tau, uint8_t *__restrict__ payload) {
+    using G = Geo<B>;
+    using C = Codec<F>;
+    constexpr int kRec = B + 8;                 // bytes per record
+    constexpr int R = 16;                       // records per unit
+    constexpr int S = R / G::BPW;               // wave-steps per unit (1 or 2)
+    constexpr int kUnit = R * kRec;             // bytes per unit
+    static_assert(kUnit % 128 == 0 && R % G::BPW == 0, "unit layout");
+    __shared__ __align__(16) uint8_t stage_all[kWavesPerGroup][kUnit];
+
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int t = lane_sub<G::LPB>(lane);
+    const int g = lane_slot<G::LPB>(lane);
+    const float sg1 = (lane & 1) ? -1.0f : 1.0f;
+    const float sg2 = (lane & 2) ? -1.0f : 1.0f;
+    const float sg8 = (lane & 8) ? -1.0f : 1.0f;
+    const float lane_sign = (__popc(t) & 1) ? -1.0f : 1.0f;
+    constexpr float kScaleFactor = (float)(inv_sqrt(B) / (double)C::kQmax);
+    constexpr float kInvB = 1.0f / (float)B;
+    uint8_t *stage = stage_all[wave];
+
+    const int64_t nsteps = (nblocks + G::BPW - 1) / G::BPW;
+    const int64_t nunits = (nblocks + R - 1) / R;
+    const int64_t unit0 = (int64_t)blockIdx.x * kWavesPerGroup + wave;
+    const int64_t nunits_grid = (int64_t)gridDim.x * kWavesPerGroup;
+
+    // As in compress_kernel: slots past the last block re-read it.
+    auto lane_offset = [&](int64_t step) -> uint32_t {
+        const int64_t left = nblocks - step * G::BPW;
+        const int gl = (left >= G::BPW || g < left) ? g : (int)left - 1;
+        return (uint32_t)(gl * B + 8 * t);
+    };
+    u4v buf[G::CH];
+    auto load = [&](int64_t step) {
+        const uint16_t *p = x + step * (G::BPW * B) + lane_offset(step);
+#pragma unroll
+        for (int k = 0; k < G::CH; ++k) buf[k] = ld16(p + k * G::SPAN);
+    };
+
+    for (int64_t unit = unit0; unit < nunits; unit += nunits_grid) {
+        const int64_t step0 = unit * S;
+        load(step0);
+#pragma unroll
+        for (int h = 0; h < S; ++h) {
+            const int64_t step = step0 + h;
+            if (step >= nsteps) break;                       // wave-uniform
+            float v[G::EPL];
+#pragma unroll
+            for (int k = 0; k < G::CH; ++k) unpack8(buf[k], &v[8 * k]);
+#if TACO_DOT2_ENERGY
+            float energy = energy_packed<G::CH>(buf);
+#else
+            float energy = sum_squares<G::EPL>(v);
+#endif
+            pin_values(v);
+            asm volatile("" : "+v"(energy));
+            if (h + 1 < S && step + 1 < nsteps) load(step + 1);
+
+            const int64_t blk = step * G::BPW + g;
+            energy = block_sum<G::LPB>(energy);
+            float unshift = 1.0f;
+            if (__builtin_expect(energy >= kBigEnergy, 0)) {
+                const uint16_t *p = x + step * (G::BPW * B) + lane_offset(step);
+#pragma unroll
+                for (int k = 0; k < G::CH; ++k) unpack8(ld16(p + k * G::SPAN), &v[8 * k]);
+#pragma unroll
+                for (int i = 0; i < G::EPL; ++i) v[i] *= kBigShift;
+                energy = block_sum<G::LPB>(sum_squares<G::EPL>(v));
+                unshift = kBigUnshift;
+            }
+            const float a = tau * __builtin_amdgcn_rsqf(energy * kInvB + TACO_EPS);
+            fwht_block<G::LPB, G::EPL>(v, sg1, sg2, sg8);
+            float m = block_max<G::LPB>(max_abs<G::EPL>(v));
+            const float s = a * m * kScaleFactor;
+            if (__builtin_expect(m < kTinyMax && m > 0.0f, 0)) {
+#pragma unroll
+                for (int i = 0; i < G::EPL; ++i) v[i] *= kTinyShift;
+                m *= kTinyShift;
+            }
+            Quot r = quotient(C::kQmax, m);
+            r.hi = (m > 0.0f) ? r.hi * lane_sign : 0.0f;
+            r.lo = (m > 0.0f) ? r.lo * lane_sign : 0.0f;
+
+            if (blk < nblocks) {
+                uint8_t *rec = stage + (h * G::BPW + g) * kRec;
+#pragma unroll
+                for (int k = 0; k < G::CH; ++k)
+                    *reinterpret_cast<u2v *>(rec + 8 * t + k * G::SPAN) = encode8<F>(&v[8 * k], r);
+                if (t == 0) {
+                    const f2v as = {a * unshift, s};
+                    *reinterpret_cast<f2v *>(rec + B) = as;
+                }
+            }
+        }
+        // The unit's records are in LDS: write its valid bytes out.
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        const int64_t left = nblocks - unit * R;
+        const int bytes = (int)(left < R ? left : R) * kRec;      // a multiple of 8
+        uint8_t *dst = payload + unit * kUnit;
+        for (int off = 16 * lane; off < bytes; off += 16 * kWave) {
+            if (off + 16 <= bytes)
+                st16(dst + off, *reinterpret_cast<const u4v *>(stage + off));
+            else
+                st8(dst + off, *reinterpret_cast<const u2v *>(stage + off));
+        }
+        // Every lane has read its part of the stage before it is rewritten.
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
+}
+
 // --------------------------------------------------------- decompress -----
 
 template <int B, Fmt F, Out MODE, Layout L>
@@ -1261,12 +1385,22 @@ unsigned codec_grid(int64_t n) {
 // ------------------------------------------------- per-format entry -------
 
 template <Fmt F>
+struct CompressPackedLaunch {
+    const uint16_t *x; int64_t m; float tau; uint8_t *payload; hipStream_t stream;
+    template <int B> taco_status run() const {
+        // One unit of 16 records per wave.
+        const int64_t nunits = (m + 15) / 16;
+        return launch(reinterpret_cast<const void *>(&compress_packed_kernel<B, F>),
+                      grid_for(nunits), stream, x, m, tau, payload);
+    }
+};
+
+template <Fmt F>
 taco_status Ops<F>::compress(Layout layout, int32_t block, const uint16_t *x, int64_t nblocks,
                              float tau, uint8_t *codes, float *alpha, float *scale,
                              hipStream_t stream) {
-    if (layout == Layout::kPacked)
-        return for_block(block, CompressLaunch<F, Layout::kPacked>{x, nblocks, tau, codes, alpha,
-                                                                    scale, stream});
+    if (layout == Layout::kPacked)   // codes = the payload; alpha / scale point into it
+        return for_block(block, CompressPackedLaunch<F>{x, nblocks, tau, codes, stream});
     return for_block(block, CompressLaunch<F, Layout::kSide>{x, nblocks, tau, codes, alpha, scale,
                                                               stream});
 }
