@@ -71,6 +71,7 @@ def _load():
                                                     P, P, P]
         lib.taco_oracle_roundtrip_variant.argtypes = [P, i64, i32, i32, i32, f64, f64, P]
         lib.taco_oracle_fidelity.argtypes = [P, P, i64, P]
+        lib.taco_oracle_decompress_accumulate_n.argtypes = [i32, P, P, P, i64, i32, i32, P]
         lib.taco_oracle_qmax.argtypes = [i32]
         lib.taco_oracle_qmax.restype = f64
         lib.taco_oracle_encode_array.argtypes = [i32, P, i64, P]
@@ -292,6 +293,28 @@ def decompress_accumulate(codes, alpha, scale, block: int, acc: np.ndarray,
     assert acc.dtype == np.float32 and acc.flags["C_CONTIGUOUS"] and acc.size == c.size
     _check(lib.taco_oracle_decompress_accumulate(_ptr(c), _ptr(a), _ptr(s), c.size, block,
                                                  _fmt(fmt), _ptr(acc)))
+    return acc
+
+
+def decompress_accumulate_n(payloads, block: int, acc: np.ndarray, fmt: str = "e4m3") -> np.ndarray:
+    """acc (float32, updated in place and returned) += the sum of the payloads'
+    reconstructions, summed in double and rounded once.  payloads: list of
+    (codes, alpha, scale)."""
+    lib = _load()
+    pay = [(np.ascontiguousarray(c, dtype=np.uint8), np.ascontiguousarray(a, dtype=np.float32),
+            np.ascontiguousarray(s, dtype=np.float32)) for c, a, s in payloads]
+    assert acc.dtype == np.float32 and acc.flags["C_CONTIGUOUS"]
+    n = acc.size
+    for c, a, s in pay:
+        assert c.size == n and a.size == n // block and s.size == n // block
+    arr = ctypes.c_void_p * max(1, len(pay))
+    cp = arr(*[c.ctypes.data for c, _, _ in pay])
+    ap = arr(*[a.ctypes.data for _, a, _ in pay])
+    sp = arr(*[s.ctypes.data for _, _, s in pay])
+    _check(lib.taco_oracle_decompress_accumulate_n(len(pay), ctypes.cast(cp, ctypes.c_void_p),
+                                                   ctypes.cast(ap, ctypes.c_void_p),
+                                                   ctypes.cast(sp, ctypes.c_void_p), n, block,
+                                                   _fmt(fmt), _ptr(acc)))
     return acc
 
 

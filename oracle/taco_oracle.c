@@ -443,6 +443,35 @@ int taco_oracle_decompress_accumulate(const uint8_t *codes, const float *alpha,
     return 0;
 }
 
+/*
+ * Several payloads at once (the local reduction of section 4.4.2 over P
+ * received payloads): acc += float32(sum_p G'_p), the payloads' exact
+ * reconstructions summed in double, rounded once to float32 and added with
+ * one float32 addition.  With one payload this is
+ * taco_oracle_decompress_accumulate.
+ */
+int taco_oracle_decompress_accumulate_n(int npay, const uint8_t *const *codes_in,
+                                        const float *const *alpha_in,
+                                        const float *const *scale_in, int64_t n, int B,
+                                        int fmt, float *acc)
+{
+    if (!valid_block(B) || !valid_fmt(fmt) || n < 0 || n % B || npay < 0) return -1;
+    double g[ORACLE_MAX_BLOCK], sum[ORACLE_MAX_BLOCK];
+    for (int64_t k = 0; k < n / B; ++k) {
+        for (int j = 0; j < B; ++j) sum[j] = 0.0;
+        for (int p = 0; p < npay; ++p) {
+            reconstruct_block(codes_in[p] + k * B, alpha_in[p][k], scale_in[p][k], B, fmt, g);
+            for (int j = 0; j < B; ++j) sum[j] += g[j];
+        }
+        if (npay == 0) continue;
+        for (int j = 0; j < B; ++j) {
+            float gf = (float)sum[j];
+            acc[k * B + j] = acc[k * B + j] + gf;
+        }
+    }
+    return 0;
+}
+
 /* ------------------------------------------------------------------------ */
 /* Owner step of the two-shot all-reduce ([TACO] section 4.4.2)              */
 /* ------------------------------------------------------------------------ */

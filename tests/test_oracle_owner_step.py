@@ -6,13 +6,17 @@ all-gather), built from Eq. 11-13, a sum, and Eq. 5-10.
 Pinned against: its two degenerate cases (no payloads; no own partial),
 which reduce to the already-pinned compress; closed forms for blocks whose
 payloads reconstruct exactly (constant blocks, spikes plus Walsh rows); and
-invariance under reordering the payloads.
+invariance under reordering the payloads.  The multi-payload accumulate
+(the same local reduction into a float32 accumulator) is pinned by its one-
+and zero-payload cases and by the exactly rounded sum of reconstructions.
 """
 import math
 
 import numpy as np
 import pytest
 from scipy.linalg import hadamard
+
+import synth
 
 EPS = 1e-20
 QMAX = 448.0
@@ -91,3 +95,45 @@ def test_payload_order_does_not_matter(oracle_mod, workload_blocks):
     assert np.count_nonzero(c1 != c2) <= 2          # double rounding order only
     np.testing.assert_allclose(a1, a2, rtol=1e-12)
     np.testing.assert_allclose(s1, s2, rtol=1e-12)
+
+
+# ------------------------------------------- several payloads at once ----
+
+def _payloads(oracle_mod, P, B, fmt="e4m3", seed=90):
+    r = synth.WORKLOADS["laplace_2048x1024"].with_shape(3, 1024, seed=seed)
+    return [oracle_mod.compress(synth.generate(r, seed=seed + p), B, fmt=fmt) for p in range(P)]
+
+
+@pytest.mark.parametrize("fmt", ["e4m3", "int8"])
+def test_accumulate_n_of_one_payload_is_accumulate(oracle_mod, fmt):
+    pay = _payloads(oracle_mod, 1, 128, fmt)
+    acc0 = synth.bits_to_f32(synth.generate(synth.WORKLOADS["laplace_2048x1024"].with_shape(3, 1024, seed=7)))
+    acc0 = acc0.astype(np.float32).reshape(-1)
+    a = oracle_mod.decompress_accumulate_n(pay, 128, acc0.copy(), fmt)
+    b = oracle_mod.decompress_accumulate(*pay[0], 128, acc0.copy(), fmt=fmt)
+    assert np.array_equal(a, b)
+
+
+def test_accumulate_n_of_nothing_is_a_no_op(oracle_mod):
+    acc = np.arange(3 * 1024, dtype=np.float32)
+    out = oracle_mod.decompress_accumulate_n([], 128, acc.copy())
+    assert np.array_equal(out, acc)
+
+
+def test_accumulate_n_is_the_rounded_exact_sum(oracle_mod):
+    """The payloads' exact reconstructions, summed, rounded once: a payload
+    repeated twice adds exactly twice its reconstruction (x2 is exact), and
+    several payloads agree with sequential accumulation to float32 rounding."""
+    pay = _payloads(oracle_mod, 3, 256)
+    g = [oracle_mod.reconstruct_f64(*p, 256) for p in pay]
+    zero = np.zeros(3 * 1024, np.float32)
+    twice = oracle_mod.decompress_accumulate_n([pay[0], pay[0]], 256, zero.copy())
+    assert np.array_equal(twice, (2.0 * g[0]).astype(np.float32).reshape(-1))
+    fused = oracle_mod.decompress_accumulate_n(pay, 256, zero.copy())
+    want = (g[0] + g[1] + g[2]).astype(np.float32).reshape(-1)
+    assert np.array_equal(fused, want)
+    seq = zero.copy()
+    for p in pay:
+        oracle_mod.decompress_accumulate(*p, 256, seq)
+    scale = np.abs(g[0]) + np.abs(g[1]) + np.abs(g[2])
+    assert np.all(np.abs(seq - fused) <= 4 * 2.0 ** -24 * scale.reshape(-1) + 1e-45)
