@@ -472,10 +472,12 @@ constexpr double inv_sqrt(int b) {
 // Blocks whose energy reaches this are rescaled by 2^-64 before squaring so
 // that sum x^2 stays finite for every bf16 input.  (kBigMax: the same for a
 // block maximum, before a plain rotation.)
+// With 2^-80, sum (x 2^-80)^2 <= 512 (2^128 2^-80)^2 = 2^105 for any bf16 x.
 constexpr float kBigEnergy = 0x1p100f;
 constexpr float kBigMax = 0x1p100f;
-constexpr float kBigShift = 0x1p-64f;
-constexpr float kBigUnshift = 0x1p-64f;   // alpha of the original block = alpha' * 2^-64
+constexpr float kBigShift = 0x1p-80f;
+constexpr float kBigShiftInv = 0x1p80f;
+constexpr float kBigUnshift = 0x1p-80f;   // alpha of the original block = alpha' * 2^-80
 // Blocks with max|R| below this get R and max|R| scaled by 2^64 before
 // Q / max|R| is formed, so that the quotient cannot overflow.
 constexpr float kTinyMax = 0x1p-96f;
@@ -553,7 +555,7 @@ __global__ __launch_bounds__(kGroup) void compress_kernel(
         float unshift = 1.0f;
         if (__builtin_expect(energy >= kBigEnergy, 0)) {
             // Huge block (sum x^2 near or past float32 range): reload it and
-            // work on x * 2^-64 (exact), undoing the factor in alpha.
+            // work on x * 2^-80 (exact), undoing the factor in alpha.
             const uint16_t *p = x + step * (G::BPW * B) + lane_offset(step);
 #pragma unroll
             for (int k = 0; k < G::CH; ++k) unpack8(ld16(p + k * G::SPAN), &v[8 * k]);
@@ -883,46 +885,64 @@ __global__ __launch_bounds__(kGroup) void reduce_compress_kernel(
 #pragma unroll
             for (int i = 0; i < G::EPL; ++i) v[i] = 0.0f;
         }
+        // v += sum_p c_p decode(q_p), c_p = sqrt(B) s_p / alpha_p times
+        // `shift` (with the lane sign of the stored layout) as hi + lo,
+        // added high part first: each fma then rounds relative to the
+        // running sum, so a payload that nearly cancels own keeps the
+        // precision of the result.
+        auto add_payloads = [&](const u2v (&qp)[P > 0 ? P : 1][G::CH], float shift) {
 #pragma unroll
-        for (int p = 0; p < P; ++p) {
-            // c = sqrt(B) s_p / alpha_p (with the lane sign of the stored
-            // layout) as hi + lo, added high part first: each fma then
-            // rounds relative to the running sum, so a payload that nearly
-            // cancels own keeps the precision of the result.
-            Quot sa = {0.0f, 0.0f};
-            if (ws[p] > 0.0f)   // (a subnormal alpha would overflow the reciprocal)
-                sa = wa[p] >= 0x1p-120f ? quotient(ws[p], wa[p]) : Quot{ws[p] / wa[p], 0.0f};
-            const float ch = kSqrtBHi * sa.hi;
-            const float cl = fmaf(kSqrtBHi, sa.hi, -ch) + fmaf(kSqrtBHi, sa.lo, kSqrtBLo * sa.hi);
-            const float chs = ch * lane_sign, cls = cl * lane_sign;
-            float d[G::EPL];
+            for (int p = 0; p < P; ++p) {
+                Quot sa = {0.0f, 0.0f};
+                if (ws[p] > 0.0f)   // (a subnormal alpha would overflow the reciprocal)
+                    sa = wa[p] >= 0x1p-120f ? quotient(ws[p], wa[p]) : Quot{ws[p] / wa[p], 0.0f};
+                const float sh = kSqrtBHi * shift, sl = kSqrtBLo * shift;   // exact scalings
+                const float ch = sh * sa.hi;
+                const float cl = fmaf(sh, sa.hi, -ch) + fmaf(sh, sa.lo, sl * sa.hi);
+                const float chs = ch * lane_sign, cls = cl * lane_sign;
+                float d[G::EPL];
 #pragma unroll
-            for (int k = 0; k < G::CH; ++k) C::decode8(qc[p][k], &d[8 * k]);
+                for (int k = 0; k < G::CH; ++k) C::decode8(qp[p][k], &d[8 * k]);
 #pragma unroll
-            for (int i = 0; i < G::EPL; ++i) v[i] = fmaf(d[i], cls, fmaf(d[i], chs, v[i]));
-        }
-
-        // Eq. 6 via Parseval.
-        float e0 = 0.0f, e1 = 0.0f;
-#pragma unroll
-        for (int i = 0; i < G::EPL; i += 2) {
-            e0 = fmaf(v[i], v[i], e0);
-            e1 = fmaf(v[i + 1], v[i + 1], e1);
-        }
-        float energy = block_sum<G::LPB>(e0 + e1);
-        float unshift = 1.0f;
-        if (__builtin_expect(energy >= kBigEnergy, 0)) {
-            // Work on (H X) * 2^-64 (exact), undoing the factor in alpha.
-            e0 = 0.0f;
-            e1 = 0.0f;
+                for (int i = 0; i < G::EPL; ++i) v[i] = fmaf(d[i], cls, fmaf(d[i], chs, v[i]));
+            }
+        };
+        auto energy_of_v = [&]() {
+            float e0 = 0.0f, e1 = 0.0f;
 #pragma unroll
             for (int i = 0; i < G::EPL; i += 2) {
-                v[i] *= kBigShift;
-                v[i + 1] *= kBigShift;
                 e0 = fmaf(v[i], v[i], e0);
                 e1 = fmaf(v[i + 1], v[i + 1], e1);
             }
-            energy = block_sum<G::LPB>(e0 + e1);
+            return block_sum<G::LPB>(e0 + e1);
+        };
+        add_payloads(qc, 1.0f);
+
+        // Eq. 6 via Parseval.
+        float energy = energy_of_v();
+        float unshift = 1.0f;
+        if (__builtin_expect(!(energy < kBigEnergy), 0)) {
+            // Huge block (its energy, or H X itself, may have left float32
+            // range): rebuild H X from the inputs scaled by 2^-80 (exact),
+            // undoing the factor in alpha.
+            if (has_own) {
+#pragma unroll
+                for (int k = 0; k < G::CH; ++k)
+                    unpack8(ld16(own + base + off + k * G::SPAN), &v[8 * k]);
+#pragma unroll
+                for (int i = 0; i < G::EPL; ++i) v[i] *= kBigShift;
+                fwht_block<G::LPB, G::EPL>(v, sg1, sg2, sg8);
+            } else {
+#pragma unroll
+                for (int i = 0; i < G::EPL; ++i) v[i] = 0.0f;
+            }
+            u2v qr[P > 0 ? P : 1][G::CH];
+#pragma unroll
+            for (int p = 0; p < P; ++p)
+#pragma unroll
+                for (int k = 0; k < G::CH; ++k) qr[p][k] = ld8(pay.codes[p] + cbase + coff + k * G::SPAN);
+            add_payloads(qr, kBigShift);
+            energy = energy_of_v();
             unshift = kBigUnshift;
         }
         // Eq. 7.
@@ -1151,13 +1171,13 @@ __global__ __launch_bounds__(kGroup) void roundtrip_kernel(
             }
         } else if (V == Variant::kHadamard) {
             // Blocks whose rotated values could overflow float32 are rotated
-            // as x 2^-64 (exact); the codes of Z = 2^64 R' / sqrt(B) then
+            // as x 2^-80 (exact); the codes of Z = 2^80 R' / sqrt(B) then
             // saturate as Z's would.
             float zf = kInvSqrtB * lane_sign;
             if (__builtin_expect(block_max<G::LPB>(max_abs<G::EPL>(v)) >= kBigMax, 0)) {
 #pragma unroll
                 for (int i = 0; i < G::EPL; ++i) v[i] *= kBigShift;
-                zf *= kTinyShift;
+                zf *= kBigShiftInv;
             }
             fwht_block<G::LPB, G::EPL>(v, sg1, sg2, sg8);
             rotate_back = true;
@@ -1171,6 +1191,12 @@ __global__ __launch_bounds__(kGroup) void roundtrip_kernel(
             // DS (block max) or TENSOR (tensor max): codes of x Q / m, x' = decode * (m / Q).
             float m = (V == Variant::kDs) ? block_max<G::LPB>(max_abs<G::EPL>(v)) : tmax;
             const float s = m / C::kQmax;
+            // quotient() needs Q / m and 1 / m in the normal range.
+            if (__builtin_expect(m >= kBigMax, 0)) {
+#pragma unroll
+                for (int i = 0; i < G::EPL; ++i) v[i] *= kBigShift;
+                m *= kBigShift;
+            }
             if (__builtin_expect(m < kTinyMax && m > 0.0f, 0)) {
 #pragma unroll
                 for (int i = 0; i < G::EPL; ++i) v[i] *= kTinyShift;

@@ -70,7 +70,7 @@ def test_without_own_partial(taco, B):
 def test_cancelling_and_special_sums(taco):
     """own = x and a payload compressed from -x leave only the quantisation
     error; constant blocks sum exactly; huge values exercise the rescaled
-    energy branch."""
+    energy branch, up to the top of the bf16 range."""
     B = 128
     rng = np.random.default_rng(3)
     x = synth.f32_to_bits(rng.laplace(0, 0.02, 16 * B))
@@ -83,6 +83,11 @@ def test_cancelling_and_special_sums(taco):
     run_case(taco, huge, [huge], B)
     zero = np.zeros(16 * B, np.uint16)
     run_case(taco, zero, [x], B)
+    # Top of the bf16 range, where H X (B |X|) leaves float32 range.
+    for b in (128, 512):
+        top = synth.f32_to_bits(np.clip(rng.standard_normal(16 * b) * 5e37, -2.5e38, 2.5e38))
+        run_case(taco, top, [top], b)
+        run_case(taco, None, [top, top], b)
 
 
 def test_tau_scales_alpha_and_s(taco):

@@ -193,6 +193,9 @@ def special_blocks(B):
     pm = np.zeros(B, np.float32); pm[0:B // 2:2] = -0.0; pm[B // 2:] = 0.75
     rows.append(f(pm))                                                 # signed zeros in Z
     ties = np.full(B, 1.0); ties[0] = 448.0 / 17 * 16; rows.append(f(ties))
+    # Top of the bf16 range: sum x^2 and B |x| overflow float32.
+    rows.append(f(np.full(B, 3.0e38)))
+    top = np.clip(rng.standard_normal(B) * 5e37, -2.5e38, 2.5e38); rows.append(f(top))
     return np.stack(rows)
 
 
