@@ -108,6 +108,13 @@ _lib.taco_decompress_packed_fmt.argtypes = [_P, _I64, _I64, _I32, _I32, _P, _P]
 _lib.taco_decompress_accumulate_packed_fmt.argtypes = [_P, _I64, _I64, _I32, _I32, _P, _P]
 _lib.taco_reduce_compress_packed_fmt.argtypes = [_P, _I32, _P, _I64, _I64, _I32, _F32, _I32,
                                                  _P, _P]
+_lib.taco_decompress_accumulate_n.argtypes = [_I32, _P, _P, _P, _I64, _I64, _I32, _P, _P]
+_lib.taco_decompress_accumulate_n_fmt.argtypes = [_I32, _P, _P, _P, _I64, _I64, _I32, _I32, _P, _P]
+_lib.taco_decompress_accumulate_n_packed.argtypes = [_I32, _P, _I64, _I64, _I32, _P, _P]
+_lib.taco_decompress_accumulate_n_packed_fmt.argtypes = [_I32, _P, _I64, _I64, _I32, _I32, _P, _P]
+for _name in ("decompress_accumulate_n", "decompress_accumulate_n_fmt",
+              "decompress_accumulate_n_packed", "decompress_accumulate_n_packed_fmt"):
+    getattr(_lib, "taco_" + _name).restype = ctypes.c_int
 _lib.taco_roundtrip.argtypes = [_P, _I64, _I64, _I32, _F32, _I32, _I32, _P, _P, _P]
 _lib.taco_roundtrip.restype = ctypes.c_int
 _lib.taco_encode.argtypes = [_I32, _P, _I64, _P, _P]
@@ -129,7 +136,9 @@ EXPORTS = ("taco_num_blocks", "taco_compress", "taco_decompress",
            "taco_decompress_accumulate_fmt", "taco_reduce_compress_fmt",
            "taco_compress_packed_fmt", "taco_decompress_packed_fmt",
            "taco_decompress_accumulate_packed_fmt", "taco_reduce_compress_packed_fmt",
-           "taco_encode", "taco_decode", "taco_roundtrip")
+           "taco_encode", "taco_decode", "taco_roundtrip", "taco_decompress_accumulate_n",
+           "taco_decompress_accumulate_n_fmt", "taco_decompress_accumulate_n_packed",
+           "taco_decompress_accumulate_n_packed_fmt")
 
 #: Most payloads one taco_reduce_compress call sums.
 MAX_PAYLOADS = 8
@@ -267,6 +276,36 @@ def taco_encode(format: int, x: int, n: int, codes: int, stream: int) -> int:
 
 def taco_decode(format: int, codes: int, n: int, out: int, stream: int) -> int:
     return _lib.taco_decode(format, codes, n, out, stream)
+
+
+def _arr(ptrs):
+    return None if ptrs is None else ctypes.cast(_ptr_array(ptrs), ctypes.c_void_p)
+
+
+def taco_decompress_accumulate_n(npayloads: int, codes_e4m3, alpha, scale, tokens: int,
+                                 hidden: int, block: int, acc_f32: int, stream: int) -> int:
+    return _lib.taco_decompress_accumulate_n(npayloads, _arr(codes_e4m3), _arr(alpha),
+                                             _arr(scale), tokens, hidden, block, acc_f32, stream)
+
+
+def taco_decompress_accumulate_n_fmt(npayloads: int, codes, alpha, scale, tokens: int,
+                                     hidden: int, block: int, format: int, acc_f32: int,
+                                     stream: int) -> int:
+    return _lib.taco_decompress_accumulate_n_fmt(npayloads, _arr(codes), _arr(alpha), _arr(scale),
+                                                 tokens, hidden, block, format, acc_f32, stream)
+
+
+def taco_decompress_accumulate_n_packed(npayloads: int, payloads, tokens: int, hidden: int,
+                                        block: int, acc_f32: int, stream: int) -> int:
+    return _lib.taco_decompress_accumulate_n_packed(npayloads, _arr(payloads), tokens, hidden,
+                                                    block, acc_f32, stream)
+
+
+def taco_decompress_accumulate_n_packed_fmt(npayloads: int, payloads, tokens: int, hidden: int,
+                                            block: int, format: int, acc_f32: int,
+                                            stream: int) -> int:
+    return _lib.taco_decompress_accumulate_n_packed_fmt(npayloads, _arr(payloads), tokens, hidden,
+                                                        block, format, acc_f32, stream)
 
 
 def taco_roundtrip(x_bf16: int, tokens: int, hidden: int, block: int, target_energy: float,
@@ -672,3 +711,53 @@ def fidelity_metrics(sums, n: int) -> dict:
             "max_err": me, "mse": se / n if n else 0.0,
             "sum_sq_err": se, "sum_sq_ref": sr, "sum_sq_out": so, "sum_dot": sd,
             "tensor_absmax": tm}
+
+
+def decompress_accumulate_n(payloads, acc, block: int = 256, stream=None, fmt: str = "e4m3"):
+    """acc (float32) += the sum of the payloads' reconstructions, in one pass.
+    payloads: list of (codes, alpha, scale) as returned by compress()."""
+    torch = _torch()
+    f = _format(fmt)
+    _need(acc, torch.float32, "acc")
+    tokens, hidden = _shape2(acc)
+    m = taco_num_blocks(tokens, hidden, block)
+    for c, a, s in payloads:
+        _need(c, torch.uint8, "payload codes")
+        _need(a, torch.float32, "payload alpha")
+        _need(s, torch.float32, "payload scale")
+        if c.numel() != acc.numel() or (m >= 0 and (a.numel() < m or s.numel() < m)):
+            raise ValueError("every payload must match acc's shape")
+    n = len(payloads)
+    args = (n, [c.data_ptr() for c, _, _ in payloads] if n else None,
+            [a.data_ptr() for _, a, _ in payloads] if n else None,
+            [s.data_ptr() for _, _, s in payloads] if n else None, tokens, hidden, block)
+    if fmt == "e4m3":
+        st = taco_decompress_accumulate_n(*args, acc.data_ptr(), _stream(stream))
+    else:
+        st = taco_decompress_accumulate_n_fmt(*args, f, acc.data_ptr(), _stream(stream))
+    _check(st, "taco_decompress_accumulate_n")
+    return acc
+
+
+def decompress_accumulate_n_packed(payloads, acc, block: int = 256, stream=None,
+                                   fmt: str = "e4m3"):
+    """acc (float32) += the sum of interleaved payloads' reconstructions."""
+    torch = _torch()
+    f = _format(fmt)
+    _need(acc, torch.float32, "acc")
+    tokens, hidden = _shape2(acc)
+    nb = _packed_len(tokens, hidden, block)
+    for p in payloads:
+        _need(p, torch.uint8, "payload")
+        if p.numel() < nb:
+            raise ValueError("payload is too small for acc's shape")
+    n = len(payloads)
+    ptrs = [p.data_ptr() for p in payloads] if n else None
+    if fmt == "e4m3":
+        st = taco_decompress_accumulate_n_packed(n, ptrs, tokens, hidden, block, acc.data_ptr(),
+                                                 _stream(stream))
+    else:
+        st = taco_decompress_accumulate_n_packed_fmt(n, ptrs, tokens, hidden, block, f,
+                                                     acc.data_ptr(), _stream(stream))
+    _check(st, "taco_decompress_accumulate_n_packed")
+    return acc

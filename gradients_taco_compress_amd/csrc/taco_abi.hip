@@ -269,6 +269,30 @@ taco_status reduce_packed(const uint16_t *own, int32_t npayloads, const uint8_t 
     });
 }
 
+taco_status accumulate_n_any(int32_t npayloads, const uint8_t *const *codes,
+                             const float *const *alpha, const float *const *scale, bool packed,
+                             int64_t tokens, int64_t hidden, int32_t block, taco_format format,
+                             float *acc, hipStream_t stream) {
+    if (!valid_format(format)) return TACO_ERR_FORMAT;
+    int64_t n = 0;
+    taco_status st = check_shape(tokens, hidden, block, &n);
+    if (st != TACO_OK) return st;
+    if (npayloads < 0 || npayloads > TACO_MAX_PAYLOADS) return TACO_ERR_PARAM;
+    if (n == 0 || npayloads == 0) return TACO_OK;
+    if (!acc) return TACO_ERR_NULL;
+    if (!codes || (!packed && (!alpha || !scale))) return TACO_ERR_NULL;
+    if (!aligned(acc, 16)) return TACO_ERR_ALIGN;
+    const void *outs[1] = {acc};
+    const size_t out_len[1] = {(size_t)n * sizeof(float)};
+    Payloads pay = {};
+    st = check_payloads(npayloads, codes, alpha, scale, n, block, packed, outs, out_len, 1, &pay);
+    if (st != TACO_OK) return st;
+    const Layout layout = packed ? Layout::kPacked : Layout::kSide;
+    return with_format(format, [&](auto ops) {
+        return decltype(ops)::accumulate_n(layout, block, npayloads, pay, n / block, acc, stream);
+    });
+}
+
 taco_status encode_any(taco_format format, const float *x, int64_t n, uint8_t *codes,
                        hipStream_t stream) {
     if (!valid_format(format)) return TACO_ERR_FORMAT;
@@ -449,6 +473,39 @@ taco_status taco_reduce_compress_packed_fmt(const uint16_t *own_bf16, int32_t np
                                             hipStream_t stream) {
     return reduce_packed(own_bf16, npayloads, payloads, tokens, hidden, block, target_energy,
                          format, out_payload, stream);
+}
+
+taco_status taco_decompress_accumulate_n(int32_t npayloads, const uint8_t *const *codes_e4m3,
+                                         const float *const *alpha, const float *const *scale,
+                                         int64_t tokens, int64_t hidden, int32_t block,
+                                         float *acc_f32, hipStream_t stream) {
+    return accumulate_n_any(npayloads, codes_e4m3, alpha, scale, false, tokens, hidden, block,
+                            TACO_FORMAT_E4M3, acc_f32, stream);
+}
+
+taco_status taco_decompress_accumulate_n_fmt(int32_t npayloads, const uint8_t *const *codes,
+                                             const float *const *alpha, const float *const *scale,
+                                             int64_t tokens, int64_t hidden, int32_t block,
+                                             taco_format format, float *acc_f32,
+                                             hipStream_t stream) {
+    return accumulate_n_any(npayloads, codes, alpha, scale, false, tokens, hidden, block, format,
+                            acc_f32, stream);
+}
+
+taco_status taco_decompress_accumulate_n_packed(int32_t npayloads, const uint8_t *const *payloads,
+                                                int64_t tokens, int64_t hidden, int32_t block,
+                                                float *acc_f32, hipStream_t stream) {
+    return accumulate_n_any(npayloads, payloads, nullptr, nullptr, true, tokens, hidden, block,
+                            TACO_FORMAT_E4M3, acc_f32, stream);
+}
+
+taco_status taco_decompress_accumulate_n_packed_fmt(int32_t npayloads,
+                                                    const uint8_t *const *payloads, int64_t tokens,
+                                                    int64_t hidden, int32_t block,
+                                                    taco_format format, float *acc_f32,
+                                                    hipStream_t stream) {
+    return accumulate_n_any(npayloads, payloads, nullptr, nullptr, true, tokens, hidden, block,
+                            format, acc_f32, stream);
 }
 
 taco_status taco_e4m3_encode(const float *x, int64_t n, uint8_t *codes, hipStream_t stream) {

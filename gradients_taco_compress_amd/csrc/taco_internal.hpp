@@ -47,6 +47,9 @@ struct Ops {
                                        const uint16_t *own, const Payloads &pay, int64_t nblocks,
                                        float tau, uint8_t *codes, float *alpha, float *scale,
                                        hipStream_t stream);
+    // acc += the sum of npay (1..8) payloads' reconstructions.
+    static taco_status accumulate_n(Layout layout, int32_t block, int npay, const Payloads &pay,
+                                    int64_t nblocks, float *acc, hipStream_t stream);
     // Clears *sums, then (kTensor) finds max|x|, then runs the round trip.
     static taco_status roundtrip(Variant variant, int32_t block, const uint16_t *x,
                                  int64_t nblocks, float tau, uint16_t *y,

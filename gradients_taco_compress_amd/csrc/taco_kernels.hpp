@@ -893,12 +893,17 @@ __global__ __launch_bounds__(kGroup) void reduce_compress_kernel(
         auto add_payloads = [&](const u2v (&qp)[P > 0 ? P : 1][G::CH], float shift) {
 #pragma unroll
             for (int p = 0; p < P; ++p) {
+                // (shift s_p) / alpha_p: the shift is applied before the
+                // division, so that the quotient is not a float32 subnormal
+                // for tiny blocks; a subnormal alpha would overflow the
+                // reciprocal, so it takes a plain division.
                 Quot sa = {0.0f, 0.0f};
-                if (ws[p] > 0.0f)   // (a subnormal alpha would overflow the reciprocal)
-                    sa = wa[p] >= 0x1p-120f ? quotient(ws[p], wa[p]) : Quot{ws[p] / wa[p], 0.0f};
-                const float sh = kSqrtBHi * shift, sl = kSqrtBLo * shift;   // exact scalings
-                const float ch = sh * sa.hi;
-                const float cl = fmaf(sh, sa.hi, -ch) + fmaf(sh, sa.lo, sl * sa.hi);
+                const float sp = ws[p] * shift;
+                if (ws[p] > 0.0f)
+                    sa = wa[p] >= 0x1p-120f ? quotient(sp, wa[p]) : Quot{sp / wa[p], 0.0f};
+                const float ch = kSqrtBHi * sa.hi;
+                const float cl = fmaf(kSqrtBHi, sa.hi, -ch) +
+                                 fmaf(kSqrtBHi, sa.lo, kSqrtBLo * sa.hi);
                 const float chs = ch * lane_sign, cls = cl * lane_sign;
                 float d[G::EPL];
 #pragma unroll
@@ -947,13 +952,32 @@ __global__ __launch_bounds__(kGroup) void reduce_compress_kernel(
         }
         // Eq. 7.
         const float a = tau * __builtin_amdgcn_rsqf(energy * kInvB2 + TACO_EPS);
-        // Eq. 9-10 exactly as in compress_kernel.
+        // Eq. 9-10 as in compress_kernel.
         float m = block_max<G::LPB>(max_abs<G::EPL>(v));
-        const float s = a * m * kScaleFactor;
+        float s = a * m * kScaleFactor;
         if (__builtin_expect(m < kTinyMax && m > 0.0f, 0)) {
+            // Tiny block: its rotated values (and payload factors) are
+            // float32 subnormals, with too few bits for the codes.  Rebuild
+            // H X from the inputs scaled by 2^64 (exact).
+            if (has_own) {
 #pragma unroll
-            for (int i = 0; i < G::EPL; ++i) v[i] *= kTinyShift;
-            m *= kTinyShift;
+                for (int k = 0; k < G::CH; ++k)
+                    unpack8(ld16(own + base + off + k * G::SPAN), &v[8 * k]);
+#pragma unroll
+                for (int i = 0; i < G::EPL; ++i) v[i] *= kTinyShift;
+                fwht_block<G::LPB, G::EPL>(v, sg1, sg2, sg8);
+            } else {
+#pragma unroll
+                for (int i = 0; i < G::EPL; ++i) v[i] = 0.0f;
+            }
+            u2v qr[P > 0 ? P : 1][G::CH];
+#pragma unroll
+            for (int p = 0; p < P; ++p)
+#pragma unroll
+                for (int k = 0; k < G::CH; ++k) qr[p][k] = ld8(pay.codes[p] + cbase + coff + k * G::SPAN);
+            add_payloads(qr, kTinyShift);
+            m = block_max<G::LPB>(max_abs<G::EPL>(v));                // 2^64 max|H X|
+            s = (a * m * kScaleFactor) * kOutUnshift;
         }
         // As in compress_kernel, v holds lane_sign * (H X), so r carries the
         // lane sign too.
@@ -969,6 +993,113 @@ __global__ __launch_bounds__(kGroup) void reduce_compress_kernel(
             if (t == 0) {
                 alpha[blk * W::kScalarStride] = a * unshift;
                 scale[blk * W::kScalarStride] = s;
+            }
+        }
+    }
+}
+
+// Several payloads into one float32 accumulator in one pass (the local
+// reduction of [TACO] section 4.4.2 over P received payloads): acc += sum_p
+// G'_p.  With H H = B I, sum_p G'_p = H (sum_p sqrt(B) (s_p / alpha_p)
+// decode(q_p)) / B: the payloads are summed in the rotated domain and
+// transformed back once, so each element costs P decodes and one inverse
+// transform, and the accumulator is read and written once.
+template <int B, Fmt F, int P, Layout L>
+__global__ __launch_bounds__(kGroup) void accumulate_n_kernel(Payloads pay, int64_t nblocks,
+                                                              float *__restrict__ acc) {
+    using G = Geo<B>;
+    using W = Wire<B, L>;
+    using C = Codec<F>;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int t = lane_sub<G::LPB>(lane);
+    const int g = lane_slot<G::LPB>(lane);
+    const float sg1 = (lane & 1) ? -1.0f : 1.0f;
+    const float sg2 = (lane & 2) ? -1.0f : 1.0f;
+    const float sg8 = (lane & 8) ? -1.0f : 1.0f;
+    const float lane_sign = (__popc(t) & 1) ? -1.0f : 1.0f;
+    constexpr float kSqrtBHi = (float)(1.0 / inv_sqrt(B));
+    constexpr float kSqrtBLo = (float)(1.0 / inv_sqrt(B) - (double)kSqrtBHi);
+    constexpr float kInvB = 1.0f / (float)B;                  // exact
+
+    const int64_t nsteps = (nblocks + G::BPW - 1) / G::BPW;
+    const int64_t wave0 = (int64_t)blockIdx.x * kWavesPerGroup +
+                          __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t nwaves = (int64_t)gridDim.x * kWavesPerGroup;
+    const uint32_t lane_elem = (uint32_t)(g * B + 8 * t);
+
+    for (int64_t step = wave0; step < nsteps; step += nwaves) {
+        // Slots past the last block re-read the last block and store nothing.
+        const int64_t left = nblocks - step * G::BPW;
+        const uint32_t off = left >= G::BPW ? lane_elem
+                                            : (uint32_t)((g < left ? g : (int)left - 1) * B + 8 * t);
+        const int64_t lblk = (step * (G::BPW * B) + off) / B;
+        const uint32_t coff = (uint32_t)(lblk - step * G::BPW) * (uint32_t)W::kRecord + 8 * t;
+        const int64_t cbase = step * G::BPW * W::kRecord;
+
+        u2v qc[P][G::CH];
+        float wa[P], ws[P];
+#pragma unroll
+        for (int p = 0; p < P; ++p) {
+#pragma unroll
+            for (int k = 0; k < G::CH; ++k) qc[p][k] = ld8(pay.codes[p] + cbase + coff + k * G::SPAN);
+            wa[p] = pay.alpha[p][lblk * W::kScalarStride];
+            ws[p] = pay.scale[p][lblk * W::kScalarStride];
+        }
+
+        // r_p = s_p / alpha_p as hi + lo; a power-of-two shift keeps
+        // sqrt(B) r_p decode(q_p) and the rotated sum inside float32 range
+        // (near the bf16 maximum) and out of the subnormals (tiny blocks).
+        // The shift is chosen from a plain estimate of the largest r_p and
+        // applied to s_p before the precise quotient, so that no r_p is a
+        // float32 subnormal.
+        float rmax = 0.0f;
+#pragma unroll
+        for (int p = 0; p < P; ++p) rmax = fmaxf(rmax, ws[p] > 0.0f ? ws[p] / wa[p] : 0.0f);
+        const float shift = rmax >= kBigMax ? kBigShift
+                            : (rmax > 0.0f && rmax < kTinyMax) ? kTinyShift : 1.0f;
+        Quot r[P];
+#pragma unroll
+        for (int p = 0; p < P; ++p) {
+            const float sp = ws[p] * shift;
+            r[p] = Quot{0.0f, 0.0f};
+            if (ws[p] > 0.0f)   // (a subnormal alpha would overflow the reciprocal)
+                r[p] = wa[p] >= 0x1p-120f ? quotient(sp, wa[p]) : Quot{sp / wa[p], 0.0f};
+        }
+        const float sh = kSqrtBHi, sl = kSqrtBLo;
+
+        float v[G::EPL];
+#pragma unroll
+        for (int i = 0; i < G::EPL; ++i) v[i] = 0.0f;
+#pragma unroll
+        for (int p = 0; p < P; ++p) {
+            const float ch = sh * r[p].hi;
+            const float cl = fmaf(sh, r[p].hi, -ch) + fmaf(sh, r[p].lo, sl * r[p].hi);
+            float d[G::EPL];
+#pragma unroll
+            for (int k = 0; k < G::CH; ++k) C::decode8(qc[p][k], &d[8 * k]);
+#pragma unroll
+            for (int i = 0; i < G::EPL; ++i) v[i] = fmaf(d[i], cl, fmaf(d[i], ch, v[i]));
+        }
+        fwht_block<G::LPB, G::EPL>(v, sg1, sg2, sg8);          // lane-signed H (sum)
+        // Undo the shift and divide by B (both powers of two: one rounding,
+        // in the final product).
+        const float fo = (kInvB / shift) * lane_sign;
+
+        const int64_t blk = step * G::BPW + g;
+        if (blk < nblocks) {
+            const int64_t e0 = blk * B + 8 * t;
+#pragma unroll
+            for (int k = 0; k < G::CH; ++k) {
+                float *pa = acc + e0 + k * G::SPAN;
+                const u4v p0 = ld16_acc(pa), p1 = ld16_acc(pa + 4);
+                u4v o0, o1;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    o0[j] = __float_as_uint(__uint_as_float(p0[j]) + v[8 * k + j] * fo);
+                    o1[j] = __float_as_uint(__uint_as_float(p1[j]) + v[8 * k + 4 + j] * fo);
+                }
+                st16(pa, o0);
+                st16(pa + 4, o1);
             }
         }
     }
@@ -1514,6 +1645,35 @@ taco_status Ops<F>::roundtrip(Variant variant, int32_t block, const uint16_t *x,
     st = roundtrip_variant<F>(variant, block, x, nblocks, tau, y, sums, stream);
     if (st != TACO_OK) return st;
     return launch(reinterpret_cast<const void *>(&fidelity_finish_kernel), 1u, stream, sums);
+}
+
+template <Fmt F, Layout L>
+struct AccumulateNLaunch {
+    int npay; Payloads pay; int64_t m; float *acc; hipStream_t stream;
+    template <int B, int P> taco_status go() const {
+        return launch(reinterpret_cast<const void *>(&accumulate_n_kernel<B, F, P, L>),
+                      grid_for(steps_of<B>(m)), stream, pay, m, acc);
+    }
+    template <int B> taco_status run() const {
+        switch (npay) {
+            case 1: return go<B, 1>();
+            case 2: return go<B, 2>();
+            case 3: return go<B, 3>();
+            case 4: return go<B, 4>();
+            case 5: return go<B, 5>();
+            case 6: return go<B, 6>();
+            case 7: return go<B, 7>();
+            default: return go<B, 8>();
+        }
+    }
+};
+
+template <Fmt F>
+taco_status Ops<F>::accumulate_n(Layout layout, int32_t block, int npay, const Payloads &pay,
+                                 int64_t nblocks, float *acc, hipStream_t stream) {
+    if (layout == Layout::kPacked)
+        return for_block(block, AccumulateNLaunch<F, Layout::kPacked>{npay, pay, nblocks, acc, stream});
+    return for_block(block, AccumulateNLaunch<F, Layout::kSide>{npay, pay, nblocks, acc, stream});
 }
 
 template <Fmt F>

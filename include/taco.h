@@ -147,6 +147,24 @@ taco_status taco_decompress_accumulate(const uint8_t *codes_e4m3, const float *a
                                        hipStream_t stream);
 
 /*
+ * Several payloads at once ([TACO] section 4.4.2: the owner of a segment
+ * reduces the payloads it receives): acc_f32 += sum_p G'_p over npayloads
+ * (0..TACO_MAX_PAYLOADS) payloads, in one pass.  The payloads are summed in
+ * the rotated domain (H G'_p = sqrt(B) (s_p / alpha_p) decode(q_p)) and
+ * transformed back once, so the accumulator is read and written once instead
+ * of once per payload.  codes_e4m3, alpha, scale: HOST arrays of npayloads
+ * DEVICE pointers, each payload as produced by taco_compress with the same
+ * shape and block.  acc_f32 as in taco_decompress_accumulate (16-byte aligned,
+ * must not overlap any payload).  npayloads == 0 is a no-op.  Rounding
+ * differs from npayloads separate taco_decompress_accumulate calls only by
+ * float32 evaluation order.
+ */
+taco_status taco_decompress_accumulate_n(int32_t npayloads, const uint8_t *const *codes_e4m3,
+                                         const float *const *alpha, const float *const *scale,
+                                         int64_t tokens, int64_t hidden, int32_t block,
+                                         float *acc_f32, hipStream_t stream);
+
+/*
  * Owner step of the two-shot all-reduce ([TACO] section 4.4.2: the
  * reduce-scatter phase is one compressed all-to-all followed by a single
  * local reduction, and the reduced segment is compressed again for the
@@ -242,6 +260,21 @@ taco_status taco_decompress_accumulate_packed_fmt(const uint8_t *payload, int64_
                                                   int64_t hidden, int32_t block,
                                                   taco_format format, float *acc_f32,
                                                   hipStream_t stream);
+taco_status taco_decompress_accumulate_n_fmt(int32_t npayloads, const uint8_t *const *codes,
+                                             const float *const *alpha, const float *const *scale,
+                                             int64_t tokens, int64_t hidden, int32_t block,
+                                             taco_format format, float *acc_f32,
+                                             hipStream_t stream);
+/* taco_decompress_accumulate_n with interleaved payloads (HOST array of
+ * npayloads DEVICE pointers to payloads). */
+taco_status taco_decompress_accumulate_n_packed(int32_t npayloads, const uint8_t *const *payloads,
+                                                int64_t tokens, int64_t hidden, int32_t block,
+                                                float *acc_f32, hipStream_t stream);
+taco_status taco_decompress_accumulate_n_packed_fmt(int32_t npayloads,
+                                                    const uint8_t *const *payloads, int64_t tokens,
+                                                    int64_t hidden, int32_t block,
+                                                    taco_format format, float *acc_f32,
+                                                    hipStream_t stream);
 taco_status taco_reduce_compress_packed_fmt(const uint16_t *own_bf16, int32_t npayloads,
                                             const uint8_t *const *payloads, int64_t tokens,
                                             int64_t hidden, int32_t block, float target_energy,

@@ -63,6 +63,10 @@ def lib():
     L.taco_decompress_accumulate_packed_fmt.argtypes = [P, I64, I64, I32, I32, P, P]
     L.taco_reduce_compress_packed_fmt.argtypes = [P, I32, P, I64, I64, I32, F32, I32, P, P]
     L.taco_roundtrip.argtypes = [P, I64, I64, I32, F32, I32, I32, P, P, P]
+    L.taco_decompress_accumulate_n.argtypes = [I32, P, P, P, I64, I64, I32, P, P]
+    L.taco_decompress_accumulate_n_fmt.argtypes = [I32, P, P, P, I64, I64, I32, I32, P, P]
+    L.taco_decompress_accumulate_n_packed.argtypes = [I32, P, I64, I64, I32, P, P]
+    L.taco_decompress_accumulate_n_packed_fmt.argtypes = [I32, P, I64, I64, I32, I32, P, P]
     L.taco_encode.argtypes = [I32, P, I64, P, P]
     L.taco_decode.argtypes = [I32, P, I64, P, P]
     L.taco_status_string.argtypes = [ctypes.c_int]
@@ -72,7 +76,7 @@ def lib():
 
 def test_every_declared_function_is_exported(lib):
     names = declared_functions()
-    assert len(names) == 24, names
+    assert len(names) == 28, names
     for n in names:
         assert hasattr(lib, n), n
     out = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True).stdout
@@ -320,3 +324,36 @@ def test_roundtrip_validation(lib):
     assert rt(sums=2 * A + 512) == ALIAS       # inside y
     assert rt(y=A + 1024) == ALIAS             # y overlaps x
     assert rt(tokens=0, x=None, y=None, sums=None) == OK   # empty: nothing written
+
+
+def test_accumulate_n_validation(lib):
+    arr = ctypes.c_void_p * 8
+    cs = lambda *v: None if v == (None,) else ctypes.cast(arr(*v), ctypes.c_void_p)
+    an = lambda **k: lib.taco_decompress_accumulate_n(
+        k.get("npay", 2), k.get("codes", cs(5 * A, 6 * A)), k.get("alpha", cs(7 * A, 8 * A)),
+        k.get("scale", cs(9 * A, 10 * A)), k.get("tokens", 4), k.get("hidden", 256),
+        k.get("block", 128), k.get("acc", 2 * A), None)
+    assert an(tokens=-1) == SHAPE
+    assert an(hidden=96, tokens=3) == SHAPE
+    assert an(block=48) == BLOCK
+    assert an(npay=9) == PARAM and an(npay=-1) == PARAM
+    assert an(acc=None) == NULL
+    assert an(codes=None) == NULL
+    assert an(codes=cs(5 * A, None)) == NULL
+    assert an(acc=2 * A + 8) == ALIGN
+    assert an(codes=cs(5 * A, 6 * A + 4)) == ALIGN
+    assert an(acc=5 * A - 64) == ALIAS          # acc overlaps payload 0's codes
+    assert an(acc=9 * A - 1024) == ALIAS        # acc overlaps payload 0's scale
+    # Nothing to do: empty tensors and zero payloads, even with NULL pointers.
+    assert an(tokens=0, acc=None, codes=None, alpha=None, scale=None) == OK
+    assert an(npay=0, acc=None, codes=None, alpha=None, scale=None) == OK
+    assert lib.taco_decompress_accumulate_n_fmt(2, None, None, None, 4, 256, 128, 9, 2 * A,
+                                                None) == FORMAT
+    ap = lambda **k: lib.taco_decompress_accumulate_n_packed(
+        k.get("npay", 2), k.get("pays", cs(5 * A, 6 * A)), 4, 256, 128, k.get("acc", 2 * A), None)
+    assert ap(pays=None) == NULL
+    assert ap(pays=cs(5 * A, 6 * A + 8)) == ALIGN
+    assert ap(acc=5 * A + 64) == ALIAS
+    assert ap(npay=0, pays=None, acc=None) == OK
+    assert lib.taco_decompress_accumulate_n_packed_fmt(2, None, 4, 256, 128, 3, 2 * A,
+                                                       None) == FORMAT

@@ -83,6 +83,13 @@ def test_cancelling_and_special_sums(taco):
     run_case(taco, huge, [huge], B)
     zero = np.zeros(16 * B, np.uint16)
     run_case(taco, zero, [x], B)
+    # Tiny blocks (bf16 subnormals, 1e-37 normals): rotated values and
+    # payload factors below the float32 normals.
+    sub = rng.integers(1, 0x7F, 16 * B).astype(np.uint16) | (rng.integers(0, 2, 16 * B).astype(np.uint16) << 15)
+    tiny = synth.f32_to_bits(rng.standard_normal(16 * B) * 1e-37)
+    tiny2 = synth.f32_to_bits(rng.standard_normal(16 * B) * 3e-38)
+    run_case(taco, None, [tiny, tiny2, sub], B)
+    run_case(taco, sub, [sub, tiny], B)
     # Top of the bf16 range, where H X (B |X|) leaves float32 range.
     for b in (128, 512):
         top = synth.f32_to_bits(np.clip(rng.standard_normal(16 * b) * 5e37, -2.5e38, 2.5e38))
