@@ -21,6 +21,8 @@ the dominant kernel and the CPU oracle's rate on the same workload.
 (``taco_reduce_compress`` of an own partial plus three payloads) instead;
 ``NAME:packed`` the round trip through the interleaved wire layout;
 ``NAME:e5m2`` and ``NAME:int8`` the round trip with E5M2 or INT8 codes;
+``NAME:accn`` (the four-payload workload) sums the four payloads with one
+``taco_decompress_accumulate_n`` call instead of four accumulates;
 ``NAME:fidelity`` the fidelity study's fused round trip (``taco_roundtrip``,
 the operator's variant, error sums only).
 """
@@ -89,6 +91,9 @@ def algorithmic_bytes(op: str, n: int, block: int) -> float:
         return n + side + 8.0 * n
     if op == "roundtrip":
         return 2.0 * n
+    if op.startswith("accumulate_n"):
+        npay = int(op.split(":")[1])
+        return npay * (n + side) + 8.0 * n
     raise ValueError(op)
 
 
@@ -282,7 +287,10 @@ def fidelity_case(torch, taco, synth, name: str, block: int, steps: int, warmup:
 
 
 def accumulate_case(torch, taco, synth, name: str, block: int, steps: int, warmup: int,
-                    use_graph: bool):
+                    use_graph: bool, fused: bool = False):
+    """Four payloads compressed and summed into one float32 accumulator: one
+    taco_decompress_accumulate per payload, or (fused) one
+    taco_decompress_accumulate_n over all four."""
     import numpy as np
     r = synth.WORKLOADS[name]
     n = r.numel
@@ -303,6 +311,9 @@ def accumulate_case(torch, taco, synth, name: str, block: int, steps: int, warmu
             taco.compress(x, block=block, codes=codes, alpha=alpha, scale=scale)
 
     def run_accumulate():
+        if fused:
+            taco.decompress_accumulate_n([(c, a, s) for _, c, a, s in payloads], acc, block=block)
+            return
         for _, codes, alpha, scale in payloads:
             taco.decompress_accumulate(codes, alpha, scale, acc, block=block)
 
@@ -320,14 +331,17 @@ def accumulate_case(torch, taco, synth, name: str, block: int, steps: int, warmu
     timer = Timer(torch)
     step_fn()
     t_steps = timer.time(step_fn, reps)
-    t_c = timer.time(comp_fn, reps) / (4 * reps)
-    t_a = timer.time(acc_fn, reps) / (4 * reps)
     nb = len(payloads)
+    t_c = timer.time(comp_fn, reps) / (nb * reps)
+    t_a = timer.time(acc_fn, reps) / ((1 if fused else nb) * reps)
+    acc_bytes = (algorithmic_bytes(f"accumulate_n:{nb}", n, block) if fused
+                 else nb * algorithmic_bytes("accumulate", n, block))
+    kname = "accumulate_n" if fused else "accumulate"
     return {"n": n, "block": block, "steps": reps, "t_step": t_steps / reps, "t_compress": t_c,
             "t_accumulate": t_a, "sets": 1, "rows": r.rows, "cols": r.cols,
-            "bytes_step": nb * (algorithmic_bytes("compress", n, block)
-                                + algorithmic_bytes("accumulate", n, block)),
-            "input_bytes_step": nb * 2.0 * n, "kernels": {"compress": t_c, "accumulate": t_a}}
+            "fused": fused, "nb": nb,
+            "bytes_step": nb * algorithmic_bytes("compress", n, block) + acc_bytes,
+            "input_bytes_step": nb * 2.0 * n, "kernels": {"compress": t_c, kname: t_a}}
 
 
 def owner_case(torch, taco, synth, name: str, block: int, steps: int, warmup: int,
@@ -402,7 +416,8 @@ def record(res, name: str, args, cpu=None):
     value = res["input_bytes_step"] / t_step / 1e9
     kern = max(res["kernels"], key=lambda k: res["kernels"][k])
     dur = res["kernels"][kern]
-    op = kern if kern != "reduce_compress" else f"reduce_compress:{res['npayloads']}"
+    op = (f"reduce_compress:{res['npayloads']}" if kern == "reduce_compress"
+          else f"accumulate_n:{res['nb']}" if kern == "accumulate_n" else kern)
     kbytes = algorithmic_bytes(op, res["n"], res["block"])
     achieved = kbytes / dur / 1e9
     fmt = res.get("format", "e4m3")
@@ -422,7 +437,9 @@ def record(res, name: str, args, cpu=None):
         "data": "synthetic",
         "config": {"workload": name, "tokens": res["rows"], "hidden": res["cols"],
                    "block": res["block"], "target_energy": 1.0, "format": fmt,
-                   "step": ("4x compress + 4x decompress_accumulate" if "t_accumulate" in res
+                   "step": ("4x compress + 1x decompress_accumulate_n of 4 payloads"
+                            if res.get("fused")
+                            else "4x compress + 4x decompress_accumulate" if "t_accumulate" in res
                             else f"reduce_compress of own + {res['npayloads']} payloads"
                             if "npayloads" in res
                             else "compress_packed + decompress_packed" if res.get("packed")
@@ -476,6 +493,7 @@ def main():
                  ("qwen7b_act_16384x3584", 128), ("qwen7b_act_16384x3584", 256),
                  ("grad_8192x8192", 256), ("gpt175b_hidden_32768x12288", 256),
                  ("gpt175b_hidden_32768x12288:owner", 256),
+                 ("gpt175b_hidden_32768x12288:accn", 256),
                  ("gpt2.7b_rowpar_8192x2560:packed", 128),
                  ("gpt2.7b_rowpar_8192x2560:e5m2", 128),
                  ("gpt2.7b_rowpar_8192x2560:int8", 128),
@@ -496,6 +514,10 @@ def main():
         elif name.endswith(":packed"):
             name = name.split(":")[0]
             res = packed_case(torch, taco, synth, name, block, steps, args.warmup, use_graph)
+        elif name.endswith(":accn"):
+            name = name.split(":")[0]
+            res = accumulate_case(torch, taco, synth, name, block, steps, args.warmup, use_graph,
+                                  fused=True)
         elif name.endswith(":fidelity"):
             name = name.split(":")[0]
             res = fidelity_case(torch, taco, synth, name, block, steps, args.warmup, use_graph)
