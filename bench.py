@@ -153,6 +153,53 @@ def make_graph(torch, fn, use_graph: bool):
     return g.replay
 
 
+STEP_CHUNK = 2048      # most steps captured into one HIP graph
+
+
+def run_cycle(torch, sets, one, count: int, use_graph: bool):
+    """A callable that runs one(set) for exactly `count` consecutive steps,
+    cycling through the buffer sets, as HIP graphs of at most STEP_CHUNK
+    steps (a full graph replayed, then a remainder graph)."""
+    if count <= 0:
+        return lambda: None
+
+    def body(c):
+        def run():
+            for i in range(c):
+                one(sets[i % len(sets)])
+        return run
+
+    chunk = min(count, STEP_CHUNK)
+    q, rem = divmod(count, chunk)
+    full = make_graph(torch, body(chunk), use_graph)
+    tail = make_graph(torch, body(rem), use_graph) if rem else None
+
+    def go():
+        for _ in range(q):
+            full()
+        if tail is not None:
+            tail()
+    return go
+
+
+def time_steps(torch, sets, step_one, kernels: dict, steps: int, warmup: int, use_graph: bool):
+    """Exactly `warmup` untimed steps, then exactly `steps` timed steps
+    (seconds per step); then each kernel alone over at least one pass of the
+    sets (seconds per launch), for its roofline."""
+    for i in range(warmup):
+        step_one(sets[i % len(sets)])
+    torch.cuda.synchronize()
+    timer = Timer(torch)
+    step_fn = run_cycle(torch, sets, step_one, steps, use_graph)
+    t_step = timer.time(step_fn, 1) / steps
+    per_kernel = {}
+    count = max(steps, len(sets))
+    for kname, one in kernels.items():
+        fn = run_cycle(torch, sets, one, count, use_graph)
+        per_kernel[kname] = timer.time(fn, 1) / count
+    return t_step, per_kernel
+
+
 def roundtrip_case(torch, taco, synth, name: str, block: int, steps: int, warmup: int,
                    use_graph: bool, fmt: str = "e4m3"):
     import numpy as np
@@ -173,33 +220,23 @@ def roundtrip_case(torch, taco, synth, name: str, block: int, steps: int, warmup
         sets.append((x, codes, alpha, scale, y))
     del x0
 
-    def run_compress():
-        for x, codes, alpha, scale, _ in sets:
-            taco.compress(x, block=block, codes=codes, alpha=alpha, scale=scale, fmt=fmt)
+    def one_compress(st):
+        x, codes, alpha, scale, _ = st
+        taco.compress(x, block=block, codes=codes, alpha=alpha, scale=scale, fmt=fmt)
 
-    def run_decompress():
-        for _, codes, alpha, scale, y in sets:
-            taco.decompress(codes, alpha, scale, block=block, out=y, fmt=fmt)
+    def one_decompress(st):
+        _, codes, alpha, scale, y = st
+        taco.decompress(codes, alpha, scale, block=block, out=y, fmt=fmt)
 
-    def run_steps():
-        for x, codes, alpha, scale, y in sets:
-            taco.compress(x, block=block, codes=codes, alpha=alpha, scale=scale, fmt=fmt)
-            taco.decompress(codes, alpha, scale, block=block, out=y, fmt=fmt)
+    def one_step(st):
+        one_compress(st)
+        one_decompress(st)
 
-    for _ in range(max(1, warmup // nsets)):
-        run_steps()
-    torch.cuda.synchronize()
-    step_fn = make_graph(torch, run_steps, use_graph)
-    comp_fn = make_graph(torch, run_compress, use_graph)
-    dec_fn = make_graph(torch, run_decompress, use_graph)
-    reps = max(1, -(-steps // nsets))
-    timer = Timer(torch)
-    step_fn()
-    t_steps = timer.time(step_fn, reps)
-    k = reps * nsets
-    t_c = timer.time(comp_fn, reps) / k
-    t_d = timer.time(dec_fn, reps) / k
-    return {"n": n, "block": block, "steps": k, "t_step": t_steps / k, "t_compress": t_c,
+    t_step, kt = time_steps(torch, sets, one_step,
+                            {"compress": one_compress, "decompress": one_decompress},
+                            steps, warmup, use_graph)
+    t_c, t_d = kt["compress"], kt["decompress"]
+    return {"n": n, "block": block, "steps": steps, "t_step": t_step, "t_compress": t_c,
             "t_decompress": t_d, "sets": nsets, "rows": r.rows, "cols": r.cols, "format": fmt,
             "bytes_step": algorithmic_bytes("compress", n, block)
             + algorithmic_bytes("decompress", n, block),
@@ -222,33 +259,23 @@ def packed_case(torch, taco, synth, name: str, block: int, steps: int, warmup: i
              torch.empty((r.rows, r.cols), dtype=torch.bfloat16, device="cuda")) for _ in range(nsets)]
     del x0
 
-    def run_steps():
-        for x, pay, y in sets:
-            taco.compress_packed(x, block=block, payload=pay)
-            taco.decompress_packed(pay, y.shape, block=block, out=y)
+    def one_compress(st):
+        x, pay, _ = st
+        taco.compress_packed(x, block=block, payload=pay)
 
-    def run_compress():
-        for x, pay, _ in sets:
-            taco.compress_packed(x, block=block, payload=pay)
+    def one_decompress(st):
+        _, pay, y = st
+        taco.decompress_packed(pay, y.shape, block=block, out=y)
 
-    def run_decompress():
-        for _, pay, y in sets:
-            taco.decompress_packed(pay, y.shape, block=block, out=y)
+    def one_step(st):
+        one_compress(st)
+        one_decompress(st)
 
-    for _ in range(max(1, warmup // nsets)):
-        run_steps()
-    torch.cuda.synchronize()
-    step_fn = make_graph(torch, run_steps, use_graph)
-    comp_fn = make_graph(torch, run_compress, use_graph)
-    dec_fn = make_graph(torch, run_decompress, use_graph)
-    reps = max(1, -(-steps // nsets))
-    timer = Timer(torch)
-    step_fn()
-    k = reps * nsets
-    t_steps = timer.time(step_fn, reps)
-    t_c = timer.time(comp_fn, reps) / k
-    t_d = timer.time(dec_fn, reps) / k
-    return {"n": n, "block": block, "steps": k, "t_step": t_steps / k, "sets": nsets,
+    t_step, kt = time_steps(torch, sets, one_step,
+                            {"compress": one_compress, "decompress": one_decompress},
+                            steps, warmup, use_graph)
+    t_c, t_d = kt["compress"], kt["decompress"]
+    return {"n": n, "block": block, "steps": steps, "t_step": t_step, "sets": nsets,
             "rows": r.rows, "cols": r.cols, "packed": True,
             "bytes_step": algorithmic_bytes("compress", n, block)
             + algorithmic_bytes("decompress", n, block),
@@ -268,20 +295,12 @@ def fidelity_case(torch, taco, synth, name: str, block: int, steps: int, warmup:
             for _ in range(nsets)]
     del x0
 
-    def run_steps():
-        for x, sums in sets:
-            taco.roundtrip(x, block=block, variant="taco", sums=sums)
+    def one_step(st):
+        x, sums = st
+        taco.roundtrip(x, block=block, variant="taco", sums=sums)
 
-    for _ in range(max(1, warmup // nsets)):
-        run_steps()
-    torch.cuda.synchronize()
-    step_fn = make_graph(torch, run_steps, use_graph)
-    reps = max(1, -(-steps // nsets))
-    timer = Timer(torch)
-    step_fn()
-    k = reps * nsets
-    t = timer.time(step_fn, reps) / k
-    return {"n": n, "block": block, "steps": k, "t_step": t, "sets": nsets, "rows": r.rows,
+    t, _ = time_steps(torch, sets, one_step, {}, steps, warmup, use_graph)
+    return {"n": n, "block": block, "steps": steps, "t_step": t, "sets": nsets, "rows": r.rows,
             "cols": r.cols, "fidelity": True, "bytes_step": 2.0 * n, "input_bytes_step": 2.0 * n,
             "kernels": {"roundtrip": t}}
 
@@ -321,7 +340,7 @@ def accumulate_case(torch, taco, synth, name: str, block: int, steps: int, warmu
         run_compress()
         run_accumulate()
 
-    for _ in range(max(1, warmup // 8)):
+    for _ in range(warmup):
         run_steps()
     torch.cuda.synchronize()
     step_fn = make_graph(torch, run_steps, use_graph)
@@ -367,7 +386,7 @@ def owner_case(torch, taco, synth, name: str, block: int, steps: int, warmup: in
     def run_steps():
         taco.reduce_compress(own, pay, block=block, codes=codes, alpha=alpha, scale=scale)
 
-    for _ in range(max(1, warmup)):
+    for _ in range(warmup):
         run_steps()
     torch.cuda.synchronize()
     step_fn = make_graph(torch, run_steps, use_graph)
@@ -473,6 +492,8 @@ def copy_probe(torch):
 
 def main():
     args = parse()
+    args.steps = max(1, args.steps)
+    args.warmup = max(0, args.warmup)
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the operator "
               "has no multi-GPU path in this build).", file=sys.stderr)
