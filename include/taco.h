@@ -17,7 +17,12 @@
  *             G' = H_B (decode(q) * s) / sqrt(B) / alpha.
  *   reduce   (section 4.4.2: the reduce-scatter phase of the two-shot
  *             all-reduce ends in one local reduction of the received
- *             payloads): acc += G'.
+ *             payloads): acc += G' per payload, or for several payloads in
+ *             one pass, or reduced and compressed again (the owner step).
+ *
+ * Beside the operator: the interleaved wire layout of section 4.4.2
+ * (*_packed), the E5M2 and INT8 code formats (*_fmt, taco_format), and a
+ * fidelity study of the ablation variants (taco_roundtrip).
  *
  * Conventions shared by every call below
  *   - All tensor pointers are DEVICE pointers (any device allocation, e.g. a
@@ -51,9 +56,9 @@ extern "C" {
 /* Largest finite OCP E4M3 ("E4M3FN") value: Q_max of [TACO] Eq. 9. */
 #define TACO_QMAX 448.0f
 
-/* epsilon of [TACO] Eq. 6, inside the square root ("a small constant
- * ensuring numerical stability for near-zero blocks"; its value is not
- * given).  Far below the energy of any realistic block, yet it keeps alpha
+/* epsilon of [TACO] Eq. 6, inside the square root (the page describes it
+ * only as a small stabilising constant for near-zero blocks and gives no
+ * value).  Far below the energy of any realistic block, yet it keeps alpha
  * finite (tau * 1e10) for an all-zero block. */
 #define TACO_EPS 1e-20f
 
@@ -65,8 +70,8 @@ extern "C" {
  * an all-zero block (sigma = sqrt(eps)). */
 #define TACO_MAX_TARGET_ENERGY 1e20f
 
-/* Most received payloads one taco_reduce_compress call sums (tensor
- * parallelism up to 9 ranks). */
+/* Most received payloads one taco_reduce_compress or
+ * taco_decompress_accumulate_n call sums (tensor parallelism up to 9 ranks). */
 #define TACO_MAX_PAYLOADS 8
 
 /* Code formats of Eq. 10-11.  E4M3 is the operator's; the other two keep
@@ -95,8 +100,9 @@ typedef enum {
     TACO_ERR_NULL = 1,   /* a required pointer is NULL                          */
     TACO_ERR_SHAPE = 2,  /* tokens < 0, hidden <= 0, N overflows, N % block != 0 */
     TACO_ERR_BLOCK = 3,  /* block is not one of 32, 64, 128, 256, 512            */
-    TACO_ERR_PARAM = 4,  /* target_energy not finite or outside (0, 1e20], or a
-                            payload count outside 0..TACO_MAX_PAYLOADS          */
+    TACO_ERR_PARAM = 4,  /* target_energy not finite or outside (0, 1e20], a
+                            payload count outside 0..TACO_MAX_PAYLOADS, or an
+                            unknown taco_variant                               */
     TACO_ERR_ALIGN = 5,  /* a tensor is not 16-byte aligned, or alpha / scale
                             not 4-byte aligned                                  */
     TACO_ERR_ALIAS = 6,  /* an output buffer overlaps an input or another output */
