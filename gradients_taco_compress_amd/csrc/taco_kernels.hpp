@@ -469,10 +469,10 @@ constexpr double inv_sqrt(int b) {
                       : 0.04419417382415922028;
 }
 
-// Blocks whose energy reaches this are rescaled by 2^-64 before squaring so
-// that sum x^2 stays finite for every bf16 input.  (kBigMax: the same for a
-// block maximum, before a plain rotation.)
-// With 2^-80, sum (x 2^-80)^2 <= 512 (2^128 2^-80)^2 = 2^105 for any bf16 x.
+// Blocks whose energy reaches this are rescaled by 2^-80 before squaring so
+// that sum x^2 stays finite for every bf16 input: sum (x 2^-80)^2 <=
+// 512 (2^128 2^-80)^2 = 2^105.  (kBigMax: the same for a block maximum,
+// before a plain rotation.)
 constexpr float kBigEnergy = 0x1p100f;
 constexpr float kBigMax = 0x1p100f;
 constexpr float kBigShift = 0x1p-80f;
