@@ -140,7 +140,8 @@ EXPORTS = ("taco_num_blocks", "taco_compress", "taco_decompress",
            "taco_decompress_accumulate_n_fmt", "taco_decompress_accumulate_n_packed",
            "taco_decompress_accumulate_n_packed_fmt")
 
-#: Most payloads one taco_reduce_compress call sums.
+#: Most payloads one taco_reduce_compress or taco_decompress_accumulate_n
+#: call sums.
 MAX_PAYLOADS = 8
 
 
@@ -329,9 +330,27 @@ def _torch():
     return torch
 
 
-def _stream(stream):
+def _stream(stream, *tensors):
+    """Handle of the stream to launch on: ``stream``, else torch's current
+    stream of the device the tensors live on.  Every tensor (None entries and
+    nested lists allowed) must be on that one device."""
     torch = _torch()
-    s = torch.cuda.current_stream() if stream is None else stream
+    devs = set()
+    todo = list(tensors)
+    while todo:
+        t = todo.pop()
+        if t is None:
+            continue
+        if isinstance(t, (list, tuple)):
+            todo.extend(t)
+            continue
+        devs.add(t.device)
+    if len(devs) > 1:
+        raise ValueError(f"tensors are on different devices: {sorted(str(d) for d in devs)}")
+    dev = next(iter(devs)) if devs else None
+    s = torch.cuda.current_stream(dev) if stream is None else stream
+    if dev is not None and s.device != dev:
+        raise ValueError(f"stream is on {s.device}, tensors on {dev}")
     return s.cuda_stream
 
 
@@ -384,7 +403,7 @@ def compress(x, block: int = 256, target_energy: float = DEFAULT_TARGET_ENERGY,
     m = taco_num_blocks(tokens, hidden, block)
     if m < 0:   # let the library name the validation error
         _check(_compress_call(fmt, x.data_ptr(), tokens, hidden, block, float(target_energy),
-                              0, 0, 0, _stream(stream)), "taco_compress")
+                              0, 0, 0, _stream(stream, x)), "taco_compress")
     if codes is None:
         codes = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
     if alpha is None:
@@ -397,7 +416,7 @@ def compress(x, block: int = 256, target_energy: float = DEFAULT_TARGET_ENERGY,
     if codes.numel() != x.numel() or alpha.numel() < m or scale.numel() < m:
         raise ValueError("output buffers are too small")
     _check(_compress_call(fmt, x.data_ptr(), tokens, hidden, block, float(target_energy),
-                          codes.data_ptr(), alpha.data_ptr(), scale.data_ptr(), _stream(stream)),
+                          codes.data_ptr(), alpha.data_ptr(), scale.data_ptr(), _stream(stream, x, codes, alpha, scale)),
            "taco_compress")
     return codes, alpha, scale
 
@@ -426,10 +445,10 @@ def decompress(codes, alpha, scale, block: int = 256, out=None, stream=None, fmt
         raise ValueError("out must have as many elements as codes")
     if fmt == "e4m3":
         st = taco_decompress(codes.data_ptr(), alpha.data_ptr(), scale.data_ptr(), tokens, hidden,
-                             block, out.data_ptr(), _stream(stream))
+                             block, out.data_ptr(), _stream(stream, codes, alpha, scale, out))
     else:
         st = taco_decompress_fmt(codes.data_ptr(), alpha.data_ptr(), scale.data_ptr(), tokens,
-                                 hidden, block, f, out.data_ptr(), _stream(stream))
+                                 hidden, block, f, out.data_ptr(), _stream(stream, codes, alpha, scale, out))
     _check(st, "taco_decompress")
     return out
 
@@ -445,11 +464,11 @@ def decompress_accumulate(codes, alpha, scale, acc, block: int = 256, stream=Non
         raise ValueError("acc must have as many elements as codes")
     if fmt == "e4m3":
         st = taco_decompress_accumulate(codes.data_ptr(), alpha.data_ptr(), scale.data_ptr(),
-                                        tokens, hidden, block, acc.data_ptr(), _stream(stream))
+                                        tokens, hidden, block, acc.data_ptr(), _stream(stream, codes, alpha, scale, acc))
     else:
         st = taco_decompress_accumulate_fmt(codes.data_ptr(), alpha.data_ptr(), scale.data_ptr(),
                                             tokens, hidden, block, f, acc.data_ptr(),
-                                            _stream(stream))
+                                            _stream(stream, codes, alpha, scale, acc))
     _check(st, "taco_decompress_accumulate")
     return acc
 
@@ -497,7 +516,7 @@ def reduce_compress(own, payloads, block: int = 256, target_energy: float = DEFA
             [a.data_ptr() for _, a, _ in payloads] if n else None,
             [s.data_ptr() for _, _, s in payloads] if n else None,
             tokens, hidden, block, float(target_energy))
-    outs = (codes.data_ptr(), alpha.data_ptr(), scale.data_ptr(), _stream(stream))
+    outs = (codes.data_ptr(), alpha.data_ptr(), scale.data_ptr(), _stream(stream, own, codes, alpha, scale, payloads))
     if fmt == "e4m3":
         st = taco_reduce_compress(*args, *outs)
     else:
@@ -528,10 +547,10 @@ def compress_packed(x, block: int = 256, target_energy: float = DEFAULT_TARGET_E
         raise ValueError("payload buffer is too small")
     if fmt == "e4m3":
         st = taco_compress_packed(x.data_ptr(), tokens, hidden, block, float(target_energy),
-                                  payload.data_ptr(), _stream(stream))
+                                  payload.data_ptr(), _stream(stream, x, payload))
     else:
         st = taco_compress_packed_fmt(x.data_ptr(), tokens, hidden, block, float(target_energy),
-                                      f, payload.data_ptr(), _stream(stream))
+                                      f, payload.data_ptr(), _stream(stream, x, payload))
     _check(st, "taco_compress_packed")
     return payload
 
@@ -553,10 +572,10 @@ def decompress_packed(payload, shape, block: int = 256, out=None, stream=None,
     _need(out, torch.bfloat16, "out")
     if fmt == "e4m3":
         st = taco_decompress_packed(payload.data_ptr(), tokens, hidden, block, out.data_ptr(),
-                                    _stream(stream))
+                                    _stream(stream, payload, out))
     else:
         st = taco_decompress_packed_fmt(payload.data_ptr(), tokens, hidden, block, f,
-                                        out.data_ptr(), _stream(stream))
+                                        out.data_ptr(), _stream(stream, payload, out))
     _check(st, "taco_decompress_packed")
     return out
 
@@ -572,10 +591,10 @@ def decompress_accumulate_packed(payload, acc, block: int = 256, stream=None, fm
         raise ValueError("payload is too small for acc's shape")
     if fmt == "e4m3":
         st = taco_decompress_accumulate_packed(payload.data_ptr(), tokens, hidden, block,
-                                               acc.data_ptr(), _stream(stream))
+                                               acc.data_ptr(), _stream(stream, payload, acc))
     else:
         st = taco_decompress_accumulate_packed_fmt(payload.data_ptr(), tokens, hidden, block, f,
-                                                   acc.data_ptr(), _stream(stream))
+                                                   acc.data_ptr(), _stream(stream, payload, acc))
     _check(st, "taco_decompress_accumulate_packed")
     return acc
 
@@ -609,9 +628,9 @@ def reduce_compress_packed(own, payloads, shape=None, block: int = 256,
             [p.data_ptr() for p in payloads] if n else None, tokens, hidden, block,
             float(target_energy))
     if fmt == "e4m3":
-        st = taco_reduce_compress_packed(*args, out.data_ptr(), _stream(stream))
+        st = taco_reduce_compress_packed(*args, out.data_ptr(), _stream(stream, own, out, payloads))
     else:
-        st = taco_reduce_compress_packed_fmt(*args, f, out.data_ptr(), _stream(stream))
+        st = taco_reduce_compress_packed_fmt(*args, f, out.data_ptr(), _stream(stream, own, out, payloads))
     _check(st, "taco_reduce_compress_packed")
     return out
 
@@ -623,7 +642,7 @@ def e4m3_encode(x, out=None, stream=None):
     if out is None:
         out = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
     _need(out, torch.uint8, "out")
-    _check(taco_e4m3_encode(x.data_ptr(), x.numel(), out.data_ptr(), _stream(stream)),
+    _check(taco_e4m3_encode(x.data_ptr(), x.numel(), out.data_ptr(), _stream(stream, x, out)),
            "taco_e4m3_encode")
     return out
 
@@ -635,7 +654,7 @@ def e4m3_decode(codes, out=None, stream=None):
     if out is None:
         out = torch.empty(codes.shape, dtype=torch.float32, device=codes.device)
     _need(out, torch.float32, "out")
-    _check(taco_e4m3_decode(codes.data_ptr(), codes.numel(), out.data_ptr(), _stream(stream)),
+    _check(taco_e4m3_decode(codes.data_ptr(), codes.numel(), out.data_ptr(), _stream(stream, codes, out)),
            "taco_e4m3_decode")
     return out
 
@@ -648,7 +667,7 @@ def encode(x, fmt: str = "e4m3", out=None, stream=None):
     if out is None:
         out = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
     _need(out, torch.uint8, "out")
-    _check(taco_encode(f, x.data_ptr(), x.numel(), out.data_ptr(), _stream(stream)), "taco_encode")
+    _check(taco_encode(f, x.data_ptr(), x.numel(), out.data_ptr(), _stream(stream, x, out)), "taco_encode")
     return out
 
 
@@ -660,7 +679,7 @@ def decode(codes, fmt: str = "e4m3", out=None, stream=None):
     if out is None:
         out = torch.empty(codes.shape, dtype=torch.float32, device=codes.device)
     _need(out, torch.float32, "out")
-    _check(taco_decode(f, codes.data_ptr(), codes.numel(), out.data_ptr(), _stream(stream)),
+    _check(taco_decode(f, codes.data_ptr(), codes.numel(), out.data_ptr(), _stream(stream, codes, out)),
            "taco_decode")
     return out
 
@@ -696,7 +715,7 @@ def roundtrip(x, block: int = 256, variant: str = "taco", fmt: str = "e4m3",
             raise ValueError("out must have as many elements as x")
     _check(taco_roundtrip(x.data_ptr(), tokens, hidden, block, float(target_energy), f,
                           VARIANTS[variant], 0 if out is None else out.data_ptr(),
-                          sums.data_ptr(), _stream(stream)), "taco_roundtrip")
+                          sums.data_ptr(), _stream(stream, x, out, sums)), "taco_roundtrip")
     return out, sums
 
 
@@ -732,9 +751,9 @@ def decompress_accumulate_n(payloads, acc, block: int = 256, stream=None, fmt: s
             [a.data_ptr() for _, a, _ in payloads] if n else None,
             [s.data_ptr() for _, _, s in payloads] if n else None, tokens, hidden, block)
     if fmt == "e4m3":
-        st = taco_decompress_accumulate_n(*args, acc.data_ptr(), _stream(stream))
+        st = taco_decompress_accumulate_n(*args, acc.data_ptr(), _stream(stream, acc, payloads))
     else:
-        st = taco_decompress_accumulate_n_fmt(*args, f, acc.data_ptr(), _stream(stream))
+        st = taco_decompress_accumulate_n_fmt(*args, f, acc.data_ptr(), _stream(stream, acc, payloads))
     _check(st, "taco_decompress_accumulate_n")
     return acc
 
@@ -755,9 +774,9 @@ def decompress_accumulate_n_packed(payloads, acc, block: int = 256, stream=None,
     ptrs = [p.data_ptr() for p in payloads] if n else None
     if fmt == "e4m3":
         st = taco_decompress_accumulate_n_packed(n, ptrs, tokens, hidden, block, acc.data_ptr(),
-                                                 _stream(stream))
+                                                 _stream(stream, acc, payloads))
     else:
         st = taco_decompress_accumulate_n_packed_fmt(n, ptrs, tokens, hidden, block, f,
-                                                     acc.data_ptr(), _stream(stream))
+                                                     acc.data_ptr(), _stream(stream, acc, payloads))
     _check(st, "taco_decompress_accumulate_n_packed")
     return acc
