@@ -340,11 +340,16 @@ __device__ __forceinline__ float sum_squares(const float (&v)[EPL]) {
 // costs an extra instruction per element; NaN handling is not needed here.)
 template <int EPL>
 __device__ __forceinline__ float max_abs(const float (&v)[EPL]) {
-    float m0 = 0.0f, m1 = 0.0f;
+    static_assert(EPL >= 8 && EPL % 2 == 0, "max_abs layout");
+    float m0, m1;
+    asm("v_max3_f32 %0, |%1|, |%2|, |%3|" : "=v"(m0) : "v"(v[0]), "v"(v[1]), "v"(v[2]));
+    asm("v_max3_f32 %0, |%1|, |%2|, |%3|" : "=v"(m1) : "v"(v[3]), "v"(v[4]), "v"(v[5]));
 #pragma unroll
-    for (int i = 0; i < EPL; i += 4) {
-        asm("v_max3_f32 %0, %0, |%1|, |%2|" : "+v"(m0) : "v"(v[i]), "v"(v[i + 1]));
-        asm("v_max3_f32 %0, %0, |%1|, |%2|" : "+v"(m1) : "v"(v[i + 2]), "v"(v[i + 3]));
+    for (int i = 6; i < EPL; i += 2) {
+        if ((i / 2) & 1)
+            asm("v_max3_f32 %0, %0, |%1|, |%2|" : "+v"(m0) : "v"(v[i]), "v"(v[i + 1]));
+        else
+            asm("v_max3_f32 %0, %0, |%1|, |%2|" : "+v"(m1) : "v"(v[i]), "v"(v[i + 1]));
     }
     asm("v_max_f32 %0, %0, %1" : "+v"(m0) : "v"(m1));
     return m0;
@@ -368,7 +373,9 @@ __device__ __forceinline__ Quot quotient(float q, float m) {
 // v * Q / m for 8 values, given Q / m as hi + lo: the argument of the
 // conversion is v * (hi + lo) with a single final rounding, i.e. float32 of
 // v * Q / m almost always correctly rounded; the +0 addend of the inner fma
-// maps an exact zero of either sign to +0.
+// maps an exact zero of either sign to +0.  In pack8 each word takes two
+// conversions: the second overwrites the half the first one keeps, so the
+// first is seeded with any register (its own argument) rather than zero.
 template <Fmt F>
 struct Codec;
 
@@ -385,9 +392,9 @@ template <>
 struct Codec<Fmt::kE4M3> {
     static constexpr float kQmax = TACO_QMAX;
     static __device__ __forceinline__ u2v pack8(const float *q) {
-        int lo = __builtin_amdgcn_cvt_pk_fp8_f32(q[0], q[1], 0, false);
+        int lo = __builtin_amdgcn_cvt_pk_fp8_f32(q[0], q[1], __float_as_int(q[0]), false);
         lo = __builtin_amdgcn_cvt_pk_fp8_f32(q[2], q[3], lo, true);
-        int hi = __builtin_amdgcn_cvt_pk_fp8_f32(q[4], q[5], 0, false);
+        int hi = __builtin_amdgcn_cvt_pk_fp8_f32(q[4], q[5], __float_as_int(q[4]), false);
         hi = __builtin_amdgcn_cvt_pk_fp8_f32(q[6], q[7], hi, true);
         return (u2v){(uint32_t)lo, (uint32_t)hi};
     }
@@ -406,9 +413,9 @@ template <>
 struct Codec<Fmt::kE5M2> {
     static constexpr float kQmax = TACO_E5M2_MAX;
     static __device__ __forceinline__ u2v pack8(const float *q) {
-        int lo = __builtin_amdgcn_cvt_pk_bf8_f32(q[0], q[1], 0, false);
+        int lo = __builtin_amdgcn_cvt_pk_bf8_f32(q[0], q[1], __float_as_int(q[0]), false);
         lo = __builtin_amdgcn_cvt_pk_bf8_f32(q[2], q[3], lo, true);
-        int hi = __builtin_amdgcn_cvt_pk_bf8_f32(q[4], q[5], 0, false);
+        int hi = __builtin_amdgcn_cvt_pk_bf8_f32(q[4], q[5], __float_as_int(q[4]), false);
         hi = __builtin_amdgcn_cvt_pk_bf8_f32(q[6], q[7], hi, true);
         return (u2v){(uint32_t)lo, (uint32_t)hi};
     }
@@ -511,24 +518,33 @@ __global__ __launch_bounds__(kGroup) void compress_kernel(
     const int64_t wave0 = (int64_t)blockIdx.x * kWavesPerGroup +
                           __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int64_t nwaves = (int64_t)gridDim.x * kWavesPerGroup;
-    // Element offset of this lane's data inside one wave-step's span of
-    // BPW blocks; addresses are a wave-uniform base plus this 32-bit offset.
-    const uint32_t lane_elem = (uint32_t)(g * B + 8 * t);
+    // Every address is a wave-uniform base (the wave-step's first block)
+    // plus a 32-bit byte offset of the lane, so the memory instructions take
+    // the base in scalar registers and the offset in one vector register.
+    const char *const xb = reinterpret_cast<const char *>(x);
+    const uint32_t lane_code = (uint32_t)(g * W::kRecord + 8 * t);
+    const uint32_t lane_scalar = (uint32_t)(g * W::kScalarStride * 4);
+    constexpr int64_t kStepX = G::BPW * B * 2;                        // bytes of x
+    constexpr int64_t kStepCodes = G::BPW * W::kRecord;
+    constexpr int64_t kStepScalars = G::BPW * W::kScalarStride * 4;
 
-    // Slots past the last block (only in the final wave-step) re-read the
-    // last block, so every load is in bounds and no lane needs zero-filling;
-    // their results are never stored.
-    auto lane_offset = [&](int64_t step) -> uint32_t {
+    // Index of the last block slot of a wave-step that holds a block (BPW - 1
+    // except in the final wave-step).  Slots past it re-read that block, so
+    // every load is in bounds and no lane needs zero-filling; their results
+    // are never stored.
+    auto last_slot = [&](int64_t step) -> int {
         const int64_t left = nblocks - step * G::BPW;          // wave-uniform
-        if (left >= G::BPW) return lane_elem;
-        const int gl = g < left ? g : (int)left - 1;
-        return (uint32_t)(gl * B + 8 * t);
+        return (int)(left < G::BPW ? left : G::BPW) - 1;
+    };
+    auto lane_offset = [&](int last) -> uint32_t {
+        const int gl = g < last ? g : last;
+        return (uint32_t)(gl * (2 * B) + 16 * t);
     };
     u4v buf[G::CH];
     auto load = [&](int64_t step) {
-        const uint16_t *p = x + step * (G::BPW * B) + lane_offset(step);
+        const char *p = xb + step * kStepX + lane_offset(last_slot(step));
 #pragma unroll
-        for (int k = 0; k < G::CH; ++k) buf[k] = ld16(p + k * G::SPAN);
+        for (int k = 0; k < G::CH; ++k) buf[k] = ld16(p + k * G::SPAN * 2);
     };
 
     if (wave0 < nsteps) load(wave0);
@@ -548,17 +564,17 @@ __global__ __launch_bounds__(kGroup) void compress_kernel(
         asm volatile("" : "+v"(energy));
         if (step + nwaves < nsteps) load(step + nwaves);
 
-        const int64_t blk = step * G::BPW + g;
-        const bool active = blk < nblocks;
+        const int last = last_slot(step);
+        const bool active = g <= last;
 
         energy = block_sum<G::LPB>(energy);
         float unshift = 1.0f;
         if (__builtin_expect(energy >= kBigEnergy, 0)) {
             // Huge block (sum x^2 near or past float32 range): reload it and
             // work on x * 2^-80 (exact), undoing the factor in alpha.
-            const uint16_t *p = x + step * (G::BPW * B) + lane_offset(step);
+            const char *p = xb + step * kStepX + lane_offset(last);
 #pragma unroll
-            for (int k = 0; k < G::CH; ++k) unpack8(ld16(p + k * G::SPAN), &v[8 * k]);
+            for (int k = 0; k < G::CH; ++k) unpack8(ld16(p + k * G::SPAN * 2), &v[8 * k]);
 #pragma unroll
             for (int i = 0; i < G::EPL; ++i) v[i] *= kBigShift;
             energy = block_sum<G::LPB>(sum_squares<G::EPL>(v));
@@ -584,12 +600,14 @@ __global__ __launch_bounds__(kGroup) void compress_kernel(
         r.lo = (m > 0.0f) ? r.lo * lane_sign : 0.0f;
 
         if (active) {
-            uint8_t *cq = codes + blk * W::kRecord + 8 * t;
+            uint8_t *cq = codes + step * kStepCodes + lane_code;
 #pragma unroll
             for (int k = 0; k < G::CH; ++k) st8(cq + k * G::SPAN, encode8<F>(&v[8 * k], r));
             if (t == 0) {
-                alpha[blk * W::kScalarStride] = a * unshift;
-                scale[blk * W::kScalarStride] = s;
+                const int64_t sb = step * kStepScalars;
+                *reinterpret_cast<float *>(reinterpret_cast<char *>(alpha) + sb + lane_scalar) =
+                    a * unshift;
+                *reinterpret_cast<float *>(reinterpret_cast<char *>(scale) + sb + lane_scalar) = s;
             }
         }
     }
