@@ -69,7 +69,7 @@ def parse():
     p.add_argument("--out", default=None, help="also write the JSON record(s) to this file")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0,
-                   help="minimum CPU time of the oracle baseline")
+                   help="CPU seconds of each leg of the oracle baseline")
     p.add_argument("--copy-probe", action="store_true",
                    help="run only a plain device copy of known size (HBM counter calibration)")
     p.add_argument("--no-graph", action="store_true", help="launch eagerly instead of a HIP graph")
@@ -401,9 +401,51 @@ def owner_case(torch, taco, synth, name: str, block: int, steps: int, warmup: in
             "kernels": {"reduce_compress": t}, "npayloads": npay}
 
 
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown CPU"
+
+
+def _oracle_rate(oracle, parts, block: int, accumulate: bool, min_seconds: float, pool):
+    """Round trips of the oracle over the row parts (concurrently when a
+    thread pool is given: each part is one C call, which releases the GIL),
+    repeated until min_seconds have passed.  Returns (reps, seconds)."""
+    import numpy as np
+
+    def one(part):
+        codes, alpha, scale = oracle.compress(part, block)
+        if accumulate:
+            oracle.decompress_accumulate(codes, alpha, scale, block,
+                                         np.zeros(part.size, np.float32))
+        else:
+            oracle.decompress(codes, alpha, scale, block)
+
+    reps, t = 0, 0.0
+    t0 = time.perf_counter()
+    while t < min_seconds or reps == 0:
+        if pool is None:
+            for part in parts:
+                one(part)
+        else:
+            list(pool.map(one, parts))
+        reps += 1
+        t = time.perf_counter() - t0
+    return reps, t
+
+
 def cpu_baseline(synth, name: str, block: int, min_seconds: float, accumulate: bool):
-    """The oracle (single-threaded C, double precision) on the same workload,
-    round trips repeated until min_seconds of CPU time have passed."""
+    """The oracle (plain C, double precision, unchanged) on a bounded sample
+    of the same workload: once on one thread, then with the sample's rows
+    split over the host's cores (at most 16, the CPU share of one GPU), one
+    oracle call per part and thread.  About min_seconds of CPU time each."""
+    from concurrent.futures import ThreadPoolExecutor
+
     import numpy as np
     import oracle
     r = synth.WORKLOADS[name]
@@ -413,21 +455,21 @@ def cpu_baseline(synth, name: str, block: int, min_seconds: float, accumulate: b
     sample = r.with_shape(rows)
     x = synth.generate(sample)
     n = x.size
-    reps, t = 0, 0.0
-    t0 = time.perf_counter()
-    while t < min_seconds or reps == 0:
-        codes, alpha, scale = oracle.compress(x, block)
-        if accumulate:
-            acc = np.zeros(n, np.float32)
-            oracle.decompress_accumulate(codes, alpha, scale, block, acc)
-        else:
-            oracle.decompress(codes, alpha, scale, block)
-        reps += 1
-        t = time.perf_counter() - t0
-    return {"value": 2.0 * n * reps / t / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"{rows}x{r.cols} rows of {name} (seed {r.seed}), block {block}, "
-                      f"{reps} x (compress + {'accumulate' if accumulate else 'decompress'}) "
-                      f"in {t:.1f} s, one thread"}
+    oracle.compress(x[:1], block)                 # build / load the library once
+    reps1, t1 = _oracle_rate(oracle, [x], block, accumulate, min_seconds, None)
+    threads = max(1, min(16, len(os.sched_getaffinity(0)), rows))
+    parts = np.array_split(x, threads, axis=0)
+    with ThreadPoolExecutor(threads) as pool:
+        repsn, tn = _oracle_rate(oracle, parts, block, accumulate,
+                                 max(1.0, min_seconds / threads), pool)
+    op = "accumulate" if accumulate else "decompress"
+    return {"value": 2.0 * n * repsn / tn / 1e9, "unit": "GB/s", "cores": threads,
+            "kind": "oracle",
+            "single_thread_value": 2.0 * n * reps1 / t1 / 1e9,
+            "sample": f"{rows}x{r.cols} rows of {name} (seed {r.seed}), block {block}; "
+                      f"{repsn} x (compress + {op}) in {tn:.1f} s on {threads} threads "
+                      f"(rows split evenly), {reps1} x in {t1:.1f} s on one thread; "
+                      f"{_cpu_model()}"}
 
 
 def record(res, name: str, args, cpu=None):
