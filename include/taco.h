@@ -37,6 +37,11 @@
  *     returned status covers argument validation and the kernel launch only.
  *     On any error nothing is launched and nothing is written.
  *   - N == 0 is a no-op that returns TACO_OK (pointers may then be NULL).
+ *   - Checks run in this order, and the first that fails decides the status:
+ *     format (FORMAT); tokens, hidden and N (SHAPE); block (BLOCK); N % block
+ *     (SHAPE); target energy, payload count, variant (PARAM); N == 0 (TACO_OK,
+ *     nothing else checked); required pointers (NULL); alignment (ALIGN);
+ *     overlaps (ALIAS); the launch (HIP).
  *   - Inputs must be finite.  Blocks whose RMS exceeds ~2^126 / target_energy
  *     get a subnormal float32 alpha (less precise); non-finite inputs give
  *     unspecified codes and scalars (but never out-of-bounds accesses).
@@ -98,7 +103,7 @@ typedef enum {
 typedef enum {
     TACO_OK = 0,
     TACO_ERR_NULL = 1,   /* a required pointer is NULL                          */
-    TACO_ERR_SHAPE = 2,  /* tokens < 0, hidden <= 0, N overflows, N % block != 0 */
+    TACO_ERR_SHAPE = 2,  /* tokens < 0, hidden <= 0, N > 2^60, N % block != 0    */
     TACO_ERR_BLOCK = 3,  /* block is not one of 32, 64, 128, 256, 512            */
     TACO_ERR_PARAM = 4,  /* target_energy not finite or outside (0, 1e20], a
                             payload count outside 0..TACO_MAX_PAYLOADS, or an
