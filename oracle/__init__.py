@@ -8,6 +8,11 @@ paper leaves open, are documented in ``taco_oracle.c``.
 
 Arrays are numpy arrays: bf16 tensors travel as ``uint16`` bit patterns,
 codes as ``uint8``, alpha / s as ``float32``.
+
+``TACO_ORACLE_MUTANT``, when set, names a build of a deliberately broken
+copy of ``taco_oracle.c`` to load instead: ``tests/test_oracle_mutants.py``
+uses it to show that the pins catch each planted mistake.  Nothing else sets
+it.
 """
 from __future__ import annotations
 
@@ -42,7 +47,7 @@ def build(force: bool = False) -> str:
 def _load():
     global _lib
     if _lib is None:
-        lib = ctypes.CDLL(build())
+        lib = ctypes.CDLL(os.environ.get("TACO_ORACLE_MUTANT") or build())
         P = ctypes.c_void_p
         i64, i32, f64 = ctypes.c_int64, ctypes.c_int, ctypes.c_double
         lib.taco_oracle_e4m3_decode.argtypes = [ctypes.c_uint8]
