@@ -7,8 +7,9 @@
 // 4.2.2 (Eq. 5-8), section 4.3 (Eq. 9-13), Algorithm 1 and section 4.4.1
 // (one fused kernel per direction).  The C ABI is documented in taco.h.
 //
-// Design (gfx950, wave64, no LDS, no MFMA: the path streams HBM and does
-// O(B log B) adds per block, nothing here is a dense contraction):
+// Design (gfx950, wave64, no MFMA: the path streams HBM and does O(B log B)
+// adds per block, nothing here is a dense contraction; the transform needs no
+// LDS, which only stages interleaved records and the fidelity sums):
 //
 //  * Lane layout.  A block of B elements is owned by LPB = 8 lanes of one
 //    wavefront (4 lanes when B = 32).  Lane t of a block holds the 16-byte
@@ -41,8 +42,13 @@
 //  * Grid-stride loop over wave-steps (one step per wave by default, so a
 //    large tensor launches tens of thousands of work-groups); when a wave
 //    has several steps, the next step's loads are issued before the current
-//    step is processed.  Loads and stores are non-temporal: every byte is
-//    streamed once.
+//    step is processed.  Every byte is streamed once; the cache policy of
+//    each access (non-temporal or not) is chosen by measurement below.
+//  * Beyond the operator's two directions: the owner step of the two-shot
+//    all-reduce (reduce_compress_kernel) and the multi-payload accumulate
+//    (accumulate_n_kernel) add payloads in the rotated domain, since
+//    H H = B I; the fidelity round trip (roundtrip_kernel) runs the operator
+//    and its ablation variants with the codes kept in registers.
 
 #pragma once
 
