@@ -70,6 +70,9 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="CPU seconds of each leg of the oracle baseline")
+    p.add_argument("--torch-reference", action="store_true",
+                   help="time torch's elementwise add and copy over the same bytes as each "
+                        "workload's compress (context for the roofline) and exit")
     p.add_argument("--copy-probe", action="store_true",
                    help="run only a plain device copy of known size (HBM counter calibration)")
     p.add_argument("--no-graph", action="store_true", help="launch eagerly instead of a HIP graph")
@@ -532,6 +535,45 @@ def copy_probe(torch):
     print(json.dumps({"copy_probe_bytes": n, "launches": 3}), flush=True)
 
 
+def torch_reference(torch, synth, cases, use_graph: bool):
+    """Context for the roofline: torch's own elementwise kernels moving the
+    same bytes as compress at each workload's size (add of two bf16 halves:
+    reads 2N bytes, writes N, the compress mix 2:1) and a plain bf16 copy
+    (reads 2N, writes 2N), timed like the operator's kernels (buffer sets
+    rotated over more than 1 GiB of loads, HIP graphs, events).  One JSON
+    line per workload."""
+    timer = Timer(torch)
+    for name, _block in cases:
+        n = synth.WORKLOADS[name.split(":")[0]].numel
+        out = {"torch_reference": name, "elements": n}
+        nsets = rotation_sets(2 * n, 3 * n)
+        sets = [tuple(torch.ones(n // 2, dtype=torch.bfloat16, device="cuda") for _ in range(3))
+                for _ in range(nsets)]
+
+        def add_all():
+            for a, b, c in sets:
+                torch.add(a, b, out=c)
+        fn = make_graph(torch, add_all, use_graph)
+        t = timer.time(fn, 20) / (20 * nsets)
+        out["add_2to1"] = {"bytes": 3 * n, "us": round(t * 1e6, 3),
+                           "GBps": round(3 * n / t / 1e9, 1)}
+        del sets, fn
+        nsets = rotation_sets(2 * n, 4 * n)
+        sets = [(torch.ones(n, dtype=torch.bfloat16, device="cuda"),
+                 torch.empty(n, dtype=torch.bfloat16, device="cuda")) for _ in range(nsets)]
+
+        def copy_all():
+            for a, c in sets:
+                c.copy_(a)
+        fn = make_graph(torch, copy_all, use_graph)
+        t = timer.time(fn, 20) / (20 * nsets)
+        out["copy_1to1"] = {"bytes": 4 * n, "us": round(t * 1e6, 3),
+                            "GBps": round(4 * n / t / 1e9, 1)}
+        del sets, fn
+        torch.cuda.empty_cache()
+        print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     args.steps = max(1, args.steps)
@@ -551,6 +593,12 @@ def main():
     import synth
 
     use_graph = not args.no_graph
+    if args.torch_reference:
+        names = [args.workload] if args.workload else [
+            "laplace_2048x1024", "gpt2.7b_rowpar_8192x2560", "qwen7b_act_16384x3584",
+            "grad_8192x8192", "gpt175b_hidden_32768x12288"]
+        torch_reference(torch, synth, [(nm, None) for nm in names], use_graph)
+        return
     if args.all:
         cases = [("laplace_2048x1024", 128), ("gpt2.7b_rowpar_8192x2560", 128),
                  ("qwen7b_act_16384x3584", 128), ("qwen7b_act_16384x3584", 256),
