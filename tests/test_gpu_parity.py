@@ -293,6 +293,7 @@ def test_workload_gpt175b_accumulate_four_payloads(taco):
         st = compare_compress(xb, B, codes.view(M, B)[tidx].cpu().numpy(),
                               alpha[tidx].cpu().numpy(), scale[tidx].cpu().numpy())
         o_c, o_a, o_s = st.pop("oracle")
+        print(name, B, f"payload seed {p_seed}", st, flush=True)
         oracle.decompress_accumulate(o_c, o_a, o_s, B, ref)
         del x, codes, alpha, scale
     got = acc.view(M, B)[tidx].cpu().numpy().reshape(-1)
