@@ -743,6 +743,78 @@ __global__ __launch_bounds__(kGroup) void compress_packed_kernel(
     }
 }
 
+// ------------------------------------------------ float32 accumulator -----
+
+// The accumulator update acc += G' of one wave-step, staged through LDS.  A
+// lane holds its block's values as runs of 8 elements, 8 * LPB elements
+// apart, so direct 16-byte read-modify-writes would cover only half of
+// every 32-byte sector per instruction (measured: ~5 % more HBM writes and
+// ~3 % more reads than the accumulator's bytes).  Instead the wave writes
+// its G' to a wave-private LDS region in element order, then updates the
+// accumulator in contiguous 16-byte pieces, 1 KiB per instruction.  A pass
+// stages at most 2048 floats (8 KiB per wave), so B = 512 takes two passes.
+template <int B>
+struct AccStage {
+    static constexpr int kBpw = Geo<B>::BPW;
+    static constexpr int kBlocks = (kBpw * B <= 2048) ? kBpw : 2048 / B;  // blocks per pass
+    static constexpr int kElems = kBlocks * B;                             // floats per wave
+    static constexpr int kPasses = kBpw / kBlocks;
+    static_assert(kPasses * kBlocks == kBpw && kElems % (4 * kWave) == 0, "stage layout");
+};
+
+// acc[step's elements] += v (the lane's G' values, final float32 products);
+// slots past the last block (g beyond it) are not written.  stg: this
+// wave's AccStage<B>::kElems floats of LDS.
+template <int B>
+__device__ __forceinline__ void acc_update_staged(float *stg, float *__restrict__ acc,
+                                                  int64_t step, int64_t nblocks,
+                                                  const float (&v)[Geo<B>::EPL], int g, int t,
+                                                  int lane) {
+    using G = Geo<B>;
+    using S = AccStage<B>;
+    const int64_t left = nblocks - step * G::BPW;                       // wave-uniform
+    const int nvalid = (int)(left < G::BPW ? left : G::BPW) * B;        // elements
+    float *ab = acc + step * (int64_t)(G::BPW * B);
+#pragma unroll
+    for (int pass = 0; pass < S::kPasses; ++pass) {
+        // Every lane has read the previous contents before they are rewritten.
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        const int gl = g - pass * S::kBlocks;
+        if (S::kPasses == 1 || (gl >= 0 && gl < S::kBlocks)) {
+#pragma unroll
+            for (int k = 0; k < G::CH; ++k) {
+                float *sp = stg + gl * B + k * G::SPAN + 8 * t;
+                const float *w = &v[8 * k];
+                *reinterpret_cast<u4v *>(sp) = (u4v){__float_as_uint(w[0]), __float_as_uint(w[1]),
+                                                     __float_as_uint(w[2]), __float_as_uint(w[3])};
+                *reinterpret_cast<u4v *>(sp + 4) =
+                    (u4v){__float_as_uint(w[4]), __float_as_uint(w[5]), __float_as_uint(w[6]),
+                          __float_as_uint(w[7])};
+            }
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        const int base = pass * S::kElems;
+#pragma unroll
+        for (int i0 = 0; i0 < S::kElems; i0 += 4 * kWave) {
+            const int i = i0 + 4 * lane;
+            if (base + i < nvalid) {
+                float *pa = ab + base + i;
+                const u4v p = ld16_acc(pa);
+                const u4v q = *reinterpret_cast<const u4v *>(stg + i);
+                u4v o;
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    o[j] = __float_as_uint(__uint_as_float(p[j]) + __uint_as_float(q[j]));
+                st16(pa, o);
+            }
+        }
+    }
+}
+
 // --------------------------------------------------------- decompress -----
 
 template <int B, Fmt F, Out MODE, Layout L>
@@ -752,6 +824,9 @@ __global__ __launch_bounds__(kGroup) void decompress_kernel(
     float *__restrict__ acc) {
     using G = Geo<B>;
     using W = Wire<B, L>;
+    constexpr bool kAcc = MODE == Out::kAccumulate;
+    __shared__ __align__(16) float stage_all[kAcc ? kWavesPerGroup : 1][kAcc ? AccStage<B>::kElems : 4];
+    float *stage = stage_all[kAcc ? __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) : 0];
     const int lane = threadIdx.x & (kWave - 1);
     const int t = lane_sub<G::LPB>(lane);
     const int g = lane_slot<G::LPB>(lane);
@@ -807,31 +882,16 @@ __global__ __launch_bounds__(kGroup) void decompress_kernel(
             for (int i = 0; i < G::EPL; ++i) v[i] *= f;
         }
 
-        if (active) {
+        if constexpr (kAcc) {
+            acc_update_staged<B>(stage, acc, step, nblocks, v, g, t, lane);
+        } else if (active) {
             const int64_t e0 = blk * B + 8 * t;
-            if (MODE == Out::kBf16) {
 #pragma unroll
-                for (int k = 0; k < G::CH; ++k) {
-                    const float *w = &v[8 * k];
-                    const u4v o = {pack_bf16x2(w[0], w[1]), pack_bf16x2(w[2], w[3]),
-                                   pack_bf16x2(w[4], w[5]), pack_bf16x2(w[6], w[7])};
-                    st16(y + e0 + k * G::SPAN, o);
-                }
-            } else {
-#pragma unroll
-                for (int k = 0; k < G::CH; ++k) {
-                    const float *w = &v[8 * k];
-                    float *pa = acc + e0 + k * G::SPAN;
-                    const u4v p0 = ld16_acc(pa), p1 = ld16_acc(pa + 4);
-                    u4v o0, o1;
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        o0[j] = __float_as_uint(__uint_as_float(p0[j]) + w[j]);
-                        o1[j] = __float_as_uint(__uint_as_float(p1[j]) + w[4 + j]);
-                    }
-                    st16(pa, o0);
-                    st16(pa + 4, o1);
-                }
+            for (int k = 0; k < G::CH; ++k) {
+                const float *w = &v[8 * k];
+                const u4v o = {pack_bf16x2(w[0], w[1]), pack_bf16x2(w[2], w[3]),
+                               pack_bf16x2(w[4], w[5]), pack_bf16x2(w[6], w[7])};
+                st16(y + e0 + k * G::SPAN, o);
             }
         }
     }
@@ -1034,6 +1094,8 @@ __global__ __launch_bounds__(kGroup) void accumulate_n_kernel(Payloads pay, int6
     using G = Geo<B>;
     using W = Wire<B, L>;
     using C = Codec<F>;
+    __shared__ __align__(16) float stage_all[kWavesPerGroup][AccStage<B>::kElems];
+    float *stage = stage_all[__builtin_amdgcn_readfirstlane(threadIdx.x >> 6)];
     const int lane = threadIdx.x & (kWave - 1);
     const int t = lane_sub<G::LPB>(lane);
     const int g = lane_slot<G::LPB>(lane);
@@ -1108,24 +1170,9 @@ __global__ __launch_bounds__(kGroup) void accumulate_n_kernel(Payloads pay, int6
         // Undo the shift and divide by B (both powers of two: one rounding,
         // in the final product).
         const float fo = (kInvB / shift) * lane_sign;
-
-        const int64_t blk = step * G::BPW + g;
-        if (blk < nblocks) {
-            const int64_t e0 = blk * B + 8 * t;
 #pragma unroll
-            for (int k = 0; k < G::CH; ++k) {
-                float *pa = acc + e0 + k * G::SPAN;
-                const u4v p0 = ld16_acc(pa), p1 = ld16_acc(pa + 4);
-                u4v o0, o1;
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    o0[j] = __float_as_uint(__uint_as_float(p0[j]) + v[8 * k + j] * fo);
-                    o1[j] = __float_as_uint(__uint_as_float(p1[j]) + v[8 * k + 4 + j] * fo);
-                }
-                st16(pa, o0);
-                st16(pa + 4, o1);
-            }
-        }
+        for (int i = 0; i < G::EPL; ++i) v[i] *= fo;
+        acc_update_staged<B>(stage, acc, step, nblocks, v, g, t, lane);
     }
 }
 
