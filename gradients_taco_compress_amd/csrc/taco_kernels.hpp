@@ -500,6 +500,74 @@ constexpr float kTinyOut = 0x1p-100f;
 constexpr float kOutShift = 0x1p64f;
 constexpr float kOutUnshift = 0x1p-64f;
 
+// ------------------------------------------------- staged code traffic ----
+
+// A lane's codes of a block are 8-byte runs 8 * LPB bytes apart, so direct
+// 8-byte stores or loads move 512 bytes per instruction in 64-byte pieces.
+// Staged through a wave-private LDS region (the wave-step's BPW * B code
+// bytes in element order), every instruction moves 1 KiB of contiguous
+// codes.  Measured: compress 1-3 % faster from 112 MiB up, even at 40 MiB,
+// 0.06 us slower on a 4 MiB tensor; the owner step 1-2 % faster; decompress
+// 2-3 % faster for B >= 256 and slower for B = 128, so the receive side
+// stages only from B = 256 up.  Side-buffer layout only.
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Store the wave-step's codes c (lane's runs) to cb, the step's first code
+// byte; only the first nvalid bytes (whole blocks) are written.
+template <int B>
+__device__ __forceinline__ void codes_store_staged(uint8_t *stg, uint8_t *__restrict__ cb,
+                                                   int nvalid, const u2v (&c)[Geo<B>::CH],
+                                                   int g, int t, int lane) {
+    using G = Geo<B>;
+    wave_lds_sync();                   // earlier readers of the stage are done
+#pragma unroll
+    for (int k = 0; k < G::CH; ++k)
+        *reinterpret_cast<u2v *>(stg + g * B + k * G::SPAN + 8 * t) = c[k];
+    wave_lds_sync();
+#pragma unroll
+    for (int i0 = 0; i0 < G::BPW * B; i0 += 16 * kWave) {
+        const int i = i0 + 16 * lane;
+        if (i < nvalid) st16(cb + i, *reinterpret_cast<const u4v *>(stg + i));
+    }
+}
+
+// The receive side in two halves: issue the contiguous loads (bytes past
+// nvalid read as zero), and later hand each lane its runs through LDS.
+template <int B>
+struct CodesLoad {
+    static constexpr int kBytes = Geo<B>::BPW * B;
+    static constexpr int kPieces = (kBytes + 16 * kWave - 1) / (16 * kWave);
+};
+template <int B>
+__device__ __forceinline__ void codes_load_issue(const uint8_t *__restrict__ cb, int nvalid,
+                                                 u4v (&raw)[CodesLoad<B>::kPieces], int lane) {
+#pragma unroll
+    for (int c = 0; c < CodesLoad<B>::kPieces; ++c) {
+        const int i = c * 16 * kWave + 16 * lane;
+        raw[c] = (i < nvalid) ? ld16(cb + i) : (u4v){0u, 0u, 0u, 0u};
+    }
+}
+template <int B>
+__device__ __forceinline__ void codes_load_finish(uint8_t *stg,
+                                                  const u4v (&raw)[CodesLoad<B>::kPieces],
+                                                  u2v (&c)[Geo<B>::CH], int g, int t, int lane) {
+    using G = Geo<B>;
+    wave_lds_sync();
+#pragma unroll
+    for (int p = 0; p < CodesLoad<B>::kPieces; ++p) {
+        const int i = p * 16 * kWave + 16 * lane;
+        if (i < CodesLoad<B>::kBytes) *reinterpret_cast<u4v *>(stg + i) = raw[p];
+    }
+    wave_lds_sync();
+#pragma unroll
+    for (int k = 0; k < G::CH; ++k)
+        c[k] = *reinterpret_cast<const u2v *>(stg + g * B + k * G::SPAN + 8 * t);
+}
+
 // ----------------------------------------------------------- compress -----
 
 template <int B, Fmt F, Layout L>
@@ -508,6 +576,9 @@ __global__ __launch_bounds__(kGroup) void compress_kernel(
     uint8_t *__restrict__ codes, float *__restrict__ alpha, float *__restrict__ scale) {
     using G = Geo<B>;
     using W = Wire<B, L>;
+    constexpr bool kStage = L == Layout::kSide;     // staged code stores
+    __shared__ __align__(16) uint8_t stage_all[kStage ? kWavesPerGroup : 1][kStage ? G::BPW * B : 16];
+    uint8_t *stage = stage_all[kStage ? __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) : 0];
     const int lane = threadIdx.x & (kWave - 1);
     const int t = lane_sub<G::LPB>(lane);
     const int g = lane_slot<G::LPB>(lane);
@@ -605,10 +676,18 @@ __global__ __launch_bounds__(kGroup) void compress_kernel(
         r.hi = (m > 0.0f) ? r.hi * lane_sign : 0.0f;
         r.lo = (m > 0.0f) ? r.lo * lane_sign : 0.0f;
 
-        if (active) {
-            uint8_t *cq = codes + step * kStepCodes + lane_code;
+        if constexpr (kStage) {
+            u2v c[G::CH];
 #pragma unroll
-            for (int k = 0; k < G::CH; ++k) st8(cq + k * G::SPAN, encode8<F>(&v[8 * k], r));
+            for (int k = 0; k < G::CH; ++k) c[k] = encode8<F>(&v[8 * k], r);
+            codes_store_staged<B>(stage, codes + step * kStepCodes, (last + 1) * B, c, g, t, lane);
+        }
+        if (active) {
+            if constexpr (!kStage) {
+                uint8_t *cq = codes + step * kStepCodes + lane_code;
+#pragma unroll
+                for (int k = 0; k < G::CH; ++k) st8(cq + k * G::SPAN, encode8<F>(&v[8 * k], r));
+            }
             if (t == 0) {
                 const int64_t sb = step * kStepScalars;
                 *reinterpret_cast<float *>(reinterpret_cast<char *>(alpha) + sb + lane_scalar) =
@@ -825,8 +904,15 @@ __global__ __launch_bounds__(kGroup) void decompress_kernel(
     using G = Geo<B>;
     using W = Wire<B, L>;
     constexpr bool kAcc = MODE == Out::kAccumulate;
-    __shared__ __align__(16) float stage_all[kAcc ? kWavesPerGroup : 1][kAcc ? AccStage<B>::kElems : 4];
-    float *stage = stage_all[kAcc ? __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) : 0];
+    constexpr bool kCodes = L == Layout::kSide && B >= 256;   // staged code loads
+    // One LDS region per wave serves both stages (codes first, then G').
+    constexpr int kAccBytes = kAcc ? AccStage<B>::kElems * 4 : 0;
+    constexpr int kCodeBytes = kCodes ? CodesLoad<B>::kBytes : 0;
+    constexpr int kStageBytes = kAccBytes > kCodeBytes ? kAccBytes : kCodeBytes;
+    constexpr bool kAny = kStageBytes > 0;
+    __shared__ __align__(16) uint8_t stage_all[kAny ? kWavesPerGroup : 1][kAny ? kStageBytes : 16];
+    uint8_t *stage_b = stage_all[kAny ? __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) : 0];
+    float *stage = reinterpret_cast<float *>(stage_b);
     const int lane = threadIdx.x & (kWave - 1);
     const int t = lane_sub<G::LPB>(lane);
     const int g = lane_slot<G::LPB>(lane);
@@ -843,20 +929,29 @@ __global__ __launch_bounds__(kGroup) void decompress_kernel(
     const int64_t nwaves = (int64_t)gridDim.x * kWavesPerGroup;
 
     // Slots past the last block re-read the last block (never stored).
+    // (With staged code loads those slots decode zeros.)
     u2v buf[G::CH];
+    u4v raw[kCodes ? CodesLoad<B>::kPieces : 1];
     float a_buf = 1.0f, s_buf = 0.0f;
     auto load = [&](int64_t step) {
         int64_t blk = step * G::BPW + g;
         blk = blk < nblocks ? blk : nblocks - 1;
-        const uint8_t *p = codes + blk * W::kRecord + 8 * t;
+        if constexpr (kCodes) {
+            const int64_t left = nblocks - step * G::BPW;
+            codes_load_issue<B>(codes + step * (int64_t)(G::BPW * B),
+                                (int)(left < G::BPW ? left : G::BPW) * B, raw, lane);
+        } else {
+            const uint8_t *p = codes + blk * W::kRecord + 8 * t;
 #pragma unroll
-        for (int k = 0; k < G::CH; ++k) buf[k] = ld8(p + k * G::SPAN);
+            for (int k = 0; k < G::CH; ++k) buf[k] = ld8(p + k * G::SPAN);
+        }
         a_buf = alpha[blk * W::kScalarStride];
         s_buf = scale[blk * W::kScalarStride];
     };
 
     if (wave0 < nsteps) load(wave0);
     for (int64_t step = wave0; step < nsteps; step += nwaves) {
+        if constexpr (kCodes) codes_load_finish<B>(stage_b, raw, buf, g, t, lane);
         float v[G::EPL];
 #pragma unroll
         for (int k = 0; k < G::CH; ++k) C::decode8(buf[k], &v[8 * k]);   // Eq. 11 (before * s)
@@ -912,6 +1007,9 @@ __global__ __launch_bounds__(kGroup) void reduce_compress_kernel(
     uint8_t *__restrict__ codes, float *__restrict__ alpha, float *__restrict__ scale) {
     using G = Geo<B>;
     using W = Wire<B, L>;
+    constexpr bool kStage = L == Layout::kSide;     // staged code stores
+    __shared__ __align__(16) uint8_t stage_all[kStage ? kWavesPerGroup : 1][kStage ? G::BPW * B : 16];
+    uint8_t *stage = stage_all[kStage ? __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) : 0];
     const int lane = threadIdx.x & (kWave - 1);
     const int t = lane_sub<G::LPB>(lane);
     const int g = lane_slot<G::LPB>(lane);
@@ -1070,10 +1168,20 @@ __global__ __launch_bounds__(kGroup) void reduce_compress_kernel(
         r.lo = (m > 0.0f) ? r.lo * lane_sign : 0.0f;
 
         const int64_t blk = step * G::BPW + g;
-        if (blk < nblocks) {
-            uint8_t *cq = codes + blk * W::kRecord + 8 * t;
+        if constexpr (kStage) {
+            u2v c[G::CH];
 #pragma unroll
-            for (int k = 0; k < G::CH; ++k) st8(cq + k * G::SPAN, encode8<F>(&v[8 * k], r));
+            for (int k = 0; k < G::CH; ++k) c[k] = encode8<F>(&v[8 * k], r);
+            const int64_t left = nblocks - step * G::BPW;
+            codes_store_staged<B>(stage, codes + step * (int64_t)(G::BPW * B),
+                                  (int)(left < G::BPW ? left : G::BPW) * B, c, g, t, lane);
+        }
+        if (blk < nblocks) {
+            if constexpr (!kStage) {
+                uint8_t *cq = codes + blk * W::kRecord + 8 * t;
+#pragma unroll
+                for (int k = 0; k < G::CH; ++k) st8(cq + k * G::SPAN, encode8<F>(&v[8 * k], r));
+            }
             if (t == 0) {
                 alpha[blk * W::kScalarStride] = a * unshift;
                 scale[blk * W::kScalarStride] = s;
