@@ -570,6 +570,8 @@ def decompress_packed(payload, shape, block: int = 256, out=None, stream=None,
     if out is None:
         out = torch.empty(shape, dtype=torch.bfloat16, device=payload.device)
     _need(out, torch.bfloat16, "out")
+    if out.numel() != tokens * hidden:
+        raise ValueError("out must have as many elements as the shape")
     if fmt == "e4m3":
         st = taco_decompress_packed(payload.data_ptr(), tokens, hidden, block, out.data_ptr(),
                                     _stream(stream, payload, out))
@@ -623,6 +625,8 @@ def reduce_compress_packed(own, payloads, shape=None, block: int = 256,
     if out is None:
         out = torch.empty(nb, dtype=torch.uint8, device=dev)
     _need(out, torch.uint8, "out")
+    if out.numel() < nb:
+        raise ValueError("out is too small for this shape's payload")
     n = len(payloads)
     args = (0 if own is None else own.data_ptr(), n,
             [p.data_ptr() for p in payloads] if n else None, tokens, hidden, block,
@@ -642,6 +646,8 @@ def e4m3_encode(x, out=None, stream=None):
     if out is None:
         out = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
     _need(out, torch.uint8, "out")
+    if out.numel() != x.numel():
+        raise ValueError("out must have as many elements as x")
     _check(taco_e4m3_encode(x.data_ptr(), x.numel(), out.data_ptr(), _stream(stream, x, out)),
            "taco_e4m3_encode")
     return out
@@ -654,6 +660,8 @@ def e4m3_decode(codes, out=None, stream=None):
     if out is None:
         out = torch.empty(codes.shape, dtype=torch.float32, device=codes.device)
     _need(out, torch.float32, "out")
+    if out.numel() != codes.numel():
+        raise ValueError("out must have as many elements as codes")
     _check(taco_e4m3_decode(codes.data_ptr(), codes.numel(), out.data_ptr(), _stream(stream, codes, out)),
            "taco_e4m3_decode")
     return out
@@ -667,6 +675,8 @@ def encode(x, fmt: str = "e4m3", out=None, stream=None):
     if out is None:
         out = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
     _need(out, torch.uint8, "out")
+    if out.numel() != x.numel():
+        raise ValueError("out must have as many elements as x")
     _check(taco_encode(f, x.data_ptr(), x.numel(), out.data_ptr(), _stream(stream, x, out)), "taco_encode")
     return out
 
@@ -679,6 +689,8 @@ def decode(codes, fmt: str = "e4m3", out=None, stream=None):
     if out is None:
         out = torch.empty(codes.shape, dtype=torch.float32, device=codes.device)
     _need(out, torch.float32, "out")
+    if out.numel() != codes.numel():
+        raise ValueError("out must have as many elements as codes")
     _check(taco_decode(f, codes.data_ptr(), codes.numel(), out.data_ptr(), _stream(stream, codes, out)),
            "taco_decode")
     return out

@@ -535,6 +535,39 @@ __device__ __forceinline__ void codes_store_staged(uint8_t *stg, uint8_t *__rest
     }
 }
 
+// The interleaved layout's records of one wave-step (BPW * (B + 8) bytes,
+// a multiple of 64) assembled in LDS from the lanes' code runs and each
+// block's alpha and s (written by lane t = 0), then stored 16 bytes per lane
+// (first nvalid bytes only): direct 8-byte stores of B + 8-byte records
+// straddle lines (measured: the owner step ~15 % slower than on side
+// buffers).  rb is the step's first record.
+template <int B>
+__device__ __forceinline__ void records_store_staged(uint8_t *stg, uint8_t *__restrict__ rb,
+                                                     int nvalid, const u2v (&c)[Geo<B>::CH],
+                                                     float a, float s, int g, int t, int lane) {
+    using G = Geo<B>;
+    constexpr int kRec = B + 8;
+    wave_lds_sync();
+    uint8_t *rec = stg + g * kRec;
+#pragma unroll
+    for (int k = 0; k < G::CH; ++k) *reinterpret_cast<u2v *>(rec + k * G::SPAN + 8 * t) = c[k];
+    if (t == 0) {
+        *reinterpret_cast<float *>(rec + B) = a;
+        *reinterpret_cast<float *>(rec + B + 4) = s;
+    }
+    wave_lds_sync();
+    // nvalid is a multiple of 8 (whole records) but not always of 16: the
+    // last piece may be an 8-byte one.
+#pragma unroll
+    for (int i0 = 0; i0 < G::BPW * kRec; i0 += 16 * kWave) {
+        const int i = i0 + 16 * lane;
+        if (i + 16 <= nvalid)
+            st16(rb + i, *reinterpret_cast<const u4v *>(stg + i));
+        else if (i < nvalid)
+            st8(rb + i, *reinterpret_cast<const u2v *>(stg + i));
+    }
+}
+
 // The receive side in two halves: issue the contiguous loads (bytes past
 // nvalid read as zero), and later hand each lane its runs through LDS.
 template <int B>
@@ -1007,9 +1040,9 @@ __global__ __launch_bounds__(kGroup) void reduce_compress_kernel(
     uint8_t *__restrict__ codes, float *__restrict__ alpha, float *__restrict__ scale) {
     using G = Geo<B>;
     using W = Wire<B, L>;
-    constexpr bool kStage = L == Layout::kSide;     // staged code stores
-    __shared__ __align__(16) uint8_t stage_all[kStage ? kWavesPerGroup : 1][kStage ? G::BPW * B : 16];
-    uint8_t *stage = stage_all[kStage ? __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) : 0];
+    // Codes (side buffers) or whole records (interleaved) leave through LDS.
+    __shared__ __align__(16) uint8_t stage_all[kWavesPerGroup][G::BPW * W::kRecord];
+    uint8_t *stage = stage_all[__builtin_amdgcn_readfirstlane(threadIdx.x >> 6)];
     const int lane = threadIdx.x & (kWave - 1);
     const int t = lane_sub<G::LPB>(lane);
     const int g = lane_slot<G::LPB>(lane);
@@ -1168,24 +1201,20 @@ __global__ __launch_bounds__(kGroup) void reduce_compress_kernel(
         r.lo = (m > 0.0f) ? r.lo * lane_sign : 0.0f;
 
         const int64_t blk = step * G::BPW + g;
-        if constexpr (kStage) {
-            u2v c[G::CH];
+        u2v c[G::CH];
 #pragma unroll
-            for (int k = 0; k < G::CH; ++k) c[k] = encode8<F>(&v[8 * k], r);
-            const int64_t left = nblocks - step * G::BPW;
-            codes_store_staged<B>(stage, codes + step * (int64_t)(G::BPW * B),
-                                  (int)(left < G::BPW ? left : G::BPW) * B, c, g, t, lane);
-        }
-        if (blk < nblocks) {
-            if constexpr (!kStage) {
-                uint8_t *cq = codes + blk * W::kRecord + 8 * t;
-#pragma unroll
-                for (int k = 0; k < G::CH; ++k) st8(cq + k * G::SPAN, encode8<F>(&v[8 * k], r));
+        for (int k = 0; k < G::CH; ++k) c[k] = encode8<F>(&v[8 * k], r);
+        const int nvalid = (int)(left < G::BPW ? left : G::BPW);            // blocks
+        uint8_t *rb = codes + step * (int64_t)(G::BPW * W::kRecord);
+        if constexpr (L == Layout::kSide) {
+            codes_store_staged<B>(stage, rb, nvalid * B, c, g, t, lane);
+            if (blk < nblocks && t == 0) {
+                alpha[blk] = a * unshift;
+                scale[blk] = s;
             }
-            if (t == 0) {
-                alpha[blk * W::kScalarStride] = a * unshift;
-                scale[blk * W::kScalarStride] = s;
-            }
+        } else {
+            records_store_staged<B>(stage, rb, nvalid * (int)W::kRecord, c, a * unshift, s, g, t,
+                                    lane);
         }
     }
 }
