@@ -18,7 +18,8 @@ the dominant kernel and the CPU oracle's rate on the same workload.
     python bench.py --all --out results.json     # every workload (stderr table)
 
 ``NAME:owner`` times the fused owner step of the two-shot all-reduce
-(``taco_reduce_compress`` of an own partial plus three payloads) instead;
+(``taco_reduce_compress`` of an own partial plus three payloads) instead,
+``NAME:owner_packed`` the same on interleaved records;
 ``NAME:packed`` the round trip through the interleaved wire layout;
 ``NAME:e5m2`` and ``NAME:int8`` the round trip with E5M2 or INT8 codes;
 ``NAME:accn`` (the four-payload workload) sums the four payloads with one
@@ -367,10 +368,11 @@ def accumulate_case(torch, taco, synth, name: str, block: int, steps: int, warmu
 
 
 def owner_case(torch, taco, synth, name: str, block: int, steps: int, warmup: int,
-               use_graph: bool):
+               use_graph: bool, packed: bool = False):
     """Owner step of the two-shot all-reduce: own bf16 partial plus three
     received payloads (four independently seeded tensors) reduced and
-    compressed again in one taco_reduce_compress call."""
+    compressed again in one taco_reduce_compress call (with packed, on
+    interleaved records: taco_reduce_compress_packed)."""
     import numpy as np
     r = synth.WORKLOADS[name]
     n = r.numel
@@ -380,14 +382,19 @@ def owner_case(torch, taco, synth, name: str, block: int, steps: int, warmup: in
     pay = []
     for seed in seeds[1:]:
         x = torch.from_numpy(synth.generate(r, seed=seed).view(np.int16)).cuda().view(torch.bfloat16)
-        pay.append(taco.compress(x, block=block))
+        pay.append(taco.compress_packed(x, block=block) if packed else taco.compress(x, block=block))
         del x
     codes = torch.empty((r.rows, r.cols), dtype=torch.uint8, device="cuda")
     alpha = torch.empty(m, dtype=torch.float32, device="cuda")
     scale = torch.empty(m, dtype=torch.float32, device="cuda")
+    out = torch.empty(taco.taco_packed_bytes(r.rows, r.cols, block), dtype=torch.uint8,
+                      device="cuda") if packed else None
 
     def run_steps():
-        taco.reduce_compress(own, pay, block=block, codes=codes, alpha=alpha, scale=scale)
+        if packed:
+            taco.reduce_compress_packed(own, pay, block=block, out=out)
+        else:
+            taco.reduce_compress(own, pay, block=block, codes=codes, alpha=alpha, scale=scale)
 
     for _ in range(warmup):
         run_steps()
@@ -401,7 +408,7 @@ def owner_case(torch, taco, synth, name: str, block: int, steps: int, warmup: in
     kbytes = 2.0 * n + npay * (n + 8.0 * n / block) + n + 8.0 * n / block
     return {"n": n, "block": block, "steps": reps, "t_step": t, "sets": 1, "rows": r.rows,
             "cols": r.cols, "bytes_step": kbytes, "input_bytes_step": 2.0 * n,
-            "kernels": {"reduce_compress": t}, "npayloads": npay}
+            "kernels": {"reduce_compress": t}, "npayloads": npay, "packed": packed}
 
 
 def _cpu_model() -> str:
@@ -485,7 +492,10 @@ def record(res, name: str, args, cpu=None):
     kbytes = algorithmic_bytes(op, res["n"], res["block"])
     achieved = kbytes / dur / 1e9
     fmt = res.get("format", "e4m3")
-    traffic = traffic_for(kern if fmt == "e4m3" else f"{kern}[{fmt}]", name, res["block"])
+    key = kern if fmt == "e4m3" else f"{kern}[{fmt}]"
+    if res.get("packed"):
+        key += "[packed]"           # counters are taken for the side-buffer kernels only
+    traffic = traffic_for(key, name, res["block"])
     rec = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -504,7 +514,8 @@ def record(res, name: str, args, cpu=None):
                    "step": ("4x compress + 1x decompress_accumulate_n of 4 payloads"
                             if res.get("fused")
                             else "4x compress + 4x decompress_accumulate" if "t_accumulate" in res
-                            else f"reduce_compress of own + {res['npayloads']} payloads"
+                            else (f"reduce_compress{'_packed' if res.get('packed') else ''} "
+                                  f"of own + {res['npayloads']} payloads")
                             if "npayloads" in res
                             else "compress_packed + decompress_packed" if res.get("packed")
                             else "roundtrip with error sums (fidelity study)"
@@ -604,6 +615,7 @@ def main():
                  ("qwen7b_act_16384x3584", 128), ("qwen7b_act_16384x3584", 256),
                  ("grad_8192x8192", 256), ("gpt175b_hidden_32768x12288", 256),
                  ("gpt175b_hidden_32768x12288:owner", 256),
+                 ("gpt175b_hidden_32768x12288:owner_packed", 256),
                  ("gpt175b_hidden_32768x12288:accn", 256),
                  ("gpt2.7b_rowpar_8192x2560:packed", 128),
                  ("gpt2.7b_rowpar_8192x2560:e5m2", 128),
@@ -618,9 +630,10 @@ def main():
         print(f"[bench] {name} block {block}", file=sys.stderr, flush=True)
         acc = name.startswith("gpt175b")
         steps = args.steps if not acc else max(1, min(args.steps, 10))
-        if name.endswith(":owner"):
-            name = name.split(":")[0]
-            res = owner_case(torch, taco, synth, name, block, steps, args.warmup, use_graph)
+        if name.endswith((":owner", ":owner_packed")):
+            name, kind = name.split(":")
+            res = owner_case(torch, taco, synth, name, block, steps, args.warmup, use_graph,
+                             packed=kind == "owner_packed")
             acc = False
         elif name.endswith(":packed"):
             name = name.split(":")[0]
