@@ -145,3 +145,52 @@ def test_binding_refuses_short_outputs(taco):
     with pytest.raises(ValueError):
         taco.decode(torch.zeros(64, dtype=torch.uint8, device="cuda"),
                     out=torch.empty(32, device="cuda"))
+
+
+@pytest.mark.parametrize("B", [128, 256])
+def test_non_finite_inputs_stay_in_bounds(taco, B):
+    """Non-finite inputs give unspecified codes and scalars, but every call
+    still returns TACO_OK and writes only its outputs."""
+    import torch
+    bpw = 8
+    nblocks = 2 * bpw + 5
+    n = B * nblocks
+    announce(f"non-finite inputs 1x{n} B={B}")
+    base = synth.WORKLOADS["laplace_2048x1024"]
+    x = torch.from_numpy(synth.generate(base.with_shape(1, n), seed=90).view(np.int16)).cuda()
+    x = x.view(torch.bfloat16).clone()
+    x[0, 3] = float("nan")
+    x[0, B + 7] = float("inf")
+    x[0, 5 * B] = float("-inf")
+    x[0, 6 * B:7 * B] = float("nan")                 # a whole NaN block
+    m = nblocks
+    nb = taco.taco_packed_bytes(1, n, B)
+    c, cb, ct = guarded(n, torch.uint8, 0xAB)
+    a, ab, at = guarded(m, torch.float32, 12345.0)
+    s, sb, stl = guarded(m, torch.float32, 12345.0)
+    taco.compress(x, block=B, codes=c, alpha=a, scale=s)
+    for buf, k, tail, what in ((cb, n, ct, "codes"), (ab, m, at, "alpha"), (sb, m, stl, "scale")):
+        assert_tail(buf, k, tail, what)
+    pk, pkb, pkt = guarded(nb, torch.uint8, 0xCD)
+    taco.compress_packed(x, block=B, payload=pk)
+    assert_tail(pkb, nb, pkt, "compress_packed")
+    y, yb, yt = guarded(n, torch.bfloat16, 3.0)
+    taco.decompress(c, a, s, block=B, out=y.view(1, n))
+    assert_tail(yb, n, yt, "decompress")
+    acc, accb, acct = guarded(n, torch.float32, 7.0)
+    acc.zero_()
+    taco.decompress_accumulate_n([(c, a, s), (c, a, s)], acc.view(1, n), block=B)
+    assert_tail(accb, n, acct, "decompress_accumulate_n")
+    rp, rpb, rpt = guarded(nb, torch.uint8, 0xCD)
+    taco.reduce_compress_packed(x, [pk], block=B, out=rp)
+    assert_tail(rpb, nb, rpt, "reduce_compress_packed")
+    yr, yrb, yrt = guarded(n, torch.bfloat16, 3.0)
+    taco.roundtrip(x, block=B, variant="tensor", out=yr.view(1, n))
+    assert_tail(yrb, n, yrt, "roundtrip")
+    # Blocks without a non-finite value are unaffected by their neighbours.
+    clean = x.clone()
+    clean[0, :8 * B] = 0.0
+    cc, ca, cs = taco.compress(clean, block=B)
+    fin = torch.isfinite(x.view(nblocks, B).float()).all(dim=1)
+    fin[:8] = False
+    assert torch.equal(cc.view(nblocks, B)[fin], c.view(nblocks, B)[fin])
