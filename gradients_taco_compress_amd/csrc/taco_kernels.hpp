@@ -603,15 +603,16 @@ __device__ __forceinline__ void codes_load_finish(uint8_t *stg,
 
 // ----------------------------------------------------------- compress -----
 
-template <int B, Fmt F, Layout L>
+// Side buffers: codes[N], alpha[M], scale[M].  (The interleaved layout has
+// its own kernel, compress_packed_kernel, below.)
+template <int B, Fmt F>
 __global__ __launch_bounds__(kGroup) void compress_kernel(
     const uint16_t *__restrict__ x, int64_t nblocks, float tau,
     uint8_t *__restrict__ codes, float *__restrict__ alpha, float *__restrict__ scale) {
     using G = Geo<B>;
-    using W = Wire<B, L>;
-    constexpr bool kStage = L == Layout::kSide;     // staged code stores
-    __shared__ __align__(16) uint8_t stage_all[kStage ? kWavesPerGroup : 1][kStage ? G::BPW * B : 16];
-    uint8_t *stage = stage_all[kStage ? __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) : 0];
+    // The wave-step's codes leave through this wave's LDS region.
+    __shared__ __align__(16) uint8_t stage_all[kWavesPerGroup][G::BPW * B];
+    uint8_t *stage = stage_all[__builtin_amdgcn_readfirstlane(threadIdx.x >> 6)];
     const int lane = threadIdx.x & (kWave - 1);
     const int t = lane_sub<G::LPB>(lane);
     const int g = lane_slot<G::LPB>(lane);
@@ -632,11 +633,10 @@ __global__ __launch_bounds__(kGroup) void compress_kernel(
     // plus a 32-bit byte offset of the lane, so the memory instructions take
     // the base in scalar registers and the offset in one vector register.
     const char *const xb = reinterpret_cast<const char *>(x);
-    const uint32_t lane_code = (uint32_t)(g * W::kRecord + 8 * t);
-    const uint32_t lane_scalar = (uint32_t)(g * W::kScalarStride * 4);
+    const uint32_t lane_scalar = (uint32_t)(g * 4);
     constexpr int64_t kStepX = G::BPW * B * 2;                        // bytes of x
-    constexpr int64_t kStepCodes = G::BPW * W::kRecord;
-    constexpr int64_t kStepScalars = G::BPW * W::kScalarStride * 4;
+    constexpr int64_t kStepCodes = G::BPW * B;
+    constexpr int64_t kStepScalars = G::BPW * 4;
 
     // Index of the last block slot of a wave-step that holds a block (BPW - 1
     // except in the final wave-step).  Slots past it re-read that block, so
@@ -709,24 +709,15 @@ __global__ __launch_bounds__(kGroup) void compress_kernel(
         r.hi = (m > 0.0f) ? r.hi * lane_sign : 0.0f;
         r.lo = (m > 0.0f) ? r.lo * lane_sign : 0.0f;
 
-        if constexpr (kStage) {
-            u2v c[G::CH];
+        u2v c[G::CH];
 #pragma unroll
-            for (int k = 0; k < G::CH; ++k) c[k] = encode8<F>(&v[8 * k], r);
-            codes_store_staged<B>(stage, codes + step * kStepCodes, (last + 1) * B, c, g, t, lane);
-        }
-        if (active) {
-            if constexpr (!kStage) {
-                uint8_t *cq = codes + step * kStepCodes + lane_code;
-#pragma unroll
-                for (int k = 0; k < G::CH; ++k) st8(cq + k * G::SPAN, encode8<F>(&v[8 * k], r));
-            }
-            if (t == 0) {
-                const int64_t sb = step * kStepScalars;
-                *reinterpret_cast<float *>(reinterpret_cast<char *>(alpha) + sb + lane_scalar) =
-                    a * unshift;
-                *reinterpret_cast<float *>(reinterpret_cast<char *>(scale) + sb + lane_scalar) = s;
-            }
+        for (int k = 0; k < G::CH; ++k) c[k] = encode8<F>(&v[8 * k], r);
+        codes_store_staged<B>(stage, codes + step * kStepCodes, (last + 1) * B, c, g, t, lane);
+        if (active && t == 0) {
+            const int64_t sb = step * kStepScalars;
+            *reinterpret_cast<float *>(reinterpret_cast<char *>(alpha) + sb + lane_scalar) =
+                a * unshift;
+            *reinterpret_cast<float *>(reinterpret_cast<char *>(scale) + sb + lane_scalar) = s;
         }
     }
 }
@@ -1696,12 +1687,12 @@ taco_status for_block(int32_t block, F &&f) {
 template <int B>
 int64_t steps_of(int64_t nblocks) { return (nblocks + Geo<B>::BPW - 1) / Geo<B>::BPW; }
 
-template <Fmt F, Layout L>
+template <Fmt F>
 struct CompressLaunch {
     const uint16_t *x; int64_t m; float tau; uint8_t *codes; float *alpha; float *scale;
     hipStream_t stream;
     template <int B> taco_status run() const {
-        return launch(reinterpret_cast<const void *>(&compress_kernel<B, F, L>),
+        return launch(reinterpret_cast<const void *>(&compress_kernel<B, F>),
                       grid_for(steps_of<B>(m)), stream, x, m, tau, codes, alpha, scale);
     }
 };
@@ -1766,7 +1757,7 @@ taco_status Ops<F>::compress(Layout layout, int32_t block, const uint16_t *x, in
                              hipStream_t stream) {
     if (layout == Layout::kPacked)   // codes = the payload; alpha / scale point into it
         return for_block(block, CompressPackedLaunch<F>{x, nblocks, tau, codes, stream});
-    return for_block(block, CompressLaunch<F, Layout::kSide>{x, nblocks, tau, codes, alpha, scale,
+    return for_block(block, CompressLaunch<F>{x, nblocks, tau, codes, alpha, scale,
                                                               stream});
 }
 
