@@ -9,7 +9,8 @@
 //
 // Design (gfx950, wave64, no MFMA: the path streams HBM and does O(B log B)
 // adds per block, nothing here is a dense contraction; the transform needs no
-// LDS, which only stages interleaved records and the fidelity sums):
+// LDS, which serves only as a wave-private staging area that makes the
+// memory traffic contiguous, and for the fidelity sums):
 //
 //  * Lane layout.  A block of B elements is owned by LPB = 8 lanes of one
 //    wavefront (4 lanes when B = 32).  Lane t of a block holds the 16-byte
@@ -34,7 +35,8 @@
 //    the kernel rotates the raw block R = H x, reduces sum x^2 and max |R|,
 //    and quantises v = R * (Q / max|R|).  alpha and s are computed once per
 //    block from the two reductions.
-//  * Stores: 8 codes per lane per chunk; alpha / s as float32.  E4M3 and E5M2
+//  * Stores: 8 codes per lane per chunk, gathered per wave-step in LDS and
+//    written as contiguous 16-byte pieces; alpha / s as float32.  E4M3 and E5M2
 //    use the hardware conversions (v_cvt_pk_fp8_f32 / v_cvt_pk_bf8_f32, OCP
 //    formats on gfx950, round to nearest even); INT8 rounds with one float
 //    addition (see Codec<Fmt::kInt8>).  Decompress decodes, rotates and
