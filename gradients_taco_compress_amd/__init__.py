@@ -3,7 +3,7 @@
 The binding only marshals arguments: every step of the operator runs in the
 HIP kernels of ``libtaco.so``.  PyTorch provides device memory and the
 stream; there is no CPU fallback, and importing this package fails loudly if
-the library has not been built (``python -m gradients_taco_compress_amd.build``).
+the library has not been built (``python gradients_taco_compress_amd/build.py``).
 
 Two layers:
 
@@ -69,7 +69,7 @@ except ImportError:  # pragma: no cover - the C ABI itself needs no torch
 if not os.path.exists(LIB_PATH):
     raise ImportError(
         f"libtaco.so is not built ({LIB_PATH} missing); run "
-        "`python -m gradients_taco_compress_amd.build` (there is no CPU fallback)")
+        "`python gradients_taco_compress_amd/build.py` (there is no CPU fallback)")
 
 _lib = ctypes.CDLL(LIB_PATH)
 

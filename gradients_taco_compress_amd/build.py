@@ -1,6 +1,9 @@
 """Build libtaco.so in-tree with hipcc for gfx950.
 
-    python -m gradients_taco_compress_amd.build
+    python gradients_taco_compress_amd/build.py
+
+(run as a script: importing it through the package would load the package,
+which needs the library this builds)
 """
 from __future__ import annotations
 
