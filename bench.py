@@ -591,7 +591,7 @@ def main():
     args.warmup = max(0, args.warmup)
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the operator "
-              "has no multi-GPU path in this build).", file=sys.stderr)
+              "runs on one GPU; sharding is a design, not code here).", file=sys.stderr)
         sys.exit(2)
     import torch
     if not torch.cuda.is_available():

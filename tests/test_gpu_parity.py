@@ -71,7 +71,7 @@ def full_check(taco, x_bits, B, tau=1.0):
     ref_acc = oracle.decompress_accumulate(o_codes, o_alpha, o_scale, B, acc0.copy().reshape(-1))
     r_acc = rel_rms(acc.cpu().numpy().reshape(-1), ref_acc)
     assert r_acc <= 1e-6, f"accumulate rel RMS {r_acc:.3g}"
-    # North-star round trip: GPU compress + GPU decompress vs the oracle's.
+    # Round trip: GPU compress + GPU decompress vs the oracle's.
     y2 = taco.decompress(codes, alpha, scale, block=B)
     torch.cuda.synchronize()
     ref = synth.bits_to_f32(oracle.decompress(o_codes, o_alpha, o_scale, B)).astype(np.float64)
