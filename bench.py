@@ -546,6 +546,25 @@ def copy_probe(torch):
     print(json.dumps({"copy_probe_bytes": n, "launches": 3}), flush=True)
 
 
+def add_reference(torch, n: int, use_graph: bool) -> dict:
+    """torch's bf16 elementwise add over N/2-element operands: reads 2N bytes
+    and writes N, the byte mix of compress, timed like the operator's kernels
+    (buffer sets rotated over more than 1 GiB of loads, HIP graphs, events)."""
+    timer = Timer(torch)
+    nsets = rotation_sets(2 * n, 3 * n)
+    sets = [tuple(torch.ones(n // 2, dtype=torch.bfloat16, device="cuda") for _ in range(3))
+            for _ in range(nsets)]
+
+    def add_all():
+        for a, b, c in sets:
+            torch.add(a, b, out=c)
+    fn = make_graph(torch, add_all, use_graph)
+    t = timer.time(fn, 20) / (20 * nsets)
+    del sets, fn
+    torch.cuda.empty_cache()
+    return {"bytes": 3 * n, "us": round(t * 1e6, 3), "GBps": round(3 * n / t / 1e9, 1)}
+
+
 def torch_reference(torch, synth, cases, use_graph: bool):
     """Context for the roofline: torch's own elementwise kernels moving the
     same bytes as compress at each workload's size (add of two bf16 halves:
@@ -557,18 +576,7 @@ def torch_reference(torch, synth, cases, use_graph: bool):
     for name, _block in cases:
         n = synth.WORKLOADS[name.split(":")[0]].numel
         out = {"torch_reference": name, "elements": n}
-        nsets = rotation_sets(2 * n, 3 * n)
-        sets = [tuple(torch.ones(n // 2, dtype=torch.bfloat16, device="cuda") for _ in range(3))
-                for _ in range(nsets)]
-
-        def add_all():
-            for a, b, c in sets:
-                torch.add(a, b, out=c)
-        fn = make_graph(torch, add_all, use_graph)
-        t = timer.time(fn, 20) / (20 * nsets)
-        out["add_2to1"] = {"bytes": 3 * n, "us": round(t * 1e6, 3),
-                           "GBps": round(3 * n / t / 1e9, 1)}
-        del sets, fn
+        out["add_2to1"] = add_reference(torch, n, use_graph)
         nsets = rotation_sets(2 * n, 4 * n)
         sets = [(torch.ones(n, dtype=torch.bfloat16, device="cuda"),
                  torch.empty(n, dtype=torch.bfloat16, device="cuda")) for _ in range(nsets)]
@@ -659,6 +667,15 @@ def main():
             print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
             cpu = cpu_baseline(synth, name, block, args.cpu_seconds, acc)
         rec = record(res, name, args, cpu)
+        if i == 0 and rec["roofline"]["kernel"] == "compress" and not res.get("packed"):
+            # Context for the roofline: a plain stream with compress's byte mix
+            # at the same size, measured in the same run.
+            print("[bench] same-mix stream reference (torch add)", file=sys.stderr, flush=True)
+            ref = add_reference(torch, res["n"], use_graph)
+            ref["kernel"] = "torch.add, bf16, reads 2N bytes and writes N (the compress byte mix)"
+            ref["compress_rate_vs_reference"] = round(
+                (ref["us"] * 1e-6) / res["kernels"]["compress"], 4)
+            rec["roofline"]["same_mix_stream"] = ref
         recs.append(rec)
         if args.all:
             print(json.dumps(rec), file=sys.stderr, flush=True)
