@@ -63,7 +63,9 @@ def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=400)
-    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=None,
+                   help="untimed steps right before the timed ones (default: one pass over "
+                        "every buffer set, at least 20)")
     p.add_argument("--workload", default=None)
     p.add_argument("--block", type=int, default=None)
     p.add_argument("--all", action="store_true", help="time every workload and block size")
@@ -146,10 +148,15 @@ class Timer:
         return a.elapsed_time(b) * 1e-3          # seconds
 
 
-def make_graph(torch, fn, use_graph: bool):
+def make_graph(torch, fn, use_graph: bool, prerun: bool = True):
+    """fn captured into a HIP graph (returns its replay).  prerun runs fn once
+    eagerly before the capture (lazy initialisation of torch's own kernels);
+    libtaco's launches need none, and the operator's step graphs skip it so
+    that no step runs outside the counted warmup and timed steps."""
     if not use_graph:
         return fn
-    fn()                                          # warm caches and lazy init outside capture
+    if prerun:
+        fn()
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
@@ -175,8 +182,8 @@ def run_cycle(torch, sets, one, count: int, use_graph: bool):
 
     chunk = min(count, STEP_CHUNK)
     q, rem = divmod(count, chunk)
-    full = make_graph(torch, body(chunk), use_graph)
-    tail = make_graph(torch, body(rem), use_graph) if rem else None
+    full = make_graph(torch, body(chunk), use_graph, prerun=False)
+    tail = make_graph(torch, body(rem), use_graph, prerun=False) if rem else None
 
     def go():
         for _ in range(q):
@@ -186,25 +193,47 @@ def run_cycle(torch, sets, one, count: int, use_graph: bool):
     return go
 
 
-def time_steps(torch, sets, step_one, kernels: dict, steps: int, warmup: int, use_graph: bool):
-    """Exactly `warmup` untimed steps, then exactly `steps` timed steps
-    (seconds per step); then each kernel alone over at least one pass of the
-    sets (seconds per launch), for its roofline."""
-    for i in range(warmup):
-        step_one(sets[i % len(sets)])
-    torch.cuda.synchronize()
+# The GPU's clocks ramp up during its first milliseconds of work after idle
+# time: measured on the 40 MiB round trip, a 10 ms graph replay that follows
+# 5-500 ms of host-side idling runs 5-9 % slower than back-to-back replays,
+# and about 10 ms of continuous work restores the steady rate.  So the default
+# warmup is continuous (replayed from graphs, like the timed steps) and moves
+# at least this many algorithmic bytes (about 20 ms at 5 TB/s).
+WARM_BYTES = 100e9
+
+
+def warmup_steps(warmup, nsets: int, step_bytes: float) -> int:
+    """Untimed steps: as asked; by default enough to move WARM_BYTES, at least
+    one pass over every buffer set and at least 20."""
+    if warmup is not None:
+        return warmup
+    return max(20, nsets, int(-(-WARM_BYTES // step_bytes)))
+
+
+def time_steps(torch, sets, step_one, kernels: dict, steps: int, warmup, use_graph: bool,
+               step_bytes: float):
+    """The graphs are captured first (capture runs nothing on the GPU); then
+    exactly `warmup` untimed steps replay back to back, right before exactly
+    `steps` timed steps (seconds per step).  Then each kernel alone over at
+    least one pass of the sets and at least WARM_BYTES / 4 of its step's bytes
+    (seconds per launch, after one untimed pass of the same graph), for its
+    roofline.  Returns (t_step, per_kernel, warmup steps run)."""
     timer = Timer(torch)
+    warm = warmup_steps(warmup, len(sets), step_bytes)
+    warm_fn = run_cycle(torch, sets, step_one, warm, use_graph)
     step_fn = run_cycle(torch, sets, step_one, steps, use_graph)
+    count = max(steps, len(sets), int(-(-WARM_BYTES // (4 * step_bytes))))
+    kernel_fns = {k: run_cycle(torch, sets, one, count, use_graph) for k, one in kernels.items()}
+    warm_fn()
     t_step = timer.time(step_fn, 1) / steps
     per_kernel = {}
-    count = max(steps, len(sets))
-    for kname, one in kernels.items():
-        fn = run_cycle(torch, sets, one, count, use_graph)
+    for kname, fn in kernel_fns.items():
+        fn()
         per_kernel[kname] = timer.time(fn, 1) / count
-    return t_step, per_kernel
+    return t_step, per_kernel, warm
 
 
-def roundtrip_case(torch, taco, synth, name: str, block: int, steps: int, warmup: int,
+def roundtrip_case(torch, taco, synth, name: str, block: int, steps: int, warmup,
                    use_graph: bool, fmt: str = "e4m3"):
     import numpy as np
     r = synth.WORKLOADS[name]
@@ -236,18 +265,19 @@ def roundtrip_case(torch, taco, synth, name: str, block: int, steps: int, warmup
         one_compress(st)
         one_decompress(st)
 
-    t_step, kt = time_steps(torch, sets, one_step,
-                            {"compress": one_compress, "decompress": one_decompress},
-                            steps, warmup, use_graph)
+    step_bytes = algorithmic_bytes("compress", n, block) + algorithmic_bytes("decompress", n, block)
+    t_step, kt, warm = time_steps(torch, sets, one_step,
+                                  {"compress": one_compress, "decompress": one_decompress},
+                                  steps, warmup, use_graph, step_bytes)
     t_c, t_d = kt["compress"], kt["decompress"]
-    return {"n": n, "block": block, "steps": steps, "t_step": t_step, "t_compress": t_c,
-            "t_decompress": t_d, "sets": nsets, "rows": r.rows, "cols": r.cols, "format": fmt,
+    return {"n": n, "block": block, "steps": steps, "warmup": warm, "t_step": t_step,
+            "t_compress": t_c, "t_decompress": t_d, "sets": nsets, "rows": r.rows, "cols": r.cols, "format": fmt,
             "bytes_step": algorithmic_bytes("compress", n, block)
             + algorithmic_bytes("decompress", n, block),
             "input_bytes_step": 2.0 * n, "kernels": {"compress": t_c, "decompress": t_d}}
 
 
-def packed_case(torch, taco, synth, name: str, block: int, steps: int, warmup: int,
+def packed_case(torch, taco, synth, name: str, block: int, steps: int, warmup,
                 use_graph: bool):
     """Round trip through the interleaved wire layout (one payload buffer per
     direction, codes and scalars together)."""
@@ -275,18 +305,20 @@ def packed_case(torch, taco, synth, name: str, block: int, steps: int, warmup: i
         one_compress(st)
         one_decompress(st)
 
-    t_step, kt = time_steps(torch, sets, one_step,
-                            {"compress": one_compress, "decompress": one_decompress},
-                            steps, warmup, use_graph)
+    step_bytes = (algorithmic_bytes("compress", n, block)
+                  + algorithmic_bytes("decompress", n, block))
+    t_step, kt, warm = time_steps(torch, sets, one_step,
+                                  {"compress": one_compress, "decompress": one_decompress},
+                                  steps, warmup, use_graph, step_bytes)
     t_c, t_d = kt["compress"], kt["decompress"]
-    return {"n": n, "block": block, "steps": steps, "t_step": t_step, "sets": nsets,
-            "rows": r.rows, "cols": r.cols, "packed": True,
+    return {"n": n, "block": block, "steps": steps, "warmup": warm, "t_step": t_step,
+            "sets": nsets, "rows": r.rows, "cols": r.cols, "packed": True,
             "bytes_step": algorithmic_bytes("compress", n, block)
             + algorithmic_bytes("decompress", n, block),
             "input_bytes_step": 2.0 * n, "kernels": {"compress": t_c, "decompress": t_d}}
 
 
-def fidelity_case(torch, taco, synth, name: str, block: int, steps: int, warmup: int,
+def fidelity_case(torch, taco, synth, name: str, block: int, steps: int, warmup,
                   use_graph: bool):
     """taco_roundtrip of the operator's variant with error sums only: reads
     the bf16 tensor once (plus a clearing launch of the 40-byte sums)."""
@@ -303,13 +335,14 @@ def fidelity_case(torch, taco, synth, name: str, block: int, steps: int, warmup:
         x, sums = st
         taco.roundtrip(x, block=block, variant="taco", sums=sums)
 
-    t, _ = time_steps(torch, sets, one_step, {}, steps, warmup, use_graph)
-    return {"n": n, "block": block, "steps": steps, "t_step": t, "sets": nsets, "rows": r.rows,
-            "cols": r.cols, "fidelity": True, "bytes_step": 2.0 * n, "input_bytes_step": 2.0 * n,
+    t, _, warm = time_steps(torch, sets, one_step, {}, steps, warmup, use_graph, 2.0 * n)
+    return {"n": n, "block": block, "steps": steps, "warmup": warm, "t_step": t, "sets": nsets,
+            "rows": r.rows, "cols": r.cols, "fidelity": True, "bytes_step": 2.0 * n,
+            "input_bytes_step": 2.0 * n,
             "kernels": {"roundtrip": t}}
 
 
-def accumulate_case(torch, taco, synth, name: str, block: int, steps: int, warmup: int,
+def accumulate_case(torch, taco, synth, name: str, block: int, steps: int, warmup,
                     use_graph: bool, fused: bool = False):
     """Four payloads compressed and summed into one float32 accumulator: one
     taco_decompress_accumulate per payload, or (fused) one
@@ -344,30 +377,34 @@ def accumulate_case(torch, taco, synth, name: str, block: int, steps: int, warmu
         run_compress()
         run_accumulate()
 
-    for _ in range(warmup):
-        run_steps()
-    torch.cuda.synchronize()
-    step_fn = make_graph(torch, run_steps, use_graph)
-    comp_fn = make_graph(torch, run_compress, use_graph)
-    acc_fn = make_graph(torch, run_accumulate, use_graph)
-    reps = max(1, steps)
-    timer = Timer(torch)
-    step_fn()
-    t_steps = timer.time(step_fn, reps)
+    # Graphs first, then exactly `warm` untimed steps, then the timed steps
+    # (as in time_steps); each kernel graph gets one untimed replay first.
     nb = len(payloads)
-    t_c = timer.time(comp_fn, reps) / (nb * reps)
-    t_a = timer.time(acc_fn, reps) / ((1 if fused else nb) * reps)
     acc_bytes = (algorithmic_bytes(f"accumulate_n:{nb}", n, block) if fused
                  else nb * algorithmic_bytes("accumulate", n, block))
+    step_bytes = nb * algorithmic_bytes("compress", n, block) + acc_bytes
+    step_fn = make_graph(torch, run_steps, use_graph, prerun=False)
+    comp_fn = make_graph(torch, run_compress, use_graph, prerun=False)
+    acc_fn = make_graph(torch, run_accumulate, use_graph, prerun=False)
+    warm = warmup_steps(warmup, 1, step_bytes)
+    for _ in range(warm):                 # graph replays: back to back on the GPU
+        step_fn()
+    reps = max(1, steps)
+    timer = Timer(torch)
+    t_steps = timer.time(step_fn, reps)
+    comp_fn()
+    t_c = timer.time(comp_fn, reps) / (nb * reps)
+    acc_fn()
+    t_a = timer.time(acc_fn, reps) / ((1 if fused else nb) * reps)
     kname = "accumulate_n" if fused else "accumulate"
-    return {"n": n, "block": block, "steps": reps, "t_step": t_steps / reps, "t_compress": t_c,
-            "t_accumulate": t_a, "sets": 1, "rows": r.rows, "cols": r.cols,
+    return {"n": n, "block": block, "steps": reps, "warmup": warm, "t_step": t_steps / reps,
+            "t_compress": t_c, "t_accumulate": t_a, "sets": 1, "rows": r.rows, "cols": r.cols,
             "fused": fused, "nb": nb,
             "bytes_step": nb * algorithmic_bytes("compress", n, block) + acc_bytes,
             "input_bytes_step": nb * 2.0 * n, "kernels": {"compress": t_c, kname: t_a}}
 
 
-def owner_case(torch, taco, synth, name: str, block: int, steps: int, warmup: int,
+def owner_case(torch, taco, synth, name: str, block: int, steps: int, warmup,
                use_graph: bool, packed: bool = False):
     """Owner step of the two-shot all-reduce: own bf16 partial plus three
     received payloads (four independently seeded tensors) reduced and
@@ -396,18 +433,17 @@ def owner_case(torch, taco, synth, name: str, block: int, steps: int, warmup: in
         else:
             taco.reduce_compress(own, pay, block=block, codes=codes, alpha=alpha, scale=scale)
 
-    for _ in range(warmup):
-        run_steps()
-    torch.cuda.synchronize()
-    step_fn = make_graph(torch, run_steps, use_graph)
-    reps = max(1, steps)
-    timer = Timer(torch)
-    step_fn()
-    t = timer.time(step_fn, reps) / reps
     npay = len(pay)
     kbytes = 2.0 * n + npay * (n + 8.0 * n / block) + n + 8.0 * n / block
-    return {"n": n, "block": block, "steps": reps, "t_step": t, "sets": 1, "rows": r.rows,
-            "cols": r.cols, "bytes_step": kbytes, "input_bytes_step": 2.0 * n,
+    step_fn = make_graph(torch, run_steps, use_graph, prerun=False)
+    warm = warmup_steps(warmup, 1, kbytes)
+    for _ in range(warm):                 # graph replays: back to back on the GPU
+        step_fn()
+    reps = max(1, steps)
+    timer = Timer(torch)
+    t = timer.time(step_fn, reps) / reps
+    return {"n": n, "block": block, "steps": reps, "warmup": warm, "t_step": t, "sets": 1,
+            "rows": r.rows, "cols": r.cols, "bytes_step": kbytes, "input_bytes_step": 2.0 * n,
             "kernels": {"reduce_compress": t}, "npayloads": npay, "packed": packed}
 
 
@@ -502,7 +538,7 @@ def record(res, name: str, args, cpu=None):
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": res["steps"],
-        "warmup": args.warmup,
+        "warmup": res["warmup"],
         "ms_per_step": round(t_step * 1e3, 5),
         "higher_is_better": True,
         "scaling": "weak",
@@ -559,6 +595,8 @@ def add_reference(torch, n: int, use_graph: bool) -> dict:
         for a, b, c in sets:
             torch.add(a, b, out=c)
     fn = make_graph(torch, add_all, use_graph)
+    for _ in range(int(-(-WARM_BYTES // (3 * n * nsets)))):    # continuous warmup, untimed
+        fn()
     t = timer.time(fn, 20) / (20 * nsets)
     del sets, fn
     torch.cuda.empty_cache()
@@ -596,7 +634,8 @@ def torch_reference(torch, synth, cases, use_graph: bool):
 def main():
     args = parse()
     args.steps = max(1, args.steps)
-    args.warmup = max(0, args.warmup)
+    if args.warmup is not None:
+        args.warmup = max(0, args.warmup)
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the operator "
               "runs on one GPU; sharding is a design, not code here).", file=sys.stderr)
