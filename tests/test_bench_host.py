@@ -1,0 +1,58 @@
+"""Host-side logic of bench.py (no GPU): the algorithmic byte counts that the
+roofline divides by, the buffer rotation that keeps loads out of the 256 MB
+Infinity Cache, the warmup sizing, and the refusal of more than one GPU."""
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+import bench  # noqa: E402
+
+
+@pytest.mark.parametrize("block", [32, 64, 128, 256, 512])
+def test_algorithmic_bytes_per_element(block):
+    # Per element: bf16 2 bytes, code 1 byte, two float32 scalars per block,
+    # float32 accumulator read and written.
+    n = block * 1000
+    per = 8.0 / block
+    assert bench.algorithmic_bytes("compress", n, block) == pytest.approx(n * (3 + per))
+    assert bench.algorithmic_bytes("decompress", n, block) == pytest.approx(n * (3 + per))
+    assert bench.algorithmic_bytes("accumulate", n, block) == pytest.approx(n * (9 + per))
+    for p in (1, 3, 8):
+        assert bench.algorithmic_bytes(f"accumulate_n:{p}", n, block) == pytest.approx(
+            n * (p * (1 + per) + 8))
+        assert bench.algorithmic_bytes(f"reduce_compress:{p}", n, block) == pytest.approx(
+            n * (2 + p * (1 + per) + 1 + per))
+    with pytest.raises(ValueError):
+        bench.algorithmic_bytes("nothing", n, block)
+
+
+def test_rotation_covers_four_times_the_infinity_cache():
+    assert bench.ROTATE_LOAD_BYTES >= 4 * bench.MALL_BYTES
+    for load in (4 << 20, 40 << 20, 700 << 20, 3 << 30):
+        k = bench.rotation_sets(load, 3 * load)
+        assert k >= 1
+        capped = -(-bench.ROTATE_LOAD_BYTES // load) * 3 * load > bench.MAX_SET_BYTES
+        if not capped:
+            assert k * load >= bench.ROTATE_LOAD_BYTES       # loads leave the cache
+        assert k == 1 or k * 3 * load <= bench.MAX_SET_BYTES  # and fit the memory cap
+
+
+def test_default_warmup_moves_enough_bytes_and_covers_every_set():
+    step = 128.45e6                                  # the 40 MiB round trip
+    w = bench.warmup_steps(None, 49, step)
+    assert w >= 49 and w * step >= bench.WARM_BYTES
+    assert bench.warmup_steps(None, 500, 1e12) == 500
+    assert bench.warmup_steps(None, 1, 1e12) == 20
+    assert bench.warmup_steps(7, 49, step) == 7     # an explicit count is kept
+    assert bench.warmup_steps(0, 49, step) == 0
+
+
+def test_more_than_one_gpu_is_refused():
+    out = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                         capture_output=True, text=True, cwd=ROOT)
+    assert out.returncode == 2
+    assert "one GPU" in out.stderr and out.stdout == ""
