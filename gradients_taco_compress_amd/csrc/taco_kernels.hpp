@@ -118,6 +118,17 @@ constexpr int kGroup = kWave * kWavesPerGroup;
 #ifndef TACO_STEPS_PER_WAVE
 #define TACO_STEPS_PER_WAVE 1
 #endif
+// Wave-steps per unit: a wave of compress_kernel / decompress_kernel issues
+// the loads of P consecutive wave-steps together, then processes them one
+// after the other.  With B <= 64 a wave-step moves only 1 KiB of bf16 (512
+// bytes of codes), and on large tensors P = 2 is 6-9 % faster (measured at
+// 40 and 112 MiB); on small ones the fewer, longer waves lengthen the tail
+// (10 % slower at 4 MiB), and at B >= 128 it gains at most 1 %.  So the
+// launchers take P = 2 for B <= 64 from kPairMinSteps wave-steps up (twice
+// the waves the GPU holds at once), else P = 1.
+constexpr int64_t kPairMinSteps = 16384;
+template <int B>
+constexpr bool pairs_steps() { return B <= 64; }
 
 constexpr int lanes_per_block(int b) {
     return b == 32    ? TACO_LPB_32
@@ -606,14 +617,17 @@ __device__ __forceinline__ void codes_load_finish(uint8_t *stg,
 // ----------------------------------------------------------- compress -----
 
 // Side buffers: codes[N], alpha[M], scale[M].  (The interleaved layout has
-// its own kernel, compress_packed_kernel, below.)
-template <int B, Fmt F>
+// its own kernel, compress_packed_kernel, below.)  A wave works on units of
+// P consecutive wave-steps (see kPairMinSteps): the unit's loads are issued
+// together, then its wave-steps are processed one after the other.
+template <int B, Fmt F, int P>
 __global__ __launch_bounds__(kGroup) void compress_kernel(
     const uint16_t *__restrict__ x, int64_t nblocks, float tau,
     uint8_t *__restrict__ codes, float *__restrict__ alpha, float *__restrict__ scale) {
     using G = Geo<B>;
-    // The wave-step's codes leave through this wave's LDS region.
-    __shared__ __align__(16) uint8_t stage_all[kWavesPerGroup][G::BPW * B];
+    static_assert(P == 1 || (P == 2 && pairs_steps<B>()), "wave-steps per unit");
+    // The unit's codes leave through this wave's LDS region.
+    __shared__ __align__(16) uint8_t stage_all[kWavesPerGroup][P * G::BPW * B];
     uint8_t *stage = stage_all[__builtin_amdgcn_readfirstlane(threadIdx.x >> 6)];
     const int lane = threadIdx.x & (kWave - 1);
     const int t = lane_sub<G::LPB>(lane);
@@ -628,6 +642,7 @@ __global__ __launch_bounds__(kGroup) void compress_kernel(
     constexpr float kInvB = 1.0f / (float)B;
 
     const int64_t nsteps = (nblocks + G::BPW - 1) / G::BPW;
+    const int64_t nunits = (nsteps + P - 1) / P;
     const int64_t wave0 = (int64_t)blockIdx.x * kWavesPerGroup +
                           __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int64_t nwaves = (int64_t)gridDim.x * kWavesPerGroup;
@@ -652,74 +667,91 @@ __global__ __launch_bounds__(kGroup) void compress_kernel(
         const int gl = g < last ? g : last;
         return (uint32_t)(gl * (2 * B) + 16 * t);
     };
-    u4v buf[G::CH];
-    auto load = [&](int64_t step) {
-        const char *p = xb + step * kStepX + lane_offset(last_slot(step));
+    u4v buf[P][G::CH];
+    // A unit's wave-steps past the last one re-read the last wave-step (in
+    // bounds; nothing of theirs is stored).
+    auto load = [&](int64_t unit) {
 #pragma unroll
-        for (int k = 0; k < G::CH; ++k) buf[k] = ld16(p + k * G::SPAN * 2);
+        for (int h = 0; h < P; ++h) {
+            int64_t step = unit * P + h;
+            step = step < nsteps ? step : nsteps - 1;
+            const char *p = xb + step * kStepX + lane_offset(last_slot(step));
+#pragma unroll
+            for (int k = 0; k < G::CH; ++k) buf[h][k] = ld16(p + k * G::SPAN * 2);
+        }
     };
 
-    if (wave0 < nsteps) load(wave0);
-    for (int64_t step = wave0; step < nsteps; step += nwaves) {
-        float v[G::EPL];
+    if (wave0 < nunits) load(wave0);
+    for (int64_t unit = wave0; unit < nunits; unit += nwaves) {
+        float v[P][G::EPL];
+        float energy[P];
 #pragma unroll
-        for (int k = 0; k < G::CH; ++k) unpack8(buf[k], &v[8 * k]);
-        // [TACO] Eq. 6: block energy (raw second moment), this lane's part.
+        for (int h = 0; h < P; ++h) {
+#pragma unroll
+            for (int k = 0; k < G::CH; ++k) unpack8(buf[h][k], &v[h][8 * k]);
+            // [TACO] Eq. 6: block energy (raw second moment), this lane's part.
 #if TACO_DOT2_ENERGY
-        float energy = energy_packed<G::CH>(buf);
+            energy[h] = energy_packed<G::CH>(buf[h]);
 #else
-        float energy = sum_squares<G::EPL>(v);
+            energy[h] = sum_squares<G::EPL>(v[h]);
 #endif
-        // Materialise these values here, so that the prefetch below can
-        // reuse buf's registers instead of copying them.
-        pin_values(v);
-        asm volatile("" : "+v"(energy));
-        if (step + nwaves < nsteps) load(step + nwaves);
-
-        const int last = last_slot(step);
-        const bool active = g <= last;
-
-        energy = block_sum<G::LPB>(energy);
-        float unshift = 1.0f;
-        if (__builtin_expect(energy >= kBigEnergy, 0)) {
-            // Huge block (sum x^2 near or past float32 range): reload it and
-            // work on x * 2^-80 (exact), undoing the factor in alpha.
-            const char *p = xb + step * kStepX + lane_offset(last);
-#pragma unroll
-            for (int k = 0; k < G::CH; ++k) unpack8(ld16(p + k * G::SPAN * 2), &v[8 * k]);
-#pragma unroll
-            for (int i = 0; i < G::EPL; ++i) v[i] *= kBigShift;
-            energy = block_sum<G::LPB>(sum_squares<G::EPL>(v));
-            unshift = kBigUnshift;
+            // Materialise these values here, so that the prefetch below can
+            // reuse buf's registers instead of copying them.
+            pin_values(v[h]);
+            asm volatile("" : "+v"(energy[h]));
         }
-        // [TACO] Eq. 6-7: alpha = tau / sqrt(mean(x^2) + eps).
-        const float a = tau * __builtin_amdgcn_rsqf(energy * kInvB + TACO_EPS);
+        if (unit + nwaves < nunits) load(unit + nwaves);
 
-        // [TACO] Eq. 8 without its constant factors: R = H x.
-        fwht_block<G::LPB, G::EPL>(v, sg1, sg2, sg8);
-
-        // [TACO] Eq. 9: max|Z| = alpha max|R| / sqrt(B).
-        float m = block_max<G::LPB>(max_abs<G::EPL>(v));
-        const float s = a * m * kScaleFactor;
-        if (__builtin_expect(m < kTinyMax && m > 0.0f, 0)) {
 #pragma unroll
-            for (int i = 0; i < G::EPL; ++i) v[i] *= kTinyShift;
-            m *= kTinyShift;
-        }
-        // [TACO] Eq. 10: Z / s = Q * R / max|R|.
-        Quot r = quotient(C::kQmax, m);
-        r.hi = (m > 0.0f) ? r.hi * lane_sign : 0.0f;
-        r.lo = (m > 0.0f) ? r.lo * lane_sign : 0.0f;
+        for (int h = 0; h < P; ++h) {
+            const int64_t step = unit * P + h;
+            if (step >= nsteps) break;                               // wave-uniform
+            const int last = last_slot(step);
+            const bool active = g <= last;
 
-        u2v c[G::CH];
+            float e = block_sum<G::LPB>(energy[h]);
+            float unshift = 1.0f;
+            if (__builtin_expect(e >= kBigEnergy, 0)) {
+                // Huge block (sum x^2 near or past float32 range): reload it and
+                // work on x * 2^-80 (exact), undoing the factor in alpha.
+                const char *p = xb + step * kStepX + lane_offset(last);
 #pragma unroll
-        for (int k = 0; k < G::CH; ++k) c[k] = encode8<F>(&v[8 * k], r);
-        codes_store_staged<B>(stage, codes + step * kStepCodes, (last + 1) * B, c, g, t, lane);
-        if (active && t == 0) {
-            const int64_t sb = step * kStepScalars;
-            *reinterpret_cast<float *>(reinterpret_cast<char *>(alpha) + sb + lane_scalar) =
-                a * unshift;
-            *reinterpret_cast<float *>(reinterpret_cast<char *>(scale) + sb + lane_scalar) = s;
+                for (int k = 0; k < G::CH; ++k) unpack8(ld16(p + k * G::SPAN * 2), &v[h][8 * k]);
+#pragma unroll
+                for (int i = 0; i < G::EPL; ++i) v[h][i] *= kBigShift;
+                e = block_sum<G::LPB>(sum_squares<G::EPL>(v[h]));
+                unshift = kBigUnshift;
+            }
+            // [TACO] Eq. 6-7: alpha = tau / sqrt(mean(x^2) + eps).
+            const float a = tau * __builtin_amdgcn_rsqf(e * kInvB + TACO_EPS);
+
+            // [TACO] Eq. 8 without its constant factors: R = H x.
+            fwht_block<G::LPB, G::EPL>(v[h], sg1, sg2, sg8);
+
+            // [TACO] Eq. 9: max|Z| = alpha max|R| / sqrt(B).
+            float m = block_max<G::LPB>(max_abs<G::EPL>(v[h]));
+            const float s = a * m * kScaleFactor;
+            if (__builtin_expect(m < kTinyMax && m > 0.0f, 0)) {
+#pragma unroll
+                for (int i = 0; i < G::EPL; ++i) v[h][i] *= kTinyShift;
+                m *= kTinyShift;
+            }
+            // [TACO] Eq. 10: Z / s = Q * R / max|R|.
+            Quot r = quotient(C::kQmax, m);
+            r.hi = (m > 0.0f) ? r.hi * lane_sign : 0.0f;
+            r.lo = (m > 0.0f) ? r.lo * lane_sign : 0.0f;
+
+            u2v c[G::CH];
+#pragma unroll
+            for (int k = 0; k < G::CH; ++k) c[k] = encode8<F>(&v[h][8 * k], r);
+            codes_store_staged<B>(stage + h * kStepCodes, codes + step * kStepCodes,
+                                  (last + 1) * B, c, g, t, lane);
+            if (active && t == 0) {
+                const int64_t sb = step * kStepScalars;
+                *reinterpret_cast<float *>(reinterpret_cast<char *>(alpha) + sb + lane_scalar) =
+                    a * unshift;
+                *reinterpret_cast<float *>(reinterpret_cast<char *>(scale) + sb + lane_scalar) = s;
+            }
         }
     }
 }
@@ -922,7 +954,7 @@ __device__ __forceinline__ void acc_update_staged(float *stg, float *__restrict_
 
 // --------------------------------------------------------- decompress -----
 
-template <int B, Fmt F, Out MODE, Layout L>
+template <int B, Fmt F, Out MODE, Layout L, int P>
 __global__ __launch_bounds__(kGroup) void decompress_kernel(
     const uint8_t *__restrict__ codes, const float *__restrict__ alpha,
     const float *__restrict__ scale, int64_t nblocks, uint16_t *__restrict__ y,
@@ -931,6 +963,7 @@ __global__ __launch_bounds__(kGroup) void decompress_kernel(
     using W = Wire<B, L>;
     constexpr bool kAcc = MODE == Out::kAccumulate;
     constexpr bool kCodes = L == Layout::kSide && B >= 256;   // staged code loads
+    static_assert(P == 1 || (P == 2 && pairs_steps<B>() && !kCodes), "wave-steps per unit");
     // One LDS region per wave serves both stages (codes first, then G').
     constexpr int kAccBytes = kAcc ? AccStage<B>::kElems * 4 : 0;
     constexpr int kCodeBytes = kCodes ? CodesLoad<B>::kBytes : 0;
@@ -950,69 +983,86 @@ __global__ __launch_bounds__(kGroup) void decompress_kernel(
     // 1 / sqrt(B), rounded once.
     constexpr float kInvSqrtB = (float)inv_sqrt(B);
 
+    // Units of P consecutive wave-steps (see kPairMinSteps).
     const int64_t nsteps = (nblocks + G::BPW - 1) / G::BPW;
+    const int64_t nunits = (nsteps + P - 1) / P;
     const int64_t wave0 = (int64_t)blockIdx.x * kWavesPerGroup + (threadIdx.x >> 6);
     const int64_t nwaves = (int64_t)gridDim.x * kWavesPerGroup;
 
-    // Slots past the last block re-read the last block (never stored).
-    // (With staged code loads those slots decode zeros.)
-    u2v buf[G::CH];
+    // Slots past the last block (and wave-steps past the last one) re-read
+    // the last block; nothing of theirs is stored.  (With staged code loads
+    // those slots decode zeros.)
+    u2v buf[P][G::CH];
     u4v raw[kCodes ? CodesLoad<B>::kPieces : 1];
-    float a_buf = 1.0f, s_buf = 0.0f;
-    auto load = [&](int64_t step) {
-        int64_t blk = step * G::BPW + g;
-        blk = blk < nblocks ? blk : nblocks - 1;
-        if constexpr (kCodes) {
-            const int64_t left = nblocks - step * G::BPW;
-            codes_load_issue<B>(codes + step * (int64_t)(G::BPW * B),
-                                (int)(left < G::BPW ? left : G::BPW) * B, raw, lane);
-        } else {
-            const uint8_t *p = codes + blk * W::kRecord + 8 * t;
+    float a_buf[P], s_buf[P];
+    auto load = [&](int64_t unit) {
 #pragma unroll
-            for (int k = 0; k < G::CH; ++k) buf[k] = ld8(p + k * G::SPAN);
+        for (int h = 0; h < P; ++h) {
+            const int64_t step = unit * P + h;
+            int64_t blk = step * G::BPW + g;
+            blk = blk < nblocks ? blk : nblocks - 1;
+            if constexpr (kCodes) {
+                const int64_t left = nblocks - step * G::BPW;
+                codes_load_issue<B>(codes + step * (int64_t)(G::BPW * B),
+                                    (int)(left < G::BPW ? left : G::BPW) * B, raw, lane);
+            } else {
+                const uint8_t *p = codes + blk * W::kRecord + 8 * t;
+#pragma unroll
+                for (int k = 0; k < G::CH; ++k) buf[h][k] = ld8(p + k * G::SPAN);
+            }
+            a_buf[h] = alpha[blk * W::kScalarStride];
+            s_buf[h] = scale[blk * W::kScalarStride];
         }
-        a_buf = alpha[blk * W::kScalarStride];
-        s_buf = scale[blk * W::kScalarStride];
     };
 
-    if (wave0 < nsteps) load(wave0);
-    for (int64_t step = wave0; step < nsteps; step += nwaves) {
-        if constexpr (kCodes) codes_load_finish<B>(stage_b, raw, buf, g, t, lane);
-        float v[G::EPL];
+    if (wave0 < nunits) load(wave0);
+    for (int64_t unit = wave0; unit < nunits; unit += nwaves) {
+        if constexpr (kCodes) codes_load_finish<B>(stage_b, raw, buf[0], g, t, lane);
+        float v[P][G::EPL];
+        float a[P], s[P];
 #pragma unroll
-        for (int k = 0; k < G::CH; ++k) C::decode8(buf[k], &v[8 * k]);   // Eq. 11 (before * s)
-        float a = a_buf, s = s_buf;
-        pin_values(v);
-        asm volatile("" : "+v"(a), "+v"(s));
-        if (step + nwaves < nsteps) load(step + nwaves);
-
-        const int64_t blk = step * G::BPW + g;
-        const bool active = blk < nblocks;
-
-        fwht_block<G::LPB, G::EPL>(v, sg1, sg2, sg8);                // Eq. 12 (unnormalised)
-        // Eq. 11-13 constant factors: s / sqrt(B) / alpha, with the lane sign.
-        const float f = ((s * kInvSqrtB) / a) * lane_sign;
-        if (__builtin_expect(s > 0.0f && fabsf(f) < kTinyOut, 0)) {
-            // The factor would lose bits as a float32 subnormal: apply it as
-            // (2^64 f) then 2^-64, so that only the final product rounds.
-            const float fs = (((s * kOutShift) * kInvSqrtB) / a) * lane_sign;
+        for (int h = 0; h < P; ++h) {
 #pragma unroll
-            for (int i = 0; i < G::EPL; ++i) v[i] = (v[i] * fs) * kOutUnshift;
-        } else {
-#pragma unroll
-            for (int i = 0; i < G::EPL; ++i) v[i] *= f;
+            for (int k = 0; k < G::CH; ++k) C::decode8(buf[h][k], &v[h][8 * k]);   // Eq. 11 (before * s)
+            a[h] = a_buf[h];
+            s[h] = s_buf[h];
+            pin_values(v[h]);
+            asm volatile("" : "+v"(a[h]), "+v"(s[h]));
         }
+        if (unit + nwaves < nunits) load(unit + nwaves);
 
-        if constexpr (kAcc) {
-            acc_update_staged<B>(stage, acc, step, nblocks, v, g, t, lane);
-        } else if (active) {
-            const int64_t e0 = blk * B + 8 * t;
 #pragma unroll
-            for (int k = 0; k < G::CH; ++k) {
-                const float *w = &v[8 * k];
-                const u4v o = {pack_bf16x2(w[0], w[1]), pack_bf16x2(w[2], w[3]),
-                               pack_bf16x2(w[4], w[5]), pack_bf16x2(w[6], w[7])};
-                st16(y + e0 + k * G::SPAN, o);
+        for (int h = 0; h < P; ++h) {
+            const int64_t step = unit * P + h;
+            if (step >= nsteps) break;                               // wave-uniform
+            const int64_t blk = step * G::BPW + g;
+            const bool active = blk < nblocks;
+
+            fwht_block<G::LPB, G::EPL>(v[h], sg1, sg2, sg8);          // Eq. 12 (unnormalised)
+            // Eq. 11-13 constant factors: s / sqrt(B) / alpha, with the lane sign.
+            const float f = ((s[h] * kInvSqrtB) / a[h]) * lane_sign;
+            if (__builtin_expect(s[h] > 0.0f && fabsf(f) < kTinyOut, 0)) {
+                // The factor would lose bits as a float32 subnormal: apply it as
+                // (2^64 f) then 2^-64, so that only the final product rounds.
+                const float fs = (((s[h] * kOutShift) * kInvSqrtB) / a[h]) * lane_sign;
+#pragma unroll
+                for (int i = 0; i < G::EPL; ++i) v[h][i] = (v[h][i] * fs) * kOutUnshift;
+            } else {
+#pragma unroll
+                for (int i = 0; i < G::EPL; ++i) v[h][i] *= f;
+            }
+
+            if constexpr (kAcc) {
+                acc_update_staged<B>(stage, acc, step, nblocks, v[h], g, t, lane);
+            } else if (active) {
+                const int64_t e0 = blk * B + 8 * t;
+#pragma unroll
+                for (int k = 0; k < G::CH; ++k) {
+                    const float *w = &v[h][8 * k];
+                    const u4v o = {pack_bf16x2(w[0], w[1]), pack_bf16x2(w[2], w[3]),
+                                   pack_bf16x2(w[4], w[5]), pack_bf16x2(w[6], w[7])};
+                    st16(y + e0 + k * G::SPAN, o);
+                }
             }
         }
     }
@@ -1694,8 +1744,14 @@ struct CompressLaunch {
     const uint16_t *x; int64_t m; float tau; uint8_t *codes; float *alpha; float *scale;
     hipStream_t stream;
     template <int B> taco_status run() const {
-        return launch(reinterpret_cast<const void *>(&compress_kernel<B, F>),
-                      grid_for(steps_of<B>(m)), stream, x, m, tau, codes, alpha, scale);
+        const int64_t steps = steps_of<B>(m);
+        if constexpr (pairs_steps<B>()) {
+            if (steps >= kPairMinSteps)
+                return launch(reinterpret_cast<const void *>(&compress_kernel<B, F, 2>),
+                              grid_for((steps + 1) / 2), stream, x, m, tau, codes, alpha, scale);
+        }
+        return launch(reinterpret_cast<const void *>(&compress_kernel<B, F, 1>),
+                      grid_for(steps), stream, x, m, tau, codes, alpha, scale);
     }
 };
 
@@ -1704,8 +1760,14 @@ struct DecompressLaunch {
     const uint8_t *codes; const float *alpha; const float *scale; int64_t m; uint16_t *y;
     float *acc; hipStream_t stream;
     template <int B> taco_status run() const {
-        return launch(reinterpret_cast<const void *>(&decompress_kernel<B, F, MODE, L>),
-                      grid_for(steps_of<B>(m)), stream, codes, alpha, scale, m, y, acc);
+        const int64_t steps = steps_of<B>(m);
+        if constexpr (pairs_steps<B>()) {
+            if (steps >= kPairMinSteps)
+                return launch(reinterpret_cast<const void *>(&decompress_kernel<B, F, MODE, L, 2>),
+                              grid_for((steps + 1) / 2), stream, codes, alpha, scale, m, y, acc);
+        }
+        return launch(reinterpret_cast<const void *>(&decompress_kernel<B, F, MODE, L, 1>),
+                      grid_for(steps), stream, codes, alpha, scale, m, y, acc);
     }
 };
 

@@ -131,6 +131,16 @@ def test_ragged_all_block_sizes(taco, fmt, B):
 
 
 @pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("tokens,hidden,B", [(131091, 64, 64), (262181, 32, 32)])
+def test_paired_wave_steps(taco, fmt, tokens, hidden, B):
+    # Two wave-steps per wave (B <= 64, at least 16384 wave-steps), an odd
+    # count of them and a partial last one.
+    r = synth.WORKLOADS["laplace_2048x1024"].with_shape(tokens, hidden, seed=43)
+    announce(f"{fmt} paired wave-steps {tokens}x{hidden} B={B}")
+    print(full_check(taco, synth.generate(r), B, fmt), flush=True)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
 @pytest.mark.parametrize("B", [32, 256])
 def test_special_blocks(taco, fmt, B):
     from test_gpu_parity import special_blocks

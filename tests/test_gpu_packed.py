@@ -35,12 +35,15 @@ def to_gpu(a):
     return torch.from_numpy(np.ascontiguousarray(a)).cuda()
 
 
-@pytest.mark.parametrize("B", [32, 64, 128, 256, 512])
-def test_packed_equals_side_buffers_and_oracle(taco, B):
+@pytest.mark.parametrize("B,rows,cols", [(32, 37, 1536), (64, 37, 1536), (128, 37, 1536),
+                                          (256, 37, 1536), (512, 37, 1536),
+                                          # two wave-steps per wave, odd count, partial tail
+                                          (64, 131091, 64), (32, 262181, 32)])
+def test_packed_equals_side_buffers_and_oracle(taco, B, rows, cols):
     import torch
-    r = synth.WORKLOADS["laplace_2048x1024"].with_shape(37, 1536, seed=12)
+    r = synth.WORKLOADS["laplace_2048x1024"].with_shape(rows, cols, seed=12)
     x_bits = synth.generate(r)
-    announce(f"packed 37x1536 B={B}")
+    announce(f"packed {rows}x{cols} B={B}")
     x = to_gpu_bf16(x_bits)
     c, a, s = taco.compress(x, block=B)
     pay = taco.compress_packed(x, block=B)

@@ -133,6 +133,21 @@ def test_all_block_sizes_ragged(taco, B):
     print(st, flush=True)
 
 
+# Large tensors at B <= 64 run two wave-steps per wave (from 16384 wave-steps
+# up).  These shapes give an odd number of wave-steps (16387), so the last
+# pair has one wave-step past the end, and a partial last wave-step (3 of 8
+# blocks at B = 64, 5 of 16 at B = 32).
+PAIRED_SHAPES = [(131091, 64, 64), (262181, 32, 32)]
+
+
+@pytest.mark.parametrize("tokens,hidden,B", PAIRED_SHAPES)
+def test_paired_wave_steps(taco, tokens, hidden, B):
+    r = synth.WORKLOADS["gpt2.7b_rowpar_8192x2560"].with_shape(tokens, hidden, seed=41)
+    announce(f"paired wave-steps {tokens}x{hidden} B={B}")
+    st = full_check(taco, synth.generate(r), B)
+    print(st, flush=True)
+
+
 @pytest.mark.parametrize("tokens,hidden,B", [(1, 128, 128), (1, 256, 256), (4, 96, 128),
                                              (3, 32, 32), (5, 512, 512), (7, 64, 64)])
 def test_small_and_row_crossing_shapes(taco, tokens, hidden, B):
