@@ -13,15 +13,18 @@
 // memory traffic contiguous, and for the fidelity sums):
 //
 //  * Lane layout.  A block of B elements is owned by LPB = 8 lanes of one
-//    wavefront (4 lanes when B = 32).  Lane t of a block holds the 16-byte
-//    chunks k = 0..B/(8*LPB)-1 at element offset 8*LPB*k + 8*t, so each load
-//    instruction of the wave reads whole 128-byte lines.  Within a block the
-//    element index is  e = 8*LPB*k + 8*t + j:  bits of j (register) and k
-//    (register) are butterflied in registers, bits of t across lanes.
+//    wavefront (4 lanes when B = 32, 16 when B = 512).  Lane t of a block
+//    holds the 16-byte chunks k = 0..B/(8*LPB)-1 at element offset
+//    8*LPB*k + 8*t, so each load instruction of the wave reads whole
+//    128-byte lines.  Within a block the element index is
+//    e = 8*LPB*k + 8*t + j:  bits of j (register) and k (register) are
+//    butterflied in registers, bits of t across lanes.
 //  * Lane bits of t are lane-id bits 0, 1 and 3, the three that gfx9 DPP
 //    reaches in one instruction (quad_perm [1,0,3,2], quad_perm [2,3,0,1],
 //    row_ror:8); lane-id bits 2, 4, 5 select one of the 8 blocks a wave
-//    handles per step.
+//    handles per step.  At B = 512 (16 lanes, 32 values each instead of 64,
+//    which would take 146-190 VGPRs) t also takes lane-id bit 2, whose stage
+//    goes through ds_swizzle; bits 4 and 5 select one of 4 blocks.
 //  * Cross-lane butterfly in one instruction per element:
 //    v <- v + sgn * v@partner  (v_fmac_f32_dpp, sgn = -1 on the upper lane).
 //    The upper lane then holds the negated butterfly output; partners always
@@ -89,7 +92,7 @@ constexpr int kGroup = kWave * kWavesPerGroup;
 #define TACO_LPB_256 8
 #endif
 #ifndef TACO_LPB_512
-#define TACO_LPB_512 8
+#define TACO_LPB_512 16
 #endif
 // Cache policy of the global accesses (1 = non-temporal, "streaming").
 // Measured on MI355X with inputs streamed from HBM: the 8-byte code loads
@@ -146,7 +149,7 @@ struct Geo {
     static constexpr int BPW = kWave / LPB;        // blocks per wave-step
     static constexpr int SPAN = LPB * 8;           // element stride between chunks
     static_assert(B >= 32 && B <= 512 && (B & (B - 1)) == 0, "block size");
-    static_assert((LPB == 4 || LPB == 8) && EPL >= 8, "lane layout");
+    static_assert((LPB == 4 || LPB == 8 || LPB == 16) && EPL >= 8, "lane layout");
 };
 
 // Where block k's codes, alpha and s live (Layout):
@@ -165,11 +168,13 @@ struct Wire {
 
 template <int LPB>
 __device__ __forceinline__ int lane_sub(int lane) {   // t: position inside the block
-    return (LPB == 8) ? ((lane & 3) | ((lane >> 1) & 4)) : (lane & 3);
+    return (LPB == 16) ? (lane & 15)
+           : (LPB == 8) ? ((lane & 3) | ((lane >> 1) & 4)) : (lane & 3);
 }
 template <int LPB>
 __device__ __forceinline__ int lane_slot(int lane) {  // which block of the wave-step
-    return (LPB == 8) ? (((lane >> 2) & 1) | ((lane >> 3) & 6)) : (lane >> 2);
+    return (LPB == 16) ? (lane >> 4)
+           : (LPB == 8) ? (((lane >> 2) & 1) | ((lane >> 3) & 6)) : (lane >> 2);
 }
 
 // DPP controls (gfx9 encoding) for the three lane-id bits of t.
@@ -182,11 +187,24 @@ __device__ __forceinline__ float dpp(float v) {
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
 }
 
+// Lane-id bit 2 (the fourth bit of t when 16 lanes own a block): no single
+// gfx9 DPP control swaps lanes i and i ^ 4, so this stage reads the partner
+// through ds_swizzle in bit-mask mode (source lane = lane ^ 4 inside each
+// 32-lane half; and-mask 0x1f, or-mask 0, xor-mask 4).  Every lane of the
+// wave must be active.
+constexpr int kSwizzleXor4 = 0x1F | (4 << 10);
+__device__ __forceinline__ float swz_xor4(float v) {
+    return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), kSwizzleXor4));
+}
+
 template <int LPB>
 __device__ __forceinline__ float block_sum(float v) {
+    // Butterfly order: partners add the same two values, so every lane of
+    // the block ends with the same bits.
     v += dpp<kDppXor1>(v);
     v += dpp<kDppXor2>(v);
-    if (LPB == 8) v += dpp<kDppXor8>(v);
+    if (LPB == 16) v += swz_xor4(v);
+    if (LPB >= 8) v += dpp<kDppXor8>(v);
     return v;
 }
 // Maximum over the block's lanes of a non-negative float.  Non-negative
@@ -201,7 +219,8 @@ __device__ __forceinline__ float block_max(float f) {
     uint32_t v = __float_as_uint(f);
     v = max(v, dpp_u<kDppXor1>(v));
     v = max(v, dpp_u<kDppXor2>(v));
-    if (LPB == 8) v = max(v, dpp_u<kDppXor8>(v));
+    if (LPB == 16) v = max(v, (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, kSwizzleXor4));
+    if (LPB >= 8) v = max(v, dpp_u<kDppXor8>(v));
     return __uint_as_float(v);
 }
 
@@ -263,9 +282,16 @@ __device__ __forceinline__ void fwht_block(float (&v)[EPL], float sg1, float sg2
     for (int o = 0; o < EPL; o += 8) TACO_FMAC_DPP8("quad_perm:[1,0,3,2]", v, o, sg1);
 #pragma unroll
     for (int o = 0; o < EPL; o += 8) TACO_FMAC_DPP8("quad_perm:[2,3,0,1]", v, o, sg2);
-    if (LPB == 8) {
+    if (LPB >= 8) {
 #pragma unroll
         for (int o = 0; o < EPL; o += 8) TACO_FMAC_DPP8("row_ror:8", v, o, sg8);
+    }
+    if (LPB == 16) {
+        // Lane-id bit 2 through ds_swizzle: v <- v + sgn * v@(lane ^ 4), one
+        // rounding as in the DPP stages.
+        const float sg4 = (__lane_id() & 4) ? -1.0f : 1.0f;
+#pragma unroll
+        for (int i = 0; i < EPL; ++i) v[i] = __builtin_fmaf(sg4, swz_xor4(v[i]), v[i]);
     }
 }
 
@@ -770,7 +796,7 @@ __global__ __launch_bounds__(kGroup) void compress_packed_kernel(
     using C = Codec<F>;
     constexpr int kRec = B + 8;                 // bytes per record
     constexpr int R = 16;                       // records per unit
-    constexpr int S = R / G::BPW;               // wave-steps per unit (1 or 2)
+    constexpr int S = R / G::BPW;               // wave-steps per unit (1, 2 or 4)
     constexpr int kUnit = R * kRec;             // bytes per unit
     static_assert(kUnit % 128 == 0 && R % G::BPW == 0, "unit layout");
     __shared__ __align__(16) uint8_t stage_all[kWavesPerGroup][kUnit];
