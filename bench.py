@@ -57,6 +57,11 @@ def rotation_sets(min_load_bytes: int, set_bytes: int) -> int:
     return max(1, min(nsets, MAX_SET_BYTES // max(1, set_bytes)))
 KERNEL_DIR = os.path.join(ROOT, "gradients_taco_compress_amd", "csrc")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+VALU_FILE = os.path.join(ROOT, "profiles", "valu_insts.json")
+# VALU issue peak of MI355X: a wave64 VALU instruction occupies a 16-lane SIMD
+# for 4 cycles; 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz lane-instructions/s
+# (non-packed 32-bit VALU).
+VALU_PEAK_LANE_INSTR = 256 * 4 * 16 * 2.4e9
 
 
 def parse():
@@ -112,6 +117,29 @@ def kernel_hash() -> str:
             with open(os.path.join(KERNEL_DIR, name), "rb") as f:
                 h.update(f.read())
     return h.hexdigest()[:16]
+
+
+def valu_for(kernel: str, workload: str, block: int):
+    """VALU wave-instructions per launch from the committed rocprofv3 counter
+    run (SQ_INSTS_VALU), if taken on the current kernel source; else None."""
+    try:
+        with open(VALU_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_sha256_16") != kernel_hash():
+        return None
+    e = t.get("entries", {}).get(f"{kernel}:{workload}:{block}")
+    return None if e is None else e.get("sq_insts_valu")
+
+
+def valu_roofline(insts: float, seconds: float) -> dict:
+    """VALU issue rate of a launch against the issue peak."""
+    achieved = insts * 64 / seconds
+    return {"bound": "alu", "achieved": round(achieved / 1e12, 2),
+            "peak": round(VALU_PEAK_LANE_INSTR / 1e12, 2), "unit": "T lane-instr/s",
+            "frac": round(achieved / VALU_PEAK_LANE_INSTR, 4),
+            "wave_instructions": insts}
 
 
 def traffic_for(kernel: str, workload: str, block: int):
@@ -566,6 +594,20 @@ def record(res, name: str, args, cpu=None):
                      "algorithmic_bytes": kbytes,
                      "traffic": traffic},
     }
+    valu = valu_for(key, name, res["block"]) if fmt == "e4m3" and not res.get("packed") else None
+    if valu is not None:
+        rec["roofline"]["valu"] = valu_roofline(valu, dur)
+    if res.get("fidelity"):
+        # The study's round trip keeps the codes in registers and reads the
+        # tensor once: it is bound by VALU issue, not by HBM.
+        hbm = rec["roofline"]
+        rec["roofline"] = dict(valu_roofline(valu, dur) if valu is not None else
+                               {"bound": "alu", "achieved": None,
+                                "peak": round(VALU_PEAK_LANE_INSTR / 1e12, 2),
+                                "unit": "T lane-instr/s", "frac": None},
+                               kernel=kern, traffic=hbm["traffic"],
+                               hbm={"achieved": hbm["achieved"], "peak": hbm["peak"],
+                                    "unit": hbm["unit"], "frac": hbm["frac"]})
     if cpu is not None:
         rec["cpu_baseline"] = cpu
     return rec

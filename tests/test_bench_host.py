@@ -56,3 +56,38 @@ def test_more_than_one_gpu_is_refused():
                          capture_output=True, text=True, cwd=ROOT)
     assert out.returncode == 2
     assert "one GPU" in out.stderr and out.stdout == ""
+
+
+class _Args:
+    warmup = None
+    no_graph = False
+
+
+def _res(kind):
+    n, block = 8192 * 2560, 128
+    base = {"n": n, "block": block, "steps": 400, "warmup": 779, "sets": 49, "rows": 8192,
+            "cols": 2560, "input_bytes_step": 2.0 * n}
+    if kind == "roundtrip":
+        base.update(t_step=25e-6, kernels={"compress": 12.8e-6, "decompress": 12.5e-6},
+                    bytes_step=bench.algorithmic_bytes("compress", n, block)
+                    + bench.algorithmic_bytes("decompress", n, block))
+    else:
+        base.update(t_step=22.9e-6, kernels={"roundtrip": 22.9e-6}, fidelity=True,
+                    bytes_step=2.0 * n)
+    return base
+
+
+def test_record_roofline_objects():
+    rec = bench.record(_res("roundtrip"), "gpt2.7b_rowpar_8192x2560", _Args())
+    roof = rec["roofline"]
+    assert roof["bound"] == "hbm" and roof["kernel"] == "compress"
+    assert roof["achieved"] == pytest.approx(
+        bench.algorithmic_bytes("compress", 8192 * 2560, 128) / 12.8e-6 / 1e9, rel=1e-3)
+    assert roof["frac"] == pytest.approx(roof["achieved"] / bench.HBM_PEAK_GBS, rel=1e-3)
+    if "valu" in roof:        # counters taken on the current kernel source
+        v = roof["valu"]
+        assert v["bound"] == "alu" and 0 < v["frac"] < 1
+        assert v["peak"] == pytest.approx(256 * 4 * 16 * 2.4e9 / 1e12, rel=1e-3)
+    fid = bench.record(_res("fidelity"), "gpt2.7b_rowpar_8192x2560", _Args())["roofline"]
+    assert fid["bound"] == "alu" and fid["kernel"] == "roundtrip"
+    assert fid["hbm"]["frac"] == pytest.approx(2.0 * 8192 * 2560 / 22.9e-6 / 8e12, rel=1e-3)
