@@ -108,7 +108,7 @@ def test_packed_equals_side(taco, fmt):
 def test_special_blocks(taco):
     """Zero, tiny, huge and bf16-maximum blocks (the shifted sums)."""
     from test_gpu_parity import special_blocks
-    for B in (128, 512):
+    for B in (32, 128, 512):                 # 4, 8 and 16 lanes per block
         x = special_blocks(B)
         announce(f"accumulate_n special blocks B={B}")
         g, h = payloads(taco, [x], B)

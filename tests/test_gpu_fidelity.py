@@ -105,16 +105,17 @@ def test_taco_variant_equals_compress_then_decompress(taco, fmt, B):
     assert torch.equal(y.view(torch.int16), y2.view(torch.int16))
 
 
+@pytest.mark.parametrize("B", [32, 128, 512])
 @pytest.mark.parametrize("variant", VARIANTS)
-def test_special_blocks(taco, variant):
+def test_special_blocks(taco, variant, B):
     """The rare branches (huge and tiny blocks, zeros, subnormals) in every
-    variant."""
+    variant, in the three lane layouts (4, 8 and 16 lanes per block)."""
     from test_gpu_parity import special_blocks
-    x = special_blocks(128)
-    announce(f"roundtrip {variant} special blocks B=128")
+    x = special_blocks(B)
+    announce(f"roundtrip {variant} special blocks B={B}")
     xg = to_gpu_bf16(x)
-    y, sums = taco.roundtrip(xg, block=128, variant=variant, want_output=True)
-    xo = oracle.roundtrip_variant(x, 128, variant).reshape(x.shape)
+    y, sums = taco.roundtrip(xg, block=B, variant=variant, want_output=True)
+    xo = oracle.roundtrip_variant(x, B, variant).reshape(x.shape)
     want = synth.bits_to_f32(oracle.double_to_bf16(xo)).astype(np.float64)
     got = synth.bits_to_f32(bf16_bits(y)).astype(np.float64)
     for k in range(x.shape[0]):

@@ -39,14 +39,14 @@ def gpu_payloads(taco, xs, B):
     return g, h
 
 
-def run_case(taco, own_bits, xs, B, tau=1.0):
+def run_case(taco, own_bits, xs, B, tau=1.0, cancelling=False):
     import torch
     pay_g, pay_h = gpu_payloads(taco, xs, B)
     own = None if own_bits is None else to_gpu_bf16(own_bits)
     codes, alpha, scale = taco.reduce_compress(own, pay_g, block=B, target_energy=tau)
     torch.cuda.synchronize()
     return compare_reduce(own_bits, pay_h, B, codes.cpu().numpy(), alpha.cpu().numpy(),
-                          scale.cpu().numpy(), tau)
+                          scale.cpu().numpy(), tau, cancelling=cancelling)
 
 
 @pytest.mark.parametrize("B", [32, 64, 128, 256, 512])
@@ -67,16 +67,19 @@ def test_without_own_partial(taco, B):
     run_case(taco, None, xs, B)
 
 
-def test_cancelling_and_special_sums(taco):
+@pytest.mark.parametrize("B", [32, 128, 512])
+def test_cancelling_and_special_sums(taco, B):
     """own = x and a payload compressed from -x leave only the quantisation
     error; constant blocks sum exactly; huge values exercise the rescaled
-    energy branch, up to the top of the bf16 range."""
-    B = 128
+    energy branch, up to the top of the bf16 range.  B = 32, 128 and 512
+    cover the three lane layouts (4, 8 and 16 lanes per block)."""
     rng = np.random.default_rng(3)
     x = synth.f32_to_bits(rng.laplace(0, 0.02, 16 * B))
     neg = x ^ np.uint16(0x8000)
-    announce("owner step special sums")
-    run_case(taco, x, [neg], B)
+    announce(f"owner step special sums B={B}")
+    st = run_case(taco, x, [neg], B, cancelling=True)
+    print(f"cancelling sum: {st['flips']} flips in {st['n']} elements, all at ties within "
+          f"the float32 bound", flush=True)
     const = synth.f32_to_bits(np.repeat(rng.uniform(-2, 2, 16), B))
     run_case(taco, const, [const, const], B)
     huge = synth.f32_to_bits(rng.standard_normal(16 * B) * 1e30)
@@ -91,10 +94,9 @@ def test_cancelling_and_special_sums(taco):
     run_case(taco, None, [tiny, tiny2, sub], B)
     run_case(taco, sub, [sub, tiny], B)
     # Top of the bf16 range, where H X (B |X|) leaves float32 range.
-    for b in (128, 512):
-        top = synth.f32_to_bits(np.clip(rng.standard_normal(16 * b) * 5e37, -2.5e38, 2.5e38))
-        run_case(taco, top, [top], b)
-        run_case(taco, None, [top, top], b)
+    top = synth.f32_to_bits(np.clip(rng.standard_normal(16 * B) * 5e37, -2.5e38, 2.5e38))
+    run_case(taco, top, [top], B)
+    run_case(taco, None, [top, top], B)
 
 
 def test_tau_scales_alpha_and_s(taco):
