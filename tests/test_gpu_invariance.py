@@ -83,3 +83,39 @@ def test_target_energy_at_full_size(taco):
         assert np.array_equal(ct.cpu().numpy(), c1)
         np.testing.assert_allclose(at.cpu().numpy(), a1 * tau, rtol=4 * 2.0 ** -23)
         np.testing.assert_allclose(st.cpu().numpy(), s1 * tau, rtol=4 * 2.0 ** -23)
+
+
+SPLIT_CASES = [("gpt2.7b_rowpar_8192x2560", None, 128),
+               ("laplace_2048x1024", (131091, 64), 64),       # whole call paired, pieces not
+               ("qwen7b_act_16384x3584", (2048, 3584), 512)]
+
+
+@pytest.mark.parametrize("name,shape,B", SPLIT_CASES)
+def test_split_at_block_boundaries(taco, name, shape, B):
+    """Blocks are independent: compressing (and decompressing) a tensor in
+    pieces cut at arbitrary block boundaries, each piece its own call, gives
+    exactly the bytes of one call (the property sharding relies on).  The
+    cuts fall inside wave-steps, so every piece ends on a partial one."""
+    import torch
+    r = synth.WORKLOADS[name]
+    if shape is not None:
+        r = r.with_shape(*shape)
+    n = r.rows * r.cols
+    m = n // B
+    print(f"[case] split calls {r.rows}x{r.cols} B={B}", flush=True)
+    x = to_gpu_bf16(synth.generate(r)).reshape(-1)
+    c1, a1, s1 = taco.compress(x, block=B)
+    y1 = taco.decompress(c1, a1, s1, block=B)
+    cuts = sorted({0, 1, 7, 11, 3 * m // 7 + 5, m - 3, m})
+    c2 = torch.empty_like(c1)
+    a2 = torch.empty_like(a1)
+    s2 = torch.empty_like(s1)
+    y2 = torch.empty_like(y1)
+    for lo, hi in zip(cuts[:-1], cuts[1:]):
+        taco.compress(x[lo * B:hi * B], block=B, codes=c2[lo * B:hi * B], alpha=a2[lo:hi],
+                      scale=s2[lo:hi])
+    for lo, hi in zip(cuts[:-1], cuts[1:]):
+        taco.decompress(c2[lo * B:hi * B], a2[lo:hi], s2[lo:hi], block=B, out=y2[lo * B:hi * B])
+    torch.cuda.synchronize()
+    assert torch.equal(c1, c2) and torch.equal(a1, a2) and torch.equal(s1, s2)
+    assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
