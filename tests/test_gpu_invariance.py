@@ -92,7 +92,8 @@ SPLIT_CASES = [("gpt2.7b_rowpar_8192x2560", None, 128),
 
 @pytest.mark.parametrize("name,shape,B", SPLIT_CASES)
 def test_split_at_block_boundaries(taco, name, shape, B):
-    """Blocks are independent: compressing (and decompressing) a tensor in
+    """Blocks are independent: compressing (and decompressing, and
+    accumulating) a tensor in
     pieces cut at arbitrary block boundaries, each piece its own call, gives
     exactly the bytes of one call (the property sharding relies on).  The
     cuts fall inside wave-steps, so every piece ends on a partial one."""
@@ -116,6 +117,13 @@ def test_split_at_block_boundaries(taco, name, shape, B):
                       scale=s2[lo:hi])
     for lo, hi in zip(cuts[:-1], cuts[1:]):
         taco.decompress(c2[lo * B:hi * B], a2[lo:hi], s2[lo:hi], block=B, out=y2[lo * B:hi * B])
+    acc1 = torch.full((n,), 0.5, dtype=torch.float32, device="cuda")
+    acc2 = acc1.clone()
+    taco.decompress_accumulate(c1, a1, s1, acc1, block=B)
+    for lo, hi in zip(cuts[:-1], cuts[1:]):
+        taco.decompress_accumulate(c2[lo * B:hi * B], a2[lo:hi], s2[lo:hi], acc2[lo * B:hi * B],
+                                   block=B)
     torch.cuda.synchronize()
     assert torch.equal(c1, c2) and torch.equal(a1, a2) and torch.equal(s1, s2)
     assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
+    assert torch.equal(acc1, acc2)
