@@ -228,6 +228,8 @@ def run_cycle(torch, sets, one, count: int, use_graph: bool):
 # warmup is continuous (replayed from graphs, like the timed steps) and moves
 # at least this many algorithmic bytes (about 20 ms at 5 TB/s).
 WARM_BYTES = 100e9
+# Replays of the K timed steps after the timed region, for the spread.
+REPEATS = 20
 
 
 def warmup_steps(warmup, nsets: int, step_bytes: float) -> int:
@@ -245,7 +247,10 @@ def time_steps(torch, sets, step_one, kernels: dict, steps: int, warmup, use_gra
     `steps` timed steps (seconds per step).  Then each kernel alone over at
     least one pass of the sets and at least WARM_BYTES / 4 of its step's bytes
     (seconds per launch, after one untimed pass of the same graph), for its
-    roofline.  Returns (t_step, per_kernel, warmup steps run)."""
+    roofline.  After the timed steps, REPEATS more replays of the same K
+    steps give the spread of the measurement (reported beside the value,
+    never in it).  Returns (t_step, per_kernel, warmup steps run, seconds
+    per step of each repeat)."""
     timer = Timer(torch)
     warm = warmup_steps(warmup, len(sets), step_bytes)
     warm_fn = run_cycle(torch, sets, step_one, warm, use_graph)
@@ -254,11 +259,12 @@ def time_steps(torch, sets, step_one, kernels: dict, steps: int, warmup, use_gra
     kernel_fns = {k: run_cycle(torch, sets, one, count, use_graph) for k, one in kernels.items()}
     warm_fn()
     t_step = timer.time(step_fn, 1) / steps
+    repeats = [timer.time(step_fn, 1) / steps for _ in range(REPEATS)]
     per_kernel = {}
     for kname, fn in kernel_fns.items():
         fn()
         per_kernel[kname] = timer.time(fn, 1) / count
-    return t_step, per_kernel, warm
+    return t_step, per_kernel, warm, repeats
 
 
 def roundtrip_case(torch, taco, synth, name: str, block: int, steps: int, warmup,
@@ -294,12 +300,12 @@ def roundtrip_case(torch, taco, synth, name: str, block: int, steps: int, warmup
         one_decompress(st)
 
     step_bytes = algorithmic_bytes("compress", n, block) + algorithmic_bytes("decompress", n, block)
-    t_step, kt, warm = time_steps(torch, sets, one_step,
+    t_step, kt, warm, reps = time_steps(torch, sets, one_step,
                                   {"compress": one_compress, "decompress": one_decompress},
                                   steps, warmup, use_graph, step_bytes)
     t_c, t_d = kt["compress"], kt["decompress"]
     return {"n": n, "block": block, "steps": steps, "warmup": warm, "t_step": t_step,
-            "t_compress": t_c, "t_decompress": t_d, "sets": nsets, "rows": r.rows, "cols": r.cols, "format": fmt,
+            "repeats": reps, "t_compress": t_c, "t_decompress": t_d, "sets": nsets, "rows": r.rows, "cols": r.cols, "format": fmt,
             "bytes_step": algorithmic_bytes("compress", n, block)
             + algorithmic_bytes("decompress", n, block),
             "input_bytes_step": 2.0 * n, "kernels": {"compress": t_c, "decompress": t_d}}
@@ -335,12 +341,12 @@ def packed_case(torch, taco, synth, name: str, block: int, steps: int, warmup,
 
     step_bytes = (algorithmic_bytes("compress", n, block)
                   + algorithmic_bytes("decompress", n, block))
-    t_step, kt, warm = time_steps(torch, sets, one_step,
+    t_step, kt, warm, reps = time_steps(torch, sets, one_step,
                                   {"compress": one_compress, "decompress": one_decompress},
                                   steps, warmup, use_graph, step_bytes)
     t_c, t_d = kt["compress"], kt["decompress"]
     return {"n": n, "block": block, "steps": steps, "warmup": warm, "t_step": t_step,
-            "sets": nsets, "rows": r.rows, "cols": r.cols, "packed": True,
+            "repeats": reps, "sets": nsets, "rows": r.rows, "cols": r.cols, "packed": True,
             "bytes_step": algorithmic_bytes("compress", n, block)
             + algorithmic_bytes("decompress", n, block),
             "input_bytes_step": 2.0 * n, "kernels": {"compress": t_c, "decompress": t_d}}
@@ -363,9 +369,9 @@ def fidelity_case(torch, taco, synth, name: str, block: int, steps: int, warmup,
         x, sums = st
         taco.roundtrip(x, block=block, variant="taco", sums=sums)
 
-    t, _, warm = time_steps(torch, sets, one_step, {}, steps, warmup, use_graph, 2.0 * n)
+    t, _, warm, reps = time_steps(torch, sets, one_step, {}, steps, warmup, use_graph, 2.0 * n)
     return {"n": n, "block": block, "steps": steps, "warmup": warm, "t_step": t, "sets": nsets,
-            "rows": r.rows, "cols": r.cols, "fidelity": True, "bytes_step": 2.0 * n,
+            "repeats": reps, "rows": r.rows, "cols": r.cols, "fidelity": True, "bytes_step": 2.0 * n,
             "input_bytes_step": 2.0 * n,
             "kernels": {"roundtrip": t}}
 
@@ -420,13 +426,14 @@ def accumulate_case(torch, taco, synth, name: str, block: int, steps: int, warmu
     reps = max(1, steps)
     timer = Timer(torch)
     t_steps = timer.time(step_fn, reps)
+    repeats = [timer.time(step_fn, reps) / reps for _ in range(REPEATS)]
     comp_fn()
     t_c = timer.time(comp_fn, reps) / (nb * reps)
     acc_fn()
     t_a = timer.time(acc_fn, reps) / ((1 if fused else nb) * reps)
     kname = "accumulate_n" if fused else "accumulate"
     return {"n": n, "block": block, "steps": reps, "warmup": warm, "t_step": t_steps / reps,
-            "t_compress": t_c, "t_accumulate": t_a, "sets": 1, "rows": r.rows, "cols": r.cols,
+            "repeats": repeats, "t_compress": t_c, "t_accumulate": t_a, "sets": 1, "rows": r.rows, "cols": r.cols,
             "fused": fused, "nb": nb,
             "bytes_step": nb * algorithmic_bytes("compress", n, block) + acc_bytes,
             "input_bytes_step": nb * 2.0 * n, "kernels": {"compress": t_c, kname: t_a}}
@@ -470,8 +477,9 @@ def owner_case(torch, taco, synth, name: str, block: int, steps: int, warmup,
     reps = max(1, steps)
     timer = Timer(torch)
     t = timer.time(step_fn, reps) / reps
+    repeats = [timer.time(step_fn, reps) / reps for _ in range(REPEATS)]
     return {"n": n, "block": block, "steps": reps, "warmup": warm, "t_step": t, "sets": 1,
-            "rows": r.rows, "cols": r.cols, "bytes_step": kbytes, "input_bytes_step": 2.0 * n,
+            "repeats": repeats, "rows": r.rows, "cols": r.cols, "bytes_step": kbytes, "input_bytes_step": 2.0 * n,
             "kernels": {"reduce_compress": t}, "npayloads": npay, "packed": packed}
 
 
@@ -546,6 +554,22 @@ def cpu_baseline(synth, name: str, block: int, min_seconds: float, accumulate: b
                       f"{_cpu_model()}"}
 
 
+def repeat_stats(res):
+    """Spread of the measurement: the K timed steps replayed REPEATS more
+    times after the timed region (not part of `value`)."""
+    r = sorted(res.get("repeats") or [])
+    if not r:
+        return None
+    mid = len(r) // 2
+    med = r[mid] if len(r) % 2 else 0.5 * (r[mid - 1] + r[mid])
+
+    def pct(t):
+        return round(100.0 * res["bytes_step"] / t / 1e9 / HBM_PEAK_GBS, 2)
+    return {"n": len(r), "ms_per_step_median": round(med * 1e3, 5),
+            "ms_per_step_min": round(r[0] * 1e3, 5), "ms_per_step_max": round(r[-1] * 1e3, 5),
+            "pct_hbm_peak_median": pct(med)}
+
+
 def record(res, name: str, args, cpu=None):
     t_step = res["t_step"]
     value = res["input_bytes_step"] / t_step / 1e9
@@ -587,6 +611,7 @@ def record(res, name: str, args, cpu=None):
                             else "compress + decompress"),
                    "buffer_sets": res["sets"], "graph": not args.no_graph},
         "pct_hbm_peak": round(100.0 * res["bytes_step"] / t_step / 1e9 / HBM_PEAK_GBS, 2),
+        "repeats": repeat_stats(res),
         "kernel_us": {k: round(v * 1e6, 3) for k, v in res["kernels"].items()},
         "roofline": {"bound": "hbm", "kernel": kern, "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",

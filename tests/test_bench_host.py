@@ -91,3 +91,14 @@ def test_record_roofline_objects():
     fid = bench.record(_res("fidelity"), "gpt2.7b_rowpar_8192x2560", _Args())["roofline"]
     assert fid["bound"] == "alu" and fid["kernel"] == "roundtrip"
     assert fid["hbm"]["frac"] == pytest.approx(2.0 * 8192 * 2560 / 22.9e-6 / 8e12, rel=1e-3)
+
+
+def test_repeat_stats():
+    res = _res("roundtrip")
+    assert bench.repeat_stats(res) is None
+    res["repeats"] = [25e-6, 26e-6, 24e-6, 30e-6]
+    st = bench.repeat_stats(res)
+    assert st["n"] == 4 and st["ms_per_step_min"] == 0.024 and st["ms_per_step_max"] == 0.03
+    assert st["ms_per_step_median"] == pytest.approx(0.0255)
+    assert st["pct_hbm_peak_median"] == pytest.approx(
+        100 * res["bytes_step"] / 25.5e-6 / 1e9 / bench.HBM_PEAK_GBS, abs=0.01)

@@ -49,3 +49,6 @@ def test_bench_line_fields():
     assert 0 < roof["frac"] < 1 and roof["frac"] == pytest.approx(roof["achieved"] / 8000.0,
                                                                   rel=1e-3)
     assert "cpu_baseline" not in rec
+    rep = rec["repeats"]
+    assert rep["n"] == 20
+    assert rep["ms_per_step_min"] <= rep["ms_per_step_median"] <= rep["ms_per_step_max"]
