@@ -10,6 +10,8 @@ contract:
 """
 from __future__ import annotations
 
+import math
+
 import numpy as np
 
 import oracle
@@ -28,8 +30,14 @@ U32 = 2.0 ** -24          # float32 unit roundoff
 TOTALS = {"flips": 0, "n": 0}
 
 
-def allowed_flips(n: int) -> float:
-    return max(FLIP_RATE * n, 1.0)
+def allowed_flips(n: int, rate: float = FLIP_RATE) -> float:
+    """Largest flip count one case may show when tie flips occur at `rate`:
+    a Poisson upper bound (mean + 3 standard deviations + 1), so that a case
+    of 10^5 elements is not failed by two tie flips that the rate allows on
+    average once; the rate itself is asserted on the session total, and
+    every flip must be an adjacent code at a tie."""
+    lam = rate * n
+    return lam + 3.0 * math.sqrt(lam) + 1.0
 
 
 def rel_rms(a, b) -> float:
@@ -61,23 +69,33 @@ def _adjacent(cg: int, co: int, fmt: str) -> str:
 
 
 def _tie_ok(x_block, code_gpu, code_or, j, B, fmt="e4m3") -> tuple[bool, str]:
-    """Is element j's flip a flip between adjacent codes at a rounding tie?"""
+    """Is element j's differing code one that the kernel's float32
+    evaluation order can give?  E4M3 (the operator's format): an adjacent
+    code at a rounding tie within the float32 error bound.  E5M2 and INT8:
+    the code of some value within that bound (near zero E5M2's codes are
+    finer than the bound, so the code may be a few steps away)."""
     qmax = QMAX_OF[fmt]
     _, _, z = oracle.ash_block(x_block, B)
     s64 = np.max(np.abs(z)) / qmax
-    v = float(np.float32(z[j] / s64))
+    v_exact = z[j] / s64
+    v = float(np.float32(v_exact))
     cg, co = int(code_gpu), int(code_or)
-    why = _adjacent(cg, co, fmt)
-    if why:
-        return False, f"{why} (v={v})"
-    dg, do = oracle.decode(np.array([cg, co], np.uint8), fmt)
-    mid = 0.5 * (abs(dg) + abs(do))
     # Bound on the kernel's float32 error in v: the FWHT accumulates at most
     # log2(B) roundings of partial sums bounded by sum|x|, then two roundings
     # in the quotient and the product.
     xs = synth.bits_to_f32(x_block).astype(np.float64)
     m = np.max(np.abs(oracle.fwht(xs)))
     bound = qmax * np.log2(B) * U32 * np.sum(np.abs(xs)) / m + 4 * U32 * abs(v) if m > 0 else 0
+    if fmt != "e4m3":
+        if reachable(cg, v_exact, bound, fmt):
+            return True, ""
+        return False, (f"code {cg:#x} (oracle {co:#x}) is no code of a value within "
+                       f"{bound:.3g} of {v_exact!r}")
+    why = _adjacent(cg, co, fmt)
+    if why:
+        return False, f"{why} (v={v})"
+    dg, do = oracle.decode(np.array([cg, co], np.uint8), fmt)
+    mid = 0.5 * (abs(dg) + abs(do))
     if abs(abs(v) - mid) > bound:
         return False, f"not at a tie: |v|={abs(v)!r}, midpoint={mid!r}, bound={bound:.3g}"
     return True, ""
@@ -128,6 +146,27 @@ def compare_decompress(y_bits, o_codes, o_alpha, o_scale, B, fmt="e4m3"):
     return {"rel_rms": r}
 
 
+# Owner step: cap on tie flips per case, a guard against systematic error.
+# Every flip is verified against the float32 bound individually; the rate
+# itself depends on the data, since a sum of decoded FP8 payloads is made of
+# few-bit values whose rotated sums land exactly on rounding ties far more
+# often than bf16 data do (2.7-5.4e-5 seen for two payloads without an own
+# partial).
+OWNER_FLIP_RATE = 1e-4
+
+
+def reachable(code, v, bound, fmt="e4m3") -> bool:
+    """Is `code` what the quantiser gives for some float32 value within
+    `bound` of v?  Encoding is monotone, so those codes' values are exactly
+    the representable values between the codes of v - bound and v + bound
+    (the ends widened by one float32 ulp)."""
+    lo = np.nextafter(np.float32(v - bound), np.float32(-np.inf))
+    hi = np.nextafter(np.float32(v + bound), np.float32(np.inf))
+    c_lo, c_hi = oracle.encode(np.array([lo, hi], np.float32), fmt)
+    d_lo, d_hi, d = oracle.decode(np.array([c_lo, c_hi, code], np.uint8), fmt)
+    return bool(d_lo <= d <= d_hi)
+
+
 def rotated_sum_error(own_bits, payloads, B, fmt="e4m3"):
     """Per-element bound on the float32 error of the kernel's rotated-domain
     sum of the owner step, H X = H own + sum_p c_p d_p (c_p = sqrt(B) s_p /
@@ -149,9 +188,14 @@ def rotated_sum_error(own_bits, payloads, B, fmt="e4m3"):
 def compare_reduce(own_bits, payloads, B, codes, alpha, scale, tau=1.0, max_flip_checks=200,
                    fmt="e4m3", cancelling=False):
     """Check the GPU owner step (codes, alpha, scale of own + sum of payload
-    reconstructions) against the oracle.  A flip must sit at an E4M3 tie
-    within the float32 error of the kernel's rotated-domain sum
-    (rotated_sum_error).
+    reconstructions) against the oracle.  The kernel decides the codes on a
+    float32 rotated-domain sum of the own partial and every payload, the
+    oracle on the exact sum: every code that differs must be the code of
+    some value within the float32 error of that sum (rotated_sum_error,
+    plus the oracle's own double rounding) around the exact value.  At a
+    tie that is the adjacent code; near zero, where a format's codes are
+    finer than that error (E5M2's reach far below it), it may be a few codes
+    away.  The number of such codes is capped at OWNER_FLIP_RATE.
 
     cancelling: the sum cancels to a small fraction of its terms (own = x
     plus a payload compressed from -x leaves only the quantisation error).
@@ -173,23 +217,31 @@ def compare_reduce(own_bits, payloads, B, codes, alpha, scale, tau=1.0, max_flip
     bad = np.nonzero(codes != o_codes)[0]
     TOTALS["flips"] += int(bad.size)
     TOTALS["n"] += int(n)
+    # The codes are decided on a float32 sum of `terms` rotated vectors, each
+    # adding its own rounding: the flip rate of the operator (one rotation
+    # of exact bf16 inputs) applies per term.
+    terms = len(payloads) + (own_bits is not None)
+    allowed = allowed_flips(n, OWNER_FLIP_RATE)
     if not cancelling:
-        assert bad.size <= allowed_flips(n), \
-            f"{bad.size} code mismatches in {n} elements (allowed {allowed_flips(n):.1f})"
+        assert bad.size <= allowed, \
+            f"{bad.size} code mismatches in {n} elements (allowed {allowed:.1f})"
     err = rotated_sum_error(own_bits, payloads, B, fmt) if (bad.size or cancelling) else None
-    for i in (bad if cancelling else bad[:max_flip_checks]):
+    if err is not None:
+        # The oracle's own rounding: it reconstructs every payload in double
+        # and rotates the sum again, which leaves noise of order 2^-52 times
+        # the block's L1 norm (enough to give an exact zero a sign).
+        l1 = np.repeat(np.sum(np.abs(x.reshape(-1, B)), axis=1), B)
+        err = err + 2.0 ** -52 * (np.log2(B) + 2 * terms + 2) * l1
+    for i in bad:
         k, j = divmod(int(i), B)
         xb = x[k * B:(k + 1) * B]
         r = oracle.fwht(xb)
         m = np.max(np.abs(r))
-        v = float(np.float32(qmax * r[j] / m))
+        v = qmax * r[j] / m
         cg, co = int(codes[i]), int(o_codes[i])
-        dg, do = oracle.decode(np.array([cg, co], np.uint8), fmt)
-        why = _adjacent(cg, co, fmt)
-        assert not why, (i, why)
         bound = qmax * err[i] / m + 4 * U32 * abs(v)
-        mid = 0.5 * (abs(dg) + abs(do))
-        assert abs(abs(v) - mid) <= bound, f"element {i}: |v|={abs(v)}, mid={mid}, bound={bound:.3g}"
+        assert reachable(cg, v, bound, fmt), \
+            f"element {i}: code {cg:#x} (oracle {co:#x}) is no code of a value within {bound:.3g} of {v!r}"
     ea = max_rel(alpha, o_alpha)
     es = max_rel(scale, o_scale)
     if cancelling:
