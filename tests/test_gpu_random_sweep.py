@@ -1,0 +1,69 @@
+"""Seeded random parity sweep on the GPU: block sizes, shapes, the five input
+distributions (with random seeds), the three code formats, and owner steps
+with 1-8 payloads with and without an own partial, each compared with the
+oracle through the same helpers as the other parity tests."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from parity import compare_compress, compare_decompress, compare_reduce
+
+pytestmark = pytest.mark.gpu
+
+CASES = 300
+
+
+def test_random_sweep():
+    import torch
+    import gradients_taco_compress_amd as taco
+
+    def gpu_bf16(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).cuda().view(torch.bfloat16)
+
+    def gpu(a, shape=None):
+        t = torch.from_numpy(np.ascontiguousarray(a)).cuda()
+        return t.reshape(shape) if shape is not None else t
+
+    names = sorted(synth.WORKLOADS)
+    rng = np.random.default_rng(20261202)
+    flips = n_all = owners = 0
+    for case in range(CASES):
+        B = int(rng.choice([32, 64, 128, 256, 512]))
+        fmt = str(rng.choice(["e4m3", "e4m3", "e5m2", "int8"]))
+        rows = int(rng.integers(1, 200))
+        cols = B * int(rng.integers(1, 24))
+        name = str(rng.choice(names))
+        seed = int(rng.integers(0, 1 << 30))
+        owner = rng.random() < 0.4
+        P = int(rng.integers(1, 9))
+        with_own = rng.random() < 0.8
+        print(f"[case] sweep {case}: {name} {rows}x{cols} B={B} fmt={fmt} seed={seed}"
+              + (f" owner P={P} own={with_own}" if owner else ""), flush=True)
+        r = synth.WORKLOADS[name].with_shape(rows, cols, seed=seed)
+        x = synth.generate(r)
+        c, a, s = taco.compress(gpu_bf16(x), block=B, fmt=fmt)
+        torch.cuda.synchronize()
+        st = compare_compress(x, B, c.cpu().numpy(), a.cpu().numpy(), s.cpu().numpy(), fmt=fmt)
+        flips += st["flips"]
+        n_all += st["n"]
+        oc, oa, os_ = st.pop("oracle")
+        y = taco.decompress(gpu(oc, x.shape), gpu(oa), gpu(os_), block=B, fmt=fmt)
+        torch.cuda.synchronize()
+        compare_decompress(y.view(torch.int16).cpu().numpy().view(np.uint16), oc, oa, os_, B,
+                           fmt=fmt)
+        if owner:
+            pays = [tuple(oracle.compress(synth.generate(r.with_shape(rows, cols, seed=seed + 1 + p)),
+                                          B, fmt=fmt)) for p in range(P)]
+            own = x if with_own else None
+            co, ao, so = taco.reduce_compress(None if own is None else gpu_bf16(own),
+                                              [(gpu(pc, x.shape), gpu(pa), gpu(ps))
+                                               for pc, pa, ps in pays], block=B, fmt=fmt)
+            torch.cuda.synchronize()
+            compare_reduce(own, pays, B, co.cpu().numpy(), ao.cpu().numpy(), so.cpu().numpy(),
+                           fmt=fmt)
+            owners += 1
+    print(f"sweep: {CASES} cases ({owners} owner steps), compress flips {flips} of {n_all}",
+          flush=True)
