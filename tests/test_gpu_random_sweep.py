@@ -1,7 +1,8 @@
 """Seeded random parity sweep on the GPU: block sizes, shapes, the five input
-distributions (with random seeds), the three code formats, and owner steps
-with 1-8 payloads with and without an own partial, each compared with the
-oracle through the same helpers as the other parity tests."""
+distributions (with random seeds), the three code formats, owner steps with
+1-8 payloads with and without an own partial, the multi-payload accumulate
+and the fidelity round trip's variants, each compared with the oracle
+through the same helpers as the other parity tests."""
 from __future__ import annotations
 
 import numpy as np
@@ -10,6 +11,8 @@ import pytest
 import oracle
 import synth
 from parity import compare_compress, compare_decompress, compare_reduce
+from test_gpu_accumulate_n import check as accumulate_n_check
+from test_gpu_fidelity import check_variant
 
 pytestmark = pytest.mark.gpu
 
@@ -40,8 +43,13 @@ def test_random_sweep():
         owner = rng.random() < 0.4
         P = int(rng.integers(1, 9))
         with_own = rng.random() < 0.8
+        accn = rng.random() < 0.1
+        variant = str(rng.choice(["taco", "direct", "ds", "ash", "hadamard", "tensor"]))
+        study = rng.random() < 0.1
         print(f"[case] sweep {case}: {name} {rows}x{cols} B={B} fmt={fmt} seed={seed}"
-              + (f" owner P={P} own={with_own}" if owner else ""), flush=True)
+              + (f" owner P={P} own={with_own}" if owner else "")
+              + (f" accumulate_n P={P}" if accn else "") + (f" roundtrip {variant}" if study else ""),
+              flush=True)
         r = synth.WORKLOADS[name].with_shape(rows, cols, seed=seed)
         x = synth.generate(r)
         c, a, s = taco.compress(gpu_bf16(x), block=B, fmt=fmt)
@@ -54,6 +62,12 @@ def test_random_sweep():
         torch.cuda.synchronize()
         compare_decompress(y.view(torch.int16).cpu().numpy().view(np.uint16), oc, oa, os_, B,
                            fmt=fmt)
+        if accn:
+            xs = [synth.generate(r.with_shape(rows, cols, seed=seed + 100 + p)) for p in range(P)]
+            accumulate_n_check(taco, xs, B, (rng.standard_normal(x.size) * 0.01).astype(np.float32),
+                               fmt)
+        if study:
+            check_variant(taco, x, B, variant, fmt)
         if owner:
             pays = [tuple(oracle.compress(synth.generate(r.with_shape(rows, cols, seed=seed + 1 + p)),
                                           B, fmt=fmt)) for p in range(P)]
