@@ -11,7 +11,8 @@ Two layers:
   ``taco_reduce_compress``, their ``*_packed`` forms, the ``*_fmt`` forms of
   all eight (with a code format), ``taco_packed_bytes``, ``taco_encode``,
   ``taco_decode``, ``taco_e4m3_encode``, ``taco_e4m3_decode``,
-  ``taco_roundtrip``, ``taco_num_blocks``, ``taco_status_string``: the C ABI of
+  ``taco_roundtrip``, ``taco_roundtrip_noalloc``, ``taco_num_blocks``,
+  ``taco_status_string``: the C ABI of
   ``include/taco.h`` with the same names and arguments (device pointers as
   ints, stream handle as int, pointer arrays as sequences of ints, formats
   as the ints of ``FORMATS``).
@@ -117,6 +118,8 @@ for _name in ("decompress_accumulate_n", "decompress_accumulate_n_fmt",
     getattr(_lib, "taco_" + _name).restype = ctypes.c_int
 _lib.taco_roundtrip.argtypes = [_P, _I64, _I64, _I32, _F32, _I32, _I32, _P, _P, _P]
 _lib.taco_roundtrip.restype = ctypes.c_int
+_lib.taco_roundtrip_noalloc.argtypes = [_P, _I64, _I64, _I32, _F32, _I32, _I32, _P, _P, _P]
+_lib.taco_roundtrip_noalloc.restype = ctypes.c_int
 _lib.taco_encode.argtypes = [_I32, _P, _I64, _P, _P]
 _lib.taco_decode.argtypes = [_I32, _P, _I64, _P, _P]
 for _name in ("compress_fmt", "decompress_fmt", "decompress_accumulate_fmt",
@@ -138,7 +141,7 @@ EXPORTS = ("taco_num_blocks", "taco_compress", "taco_decompress",
            "taco_decompress_accumulate_packed_fmt", "taco_reduce_compress_packed_fmt",
            "taco_encode", "taco_decode", "taco_roundtrip", "taco_decompress_accumulate_n",
            "taco_decompress_accumulate_n_fmt", "taco_decompress_accumulate_n_packed",
-           "taco_decompress_accumulate_n_packed_fmt")
+           "taco_decompress_accumulate_n_packed_fmt", "taco_roundtrip_noalloc")
 
 #: Most payloads one taco_reduce_compress or taco_decompress_accumulate_n
 #: call sums.
@@ -313,6 +316,13 @@ def taco_roundtrip(x_bf16: int, tokens: int, hidden: int, block: int, target_ene
                    format: int, variant: int, y_bf16: int, sums: int, stream: int) -> int:
     return _lib.taco_roundtrip(x_bf16, tokens, hidden, block, target_energy, format, variant,
                                y_bf16, sums, stream)
+
+
+def taco_roundtrip_noalloc(x_bf16: int, tokens: int, hidden: int, block: int,
+                           target_energy: float, format: int, variant: int, y_bf16: int,
+                           totals: int, stream: int) -> int:
+    return _lib.taco_roundtrip_noalloc(x_bf16, tokens, hidden, block, target_energy, format,
+                                       variant, y_bf16, totals, stream)
 
 
 def taco_e4m3_encode(x: int, n: int, codes: int, stream: int) -> int:
@@ -699,6 +709,9 @@ def decode(codes, fmt: str = "e4m3", out=None, stream=None):
 #: Bytes of taco_fidelity_sums: the totals (four doubles, two floats) and
 #: the library's 64 slots of partial sums.
 FIDELITY_SUMS_BYTES = 40 + 4 * 64 * 8 + 2 * 64 * 4
+#: Bytes of taco_fidelity_totals (the totals alone, laid out as the front of
+#: taco_fidelity_sums).
+FIDELITY_TOTALS_BYTES = 40
 
 
 def roundtrip(x, block: int = 256, variant: str = "taco", fmt: str = "e4m3",

@@ -1,16 +1,28 @@
 // libtaco C ABI (declared in include/taco.h): argument validation and
 // dispatch to the per-format kernel sets (Ops<format>, one translation unit
-// each).  Nothing here touches device memory; every check runs on the host
-// before anything is launched.
+// each).  Every check runs on the host before anything is launched.  The
+// only device memory of the library itself is the fixed working array of
+// taco_roundtrip_noalloc below.
 
 #include <stdint.h>
 #include <stddef.h>
-#include <hip/hip_runtime_api.h>
+#include <atomic>
+#include <mutex>
+#include <hip/hip_runtime.h>
 
 #include "taco.h"
 #include "taco_internal.hpp"
 
 using namespace taco_internal;
+
+// Working memory of taco_roundtrip_noalloc: the slots of a
+// taco_fidelity_sums, in a fixed device array instead of the caller's
+// buffer.  Each GPU holds its own copy; host code reaches it only through
+// the address that hipGetSymbolAddress returns for the current device (the
+// array's name is a host-side stand-in, not a device address).
+static __device__ __align__(256) unsigned char scratch[TACO_ROUNDTRIP_SCRATCH_BYTES];
+static_assert(sizeof(taco_fidelity_sums) <= TACO_ROUNDTRIP_SCRATCH_BYTES,
+              "the round trip's working sums must fit the fixed array");
 
 namespace {
 
@@ -315,9 +327,26 @@ taco_status decode_any(taco_format format, const uint8_t *codes, int64_t n, floa
     return with_format(format, [&](auto ops) { return decltype(ops)::decode(codes, n, out, stream); });
 }
 
-taco_status roundtrip_any(const uint16_t *x, int64_t tokens, int64_t hidden, int32_t block,
-                          float tau, taco_format format, taco_variant variant, uint16_t *y,
-                          taco_fidelity_sums *sums, hipStream_t stream) {
+// The totals of taco_fidelity_sums sit at its front with the layout of
+// taco_fidelity_totals, so the finish kernel can write either.
+static_assert(offsetof(taco_fidelity_sums, sum_sq_err) == offsetof(taco_fidelity_totals, sum_sq_err) &&
+                  offsetof(taco_fidelity_sums, sum_sq_ref) == offsetof(taco_fidelity_totals, sum_sq_ref) &&
+                  offsetof(taco_fidelity_sums, sum_sq_out) == offsetof(taco_fidelity_totals, sum_sq_out) &&
+                  offsetof(taco_fidelity_sums, sum_dot) == offsetof(taco_fidelity_totals, sum_dot) &&
+                  offsetof(taco_fidelity_sums, max_abs_err) == offsetof(taco_fidelity_totals, max_abs_err) &&
+                  offsetof(taco_fidelity_sums, tensor_absmax) ==
+                      offsetof(taco_fidelity_totals, tensor_absmax) &&
+                  sizeof(taco_fidelity_totals) == 40,
+              "taco_fidelity_totals must match the front of taco_fidelity_sums");
+
+// Validation of a round trip.  out / out_bytes: the caller's sums or totals
+// (8-byte aligned, must not overlap x or y).  On TACO_OK with *n_out > 0
+// the caller launches.
+taco_status check_roundtrip(const uint16_t *x, int64_t tokens, int64_t hidden, int32_t block,
+                            float tau, taco_format format, taco_variant variant,
+                            const uint16_t *y, const void *out, size_t out_bytes,
+                            int64_t *n_out) {
+    *n_out = 0;
     if (!valid_format(format)) return TACO_ERR_FORMAT;
     int64_t n = 0;
     const taco_status st = check_shape(tokens, hidden, block, &n);
@@ -325,17 +354,57 @@ taco_status roundtrip_any(const uint16_t *x, int64_t tokens, int64_t hidden, int
     if (!valid_tau(tau)) return TACO_ERR_PARAM;
     if (variant < TACO_VARIANT_TACO || variant > TACO_VARIANT_TENSOR) return TACO_ERR_PARAM;
     if (n == 0) return TACO_OK;
-    if (!sums || !x) return TACO_ERR_NULL;
-    if (!aligned(sums, 8)) return TACO_ERR_ALIGN;
-    const size_t ns = sizeof(taco_fidelity_sums);
+    if (!out || !x) return TACO_ERR_NULL;
+    if (!aligned(out, 8)) return TACO_ERR_ALIGN;
     if (!aligned(x, 16) || (y && !aligned(y, 16))) return TACO_ERR_ALIGN;
-    if (overlap(sums, ns, x, (size_t)n * 2) || (y && overlap(sums, ns, y, (size_t)n * 2)) ||
+    if (overlap(out, out_bytes, x, (size_t)n * 2) ||
+        (y && overlap(out, out_bytes, y, (size_t)n * 2)) ||
         (y && overlap(y, (size_t)n * 2, x, (size_t)n * 2)))
         return TACO_ERR_ALIAS;
+    *n_out = n;
+    return TACO_OK;
+}
+
+// Launches a validated round trip of n > 0 elements: working sums in *sums,
+// totals to *totals.
+taco_status launch_roundtrip(const uint16_t *x, int64_t n, int32_t block, float tau,
+                             taco_format format, taco_variant variant, uint16_t *y,
+                             taco_fidelity_sums *sums, taco_fidelity_totals *totals,
+                             hipStream_t stream) {
     const Variant v = static_cast<Variant>(static_cast<int>(variant));
     return with_format(format, [&](auto ops) {
-        return decltype(ops)::roundtrip(v, block, x, n / block, tau, y, sums, stream);
+        return decltype(ops)::roundtrip(v, block, x, n / block, tau, y, sums, totals, stream);
     });
+}
+
+// ---------------------------------------------- working array, one per GPU ---
+
+constexpr int kMaxDevices = 64;
+std::atomic<void *> g_scratch_addr[kMaxDevices];
+std::mutex g_scratch_mutex;
+
+// Device address of the current device's copy of `scratch`, looked up on
+// the first call per device (once; later calls read the cached address).
+// The stream must belong to the current device.
+taco_status scratch_address(hipStream_t stream, void **addr) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return TACO_ERR_HIP;
+    if (stream != nullptr) {
+        hipDevice_t sdev = -1;
+        if (hipStreamGetDevice(stream, &sdev) != hipSuccess || sdev != dev) return TACO_ERR_HIP;
+    }
+    void *p = g_scratch_addr[dev].load(std::memory_order_acquire);
+    if (p == nullptr) {
+        std::lock_guard<std::mutex> lock(g_scratch_mutex);
+        p = g_scratch_addr[dev].load(std::memory_order_relaxed);
+        if (p == nullptr) {
+            if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr)
+                return TACO_ERR_HIP;
+            g_scratch_addr[dev].store(p, std::memory_order_release);
+        }
+    }
+    *addr = p;
+    return TACO_OK;
 }
 
 }  // namespace
@@ -530,8 +599,27 @@ taco_status taco_roundtrip(const uint16_t *x_bf16, int64_t tokens, int64_t hidde
                            int32_t block, float target_energy, taco_format format,
                            taco_variant variant, uint16_t *y_bf16, taco_fidelity_sums *sums,
                            hipStream_t stream) {
-    return roundtrip_any(x_bf16, tokens, hidden, block, target_energy, format, variant, y_bf16,
-                         sums, stream);
+    int64_t n = 0;
+    const taco_status st = check_roundtrip(x_bf16, tokens, hidden, block, target_energy, format,
+                                           variant, y_bf16, sums, sizeof(taco_fidelity_sums), &n);
+    if (st != TACO_OK || n == 0) return st;
+    return launch_roundtrip(x_bf16, n, block, target_energy, format, variant, y_bf16, sums,
+                            reinterpret_cast<taco_fidelity_totals *>(sums), stream);
+}
+
+taco_status taco_roundtrip_noalloc(const uint16_t *x_bf16, int64_t tokens, int64_t hidden,
+                                   int32_t block, float target_energy, taco_format format,
+                                   taco_variant variant, uint16_t *y_bf16,
+                                   taco_fidelity_totals *totals, hipStream_t stream) {
+    int64_t n = 0;
+    taco_status st = check_roundtrip(x_bf16, tokens, hidden, block, target_energy, format,
+                                     variant, y_bf16, totals, sizeof(taco_fidelity_totals), &n);
+    if (st != TACO_OK || n == 0) return st;
+    void *work = nullptr;
+    st = scratch_address(stream, &work);
+    if (st != TACO_OK) return st;
+    return launch_roundtrip(x_bf16, n, block, target_energy, format, variant, y_bf16,
+                            static_cast<taco_fidelity_sums *>(work), totals, stream);
 }
 
 const char *taco_status_string(taco_status status) {

@@ -50,10 +50,13 @@ struct Ops {
     // acc += the sum of npay (1..8) payloads' reconstructions.
     static taco_status accumulate_n(Layout layout, int32_t block, int npay, const Payloads &pay,
                                     int64_t nblocks, float *acc, hipStream_t stream);
-    // Clears *sums, then (kTensor) finds max|x|, then runs the round trip.
+    // Clears *sums, then (kTensor) finds max|x|, then runs the round trip,
+    // then writes the totals of the slots of *sums to *totals (which may be
+    // the front of *sums).
     static taco_status roundtrip(Variant variant, int32_t block, const uint16_t *x,
                                  int64_t nblocks, float tau, uint16_t *y,
-                                 taco_fidelity_sums *sums, hipStream_t stream);
+                                 taco_fidelity_sums *sums, taco_fidelity_totals *totals,
+                                 hipStream_t stream);
     static taco_status encode(const float *x, int64_t n, uint8_t *codes, hipStream_t stream);
     static taco_status decode(const uint8_t *codes, int64_t n, float *out, hipStream_t stream);
 };

@@ -1457,8 +1457,11 @@ __device__ __forceinline__ float tensor_absmax_of(const taco_fidelity_sums *sums
     return __uint_as_float(m);
 }
 
-// Totals from the slots (one wave; slot i in lane i, a fixed order).
-__global__ __launch_bounds__(kGroup) void fidelity_finish_kernel(taco_fidelity_sums *sums) {
+// Totals from the slots of `sums` (one wave; slot i in lane i, a fixed
+// order), written to `out`: the totals at the front of `sums` itself, or a
+// separate taco_fidelity_totals.
+__global__ __launch_bounds__(kGroup) void fidelity_finish_kernel(const taco_fidelity_sums *sums,
+                                                                 taco_fidelity_totals *out) {
     const int lane = threadIdx.x;
     if (lane >= kWave) return;
     double t[4];
@@ -1467,12 +1470,12 @@ __global__ __launch_bounds__(kGroup) void fidelity_finish_kernel(taco_fidelity_s
     const uint32_t me = wave_max_u(sums->slot_max_err[lane]);
     const uint32_t ma = wave_max_u(sums->slot_absmax[lane]);
     if (lane == 0) {
-        sums->sum_sq_err = t[0];
-        sums->sum_sq_ref = t[1];
-        sums->sum_sq_out = t[2];
-        sums->sum_dot = t[3];
-        sums->max_abs_err = __uint_as_float(me);
-        sums->tensor_absmax = __uint_as_float(ma);
+        out->sum_sq_err = t[0];
+        out->sum_sq_ref = t[1];
+        out->sum_sq_out = t[2];
+        out->sum_dot = t[3];
+        out->max_abs_err = __uint_as_float(me);
+        out->tensor_absmax = __uint_as_float(ma);
     }
 }
 
@@ -1920,7 +1923,7 @@ taco_status roundtrip_variant(Variant variant, int32_t block, const uint16_t *x,
 template <Fmt F>
 taco_status Ops<F>::roundtrip(Variant variant, int32_t block, const uint16_t *x, int64_t nblocks,
                               float tau, uint16_t *y, taco_fidelity_sums *sums,
-                              hipStream_t stream) {
+                              taco_fidelity_totals *totals, hipStream_t stream) {
     taco_status st = launch(reinterpret_cast<const void *>(&fidelity_clear_kernel), 1u, stream,
                             sums);
     if (st != TACO_OK || nblocks == 0) return st;
@@ -1933,7 +1936,8 @@ taco_status Ops<F>::roundtrip(Variant variant, int32_t block, const uint16_t *x,
     }
     st = roundtrip_variant<F>(variant, block, x, nblocks, tau, y, sums, stream);
     if (st != TACO_OK) return st;
-    return launch(reinterpret_cast<const void *>(&fidelity_finish_kernel), 1u, stream, sums);
+    return launch(reinterpret_cast<const void *>(&fidelity_finish_kernel), 1u, stream,
+                  static_cast<const taco_fidelity_sums *>(sums), totals);
 }
 
 template <Fmt F, Layout L>

@@ -27,7 +27,8 @@
  * Conventions shared by every call below
  *   - All tensor pointers are DEVICE pointers (any device allocation, e.g. a
  *     torch tensor's data pointer), owned by the caller; the library
- *     allocates nothing and keeps no state between calls.
+ *     allocates nothing and keeps no state between calls (except the fixed
+ *     per-GPU working array of taco_roundtrip_noalloc, described there).
  *   - A [tokens, hidden] tensor is row-major and is processed as its
  *     flattened vector of N = tokens * hidden elements; block k covers
  *     elements [k*B, (k+1)*B).  N must be a multiple of B; blocks may cross
@@ -45,7 +46,8 @@
  *   - Inputs must be finite.  Blocks whose RMS exceeds ~2^126 / target_energy
  *     get a subnormal float32 alpha (less precise); non-finite inputs give
  *     unspecified codes and scalars (but never out-of-bounds accesses).
- *   - Thread-safe: the library has no mutable state.  Calls on different
+ *   - Thread-safe: apart from taco_roundtrip_noalloc's per-GPU working
+ *     array, the library has no mutable state.  Calls on different
  *     streams may overlap if their buffers do not.
  */
 #ifndef TACO_H
@@ -356,6 +358,46 @@ taco_status taco_roundtrip(const uint16_t *x_bf16, int64_t tokens, int64_t hidde
                            int32_t block, float target_energy, taco_format format,
                            taco_variant variant, uint16_t *y_bf16, taco_fidelity_sums *sums,
                            hipStream_t stream);
+
+/* The totals of taco_fidelity_sums alone: the same six fields, in the same
+ * order and at the same offsets as its first members (40 bytes). */
+typedef struct {
+    double sum_sq_err;
+    double sum_sq_ref;
+    double sum_sq_out;
+    double sum_dot;
+    float max_abs_err;
+    float tensor_absmax;
+} taco_fidelity_totals;
+
+/*
+ * taco_roundtrip for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * It computes exactly what taco_roundtrip computes (same kernels, same
+ * validation; a bad variant is TACO_ERR_PARAM), but the working memory that
+ * taco_roundtrip keeps in the caller's taco_fidelity_sums (the per-slot
+ * partial sums) lives in a fixed array inside the library, one per GPU
+ * (TACO_ROUNDTRIP_SCRATCH_BYTES, held until the process ends); the caller
+ * passes only the outputs.
+ *   totals   (required, device, 8-byte aligned) overwritten with this call's
+ *            totals; must not overlap x or y.
+ *   y_bf16   as in taco_roundtrip (optional).
+ * The working memory does not grow with the tensor: every accepted shape
+ * fits it, so no size is refused for lack of it.  The first call on a
+ * device looks up that device's copy of the array (the current device,
+ * which must be the device of `stream`; a failed lookup is TACO_ERR_HIP and
+ * launches nothing); no call allocates or frees memory.  Every call on one
+ * GPU shares that GPU's array, and each call clears it first (with a
+ * kernel, on `stream`): calls on one GPU must therefore not overlap in time
+ * (calls on different streams race, and their totals are then undefined);
+ * calls on one stream are ordered and safe.  N == 0 is a no-op (totals not
+ * written).
+ */
+#define TACO_ROUNDTRIP_SCRATCH_BYTES 4096
+taco_status taco_roundtrip_noalloc(const uint16_t *x_bf16, int64_t tokens, int64_t hidden,
+                                   int32_t block, float target_energy, taco_format format,
+                                   taco_variant variant, uint16_t *y_bf16,
+                                   taco_fidelity_totals *totals, hipStream_t stream);
 
 /*
  * The E4M3 conversions the kernels above use (Cvt_FP8 of [TACO] Eq. 10 and

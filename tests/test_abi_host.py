@@ -63,6 +63,7 @@ def lib():
     L.taco_decompress_accumulate_packed_fmt.argtypes = [P, I64, I64, I32, I32, P, P]
     L.taco_reduce_compress_packed_fmt.argtypes = [P, I32, P, I64, I64, I32, F32, I32, P, P]
     L.taco_roundtrip.argtypes = [P, I64, I64, I32, F32, I32, I32, P, P, P]
+    L.taco_roundtrip_noalloc.argtypes = [P, I64, I64, I32, F32, I32, I32, P, P, P]
     L.taco_decompress_accumulate_n.argtypes = [I32, P, P, P, I64, I64, I32, P, P]
     L.taco_decompress_accumulate_n_fmt.argtypes = [I32, P, P, P, I64, I64, I32, I32, P, P]
     L.taco_decompress_accumulate_n_packed.argtypes = [I32, P, I64, I64, I32, P, P]
@@ -76,7 +77,7 @@ def lib():
 
 def test_every_declared_function_is_exported(lib):
     names = declared_functions()
-    assert len(names) == 28, names
+    assert len(names) == 29, names
     for n in names:
         assert hasattr(lib, n), n
     out = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True).stdout
@@ -324,6 +325,37 @@ def test_roundtrip_validation(lib):
     assert rt(sums=2 * A + 512) == ALIAS       # inside y
     assert rt(y=A + 1024) == ALIAS             # y overlaps x
     assert rt(tokens=0, x=None, y=None, sums=None) == OK   # empty: nothing written
+
+
+def test_roundtrip_noalloc_validation(lib):
+    """The no-allocation round trip validates like taco_roundtrip, with the
+    40-byte totals in place of the sums; an argument set that passes every
+    check reaches the device lookup, which fails without a GPU."""
+    rt = lambda **k: lib.taco_roundtrip_noalloc(
+        k.get("x", A), k.get("tokens", 4), k.get("hidden", 256), k.get("block", 128),
+        k.get("tau", 1.0), k.get("fmt", E4M3), k.get("variant", 0), k.get("y", 2 * A),
+        k.get("totals", 3 * A), None)
+    assert rt(fmt=7) == FORMAT
+    assert rt(fmt=7, tokens=0) == FORMAT
+    assert rt(tokens=-1) == SHAPE
+    assert rt(hidden=96, tokens=3) == SHAPE
+    assert rt(block=48) == BLOCK
+    assert rt(tau=0.0) == PARAM and rt(tau=float("nan")) == PARAM
+    for bad in (-1, 6, 99):
+        assert rt(variant=bad) == PARAM
+    assert rt(totals=None) == NULL
+    assert rt(x=None) == NULL
+    assert rt(totals=3 * A + 4) == ALIGN
+    assert rt(x=A + 8) == ALIGN
+    assert rt(y=2 * A + 2) == ALIGN
+    assert rt(totals=A + 64) == ALIAS            # inside x
+    assert rt(totals=2 * A + 512) == ALIAS       # inside y
+    assert rt(totals=2 * A - 32) == ALIAS        # its 40 bytes reach into y
+    assert rt(y=A + 1024) == ALIAS               # y overlaps x
+    assert rt(tokens=0, x=None, y=None, totals=None) == OK   # empty: nothing written
+    # Every check passes: the device lookup (no GPU here) refuses the launch.
+    assert rt(totals=2 * A - 40) == HIP          # ends right where y starts
+    assert rt(y=None) == HIP
 
 
 def test_accumulate_n_validation(lib):
