@@ -2,9 +2,11 @@
 """Benchmark of the TACO compression operator on one MI355X.
 
 One step = one pass of the whole operator over one batch of synthetic input:
-``taco_compress`` then ``taco_decompress`` (the round trip) for the
-round-trip workloads, or four ``taco_compress`` + four
-``taco_decompress_accumulate`` calls for the four-payload workload.
+four ``taco_compress`` + four ``taco_decompress_accumulate`` calls for the
+four-payload workload X[32768,12288] (the default line, the largest
+workload), or ``taco_compress`` then ``taco_decompress`` (the round trip) for
+the round-trip workloads, which the default line reports under ``configs``
+(each timed after its own warmup, never part of ``value``).
 Inputs are resident in HBM before timing starts.  Buffer sets are rotated so
 that every timed graph loads more than 1 GiB per replay (four times the
 256 MB Infinity Cache) and each kernel streams its inputs from HBM.  The timed steps are replayed from a
@@ -14,7 +16,8 @@ Prints one JSON line (rank 0, the only rank): the headline metric is input
 GB/s of bf16 (2 bytes per element) per round trip, plus a roofline object for
 the dominant kernel and the CPU oracle's rate on the same workload.
 
-    python bench.py [--steps K] [--warmup W] [--workload NAME[:owner]] [--block B]
+    python bench.py [--steps K] [--warmup W]      # exactly W warmup and K timed steps
+    python bench.py --workload NAME[:variant] [--block B]
     python bench.py --all --out results.json     # every workload (stderr table)
 
 ``NAME:owner`` times the fused owner step of the two-shot all-reduce
@@ -67,7 +70,9 @@ VALU_PEAK_LANE_INSTR = 256 * 4 * 16 * 2.4e9
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=400)
+    p.add_argument("--steps", type=int, default=None,
+                   help="timed steps (default: 100 for the four-payload workload, 400 for the "
+                        "round trips)")
     p.add_argument("--warmup", type=int, default=None,
                    help="untimed steps right before the timed ones (default: one pass over "
                         "every buffer set, at least 20)")
@@ -76,6 +81,9 @@ def parse():
     p.add_argument("--all", action="store_true", help="time every workload and block size")
     p.add_argument("--out", default=None, help="also write the JSON record(s) to this file")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-configs", action="store_true",
+                   help="default line only: skip the round trips of the other workloads "
+                        "(reported under 'configs')")
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="CPU seconds of each leg of the oracle baseline")
     p.add_argument("--torch-reference", action="store_true",
@@ -545,12 +553,15 @@ def cpu_baseline(synth, name: str, block: int, min_seconds: float, accumulate: b
         repsn, tn = _oracle_rate(oracle, parts, block, accumulate,
                                  max(1.0, min_seconds / threads), pool)
     op = "accumulate" if accumulate else "decompress"
+    host = os.cpu_count() or 0
     return {"value": 2.0 * n * repsn / tn / 1e9, "unit": "GB/s", "cores": threads,
             "kind": "oracle",
+            "host_cores": host, "available_cores": len(os.sched_getaffinity(0)),
             "single_thread_value": 2.0 * n * reps1 / t1 / 1e9,
             "sample": f"{rows}x{r.cols} rows of {name} (seed {r.seed}), block {block}; "
                       f"{repsn} x (compress + {op}) in {tn:.1f} s on {threads} threads "
-                      f"(rows split evenly), {reps1} x in {t1:.1f} s on one thread; "
+                      f"(rows split evenly; at most 16, the CPU share of one GPU, of the "
+                      f"host's {host} cores), {reps1} x in {t1:.1f} s on one thread; "
                       f"{_cpu_model()}"}
 
 
@@ -698,11 +709,81 @@ def torch_reference(torch, synth, cases, use_graph: bool):
         print(json.dumps(out), flush=True)
 
 
+#: The round-trip workloads reported under "configs" beside the default line
+#: (each block size of each workload).
+ROUNDTRIP_CONFIGS = [("laplace_2048x1024", 128), ("gpt2.7b_rowpar_8192x2560", 128),
+                     ("qwen7b_act_16384x3584", 128), ("qwen7b_act_16384x3584", 256),
+                     ("grad_8192x8192", 256)]
+#: Default timed steps: the four-payload step takes about 3 ms, a round trip
+#: 7-70 us.
+DEFAULT_STEPS_ACCUMULATE = 100
+DEFAULT_STEPS_ROUNDTRIP = 400
+
+
+def run_case(torch, taco, synth, name: str, block: int, steps, warmup, use_graph: bool):
+    """Times one workload (NAME or NAME:variant).  Returns (res, base name,
+    accumulate workload?)."""
+    base = name.split(":")[0]
+    kind = name.split(":")[1] if ":" in name else ""
+    acc = base == "gpt175b_hidden_32768x12288" and kind in ("", "accn")
+    if steps is None:
+        steps = DEFAULT_STEPS_ACCUMULATE if acc or kind.startswith("owner") \
+            else DEFAULT_STEPS_ROUNDTRIP
+    if kind in ("owner", "owner_packed"):
+        res = owner_case(torch, taco, synth, base, block, steps, warmup, use_graph,
+                         packed=kind == "owner_packed")
+    elif kind == "packed":
+        res = packed_case(torch, taco, synth, base, block, steps, warmup, use_graph)
+    elif kind == "accn":
+        res = accumulate_case(torch, taco, synth, base, block, steps, warmup, use_graph,
+                              fused=True)
+    elif kind == "fidelity":
+        res = fidelity_case(torch, taco, synth, base, block, steps, warmup, use_graph)
+    elif kind in ("e5m2", "int8"):
+        res = roundtrip_case(torch, taco, synth, base, block, steps, warmup, use_graph, kind)
+    elif kind:
+        raise SystemExit(f"unknown workload variant {name!r}")
+    elif acc:
+        res = accumulate_case(torch, taco, synth, base, block, steps, warmup, use_graph)
+    else:
+        res = roundtrip_case(torch, taco, synth, base, block, steps, warmup, use_graph)
+    torch.cuda.empty_cache()
+    return res, base, acc
+
+
+def same_mix_reference(torch, res, use_graph: bool) -> dict:
+    """A plain stream with compress's byte mix at the same size, measured in
+    the same run (context for the roofline)."""
+    ref = add_reference(torch, res["n"], use_graph)
+    ref["kernel"] = "torch.add, bf16, reads 2N bytes and writes N (the compress byte mix)"
+    ref["compress_rate_vs_reference"] = round((ref["us"] * 1e-6) / res["kernels"]["compress"], 4)
+    return ref
+
+
+def config_summary(rec: dict) -> dict:
+    """The figures of one round-trip workload for the default line's
+    "configs" list (never part of its value)."""
+    out = {"workload": rec["config"]["workload"], "block": rec["config"]["block"],
+           "step": rec["config"]["step"], "steps": rec["steps"], "warmup": rec["warmup"],
+           "ms_per_step": rec["ms_per_step"], "input_GBps": rec["value"],
+           "pct_hbm_peak": rec["pct_hbm_peak"], "kernel_us": rec["kernel_us"],
+           "repeats_pct_hbm_peak_median": (rec.get("repeats") or {}).get("pct_hbm_peak_median")}
+    roof = rec["roofline"]
+    out["roofline"] = {k: roof.get(k) for k in ("kernel", "achieved", "frac", "traffic")}
+    if "same_mix_stream" in roof:
+        out["same_mix_stream"] = roof["same_mix_stream"]
+    return out
+
+
 def main():
     args = parse()
-    args.steps = max(1, args.steps)
-    if args.warmup is not None:
-        args.warmup = max(0, args.warmup)
+    if args.steps is not None:
+        if args.steps < 1:
+            print("--steps must be at least 1", file=sys.stderr)
+            sys.exit(2)
+    if args.warmup is not None and args.warmup < 0:
+        print("--warmup must be at least 0", file=sys.stderr)
+        sys.exit(2)
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the operator "
               "runs on one GPU; sharding is a design, not code here).", file=sys.stderr)
@@ -725,9 +806,7 @@ def main():
         torch_reference(torch, synth, [(nm, None) for nm in names], use_graph)
         return
     if args.all:
-        cases = [("laplace_2048x1024", 128), ("gpt2.7b_rowpar_8192x2560", 128),
-                 ("qwen7b_act_16384x3584", 128), ("qwen7b_act_16384x3584", 256),
-                 ("grad_8192x8192", 256), ("gpt175b_hidden_32768x12288", 256),
+        cases = [("gpt175b_hidden_32768x12288", 256)] + ROUNDTRIP_CONFIGS + [
                  ("gpt175b_hidden_32768x12288:owner", 256),
                  ("gpt175b_hidden_32768x12288:owner_packed", 256),
                  ("gpt175b_hidden_32768x12288:accn", 256),
@@ -739,52 +818,35 @@ def main():
         name = args.workload or synth.DEFAULT_WORKLOAD
         block = args.block or synth.WORKLOADS[name.split(":")[0]].blocks[0]
         cases = [(name, block)]
+    default_line = not args.all and args.workload is None and args.block is None
     recs = []
     for i, (name, block) in enumerate(cases):
         print(f"[bench] {name} block {block}", file=sys.stderr, flush=True)
-        acc = name.startswith("gpt175b")
-        steps = args.steps if not acc else max(1, min(args.steps, 10))
-        if name.endswith((":owner", ":owner_packed")):
-            name, kind = name.split(":")
-            res = owner_case(torch, taco, synth, name, block, steps, args.warmup, use_graph,
-                             packed=kind == "owner_packed")
-            acc = False
-        elif name.endswith(":packed"):
-            name = name.split(":")[0]
-            res = packed_case(torch, taco, synth, name, block, steps, args.warmup, use_graph)
-        elif name.endswith(":accn"):
-            name = name.split(":")[0]
-            res = accumulate_case(torch, taco, synth, name, block, steps, args.warmup, use_graph,
-                                  fused=True)
-        elif name.endswith(":fidelity"):
-            name = name.split(":")[0]
-            res = fidelity_case(torch, taco, synth, name, block, steps, args.warmup, use_graph)
-        elif name.endswith((":e5m2", ":int8")):
-            name, fmt = name.split(":")
-            res = roundtrip_case(torch, taco, synth, name, block, steps, args.warmup, use_graph,
-                                 fmt)
-        elif acc:
-            res = accumulate_case(torch, taco, synth, name, block, steps, args.warmup, use_graph)
-        else:
-            res = roundtrip_case(torch, taco, synth, name, block, steps, args.warmup, use_graph)
-        torch.cuda.empty_cache()
+        res, base, acc = run_case(torch, taco, synth, name, block, args.steps, args.warmup,
+                                  use_graph)
         cpu = None
         if not args.no_cpu_baseline and i == 0:
             print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
-            cpu = cpu_baseline(synth, name, block, args.cpu_seconds, acc)
-        rec = record(res, name, args, cpu)
-        if i == 0 and rec["roofline"]["kernel"] == "compress" and not res.get("packed"):
-            # Context for the roofline: a plain stream with compress's byte mix
-            # at the same size, measured in the same run.
+            cpu = cpu_baseline(synth, base, block, args.cpu_seconds, acc)
+        rec = record(res, base, args, cpu)
+        if rec["roofline"]["kernel"] == "compress" and not res.get("packed") and \
+                (i == 0 or (base, block) in ROUNDTRIP_CONFIGS):
             print("[bench] same-mix stream reference (torch add)", file=sys.stderr, flush=True)
-            ref = add_reference(torch, res["n"], use_graph)
-            ref["kernel"] = "torch.add, bf16, reads 2N bytes and writes N (the compress byte mix)"
-            ref["compress_rate_vs_reference"] = round(
-                (ref["us"] * 1e-6) / res["kernels"]["compress"], 4)
-            rec["roofline"]["same_mix_stream"] = ref
+            rec["roofline"]["same_mix_stream"] = same_mix_reference(torch, res, use_graph)
         recs.append(rec)
         if args.all:
             print(json.dumps(rec), file=sys.stderr, flush=True)
+    if default_line and not args.no_configs:
+        # The other workloads' round trips, after the default line's timed
+        # region: reported beside it, never in its value.
+        configs = []
+        for name, block in ROUNDTRIP_CONFIGS:
+            print(f"[bench] config {name} block {block}", file=sys.stderr, flush=True)
+            res, base, _ = run_case(torch, taco, synth, name, block, None, None, use_graph)
+            rec = record(res, base, args)
+            rec["roofline"]["same_mix_stream"] = same_mix_reference(torch, res, use_graph)
+            configs.append(config_summary(rec))
+        recs[0]["configs"] = configs
     if args.out:
         with open(args.out, "w") as f:
             json.dump(recs if args.all else recs[0], f, indent=1)

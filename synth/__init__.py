@@ -106,8 +106,9 @@ WORKLOADS = {
 #: Payload seeds of the accumulate workload.
 ACCUMULATE_SEEDS = (4, 5, 6, 7)
 
-#: The workload the benchmark times by default.
-DEFAULT_WORKLOAD = "gpt2.7b_rowpar_8192x2560"
+#: The workload the benchmark times by default: the largest, four payloads
+#: compressed and accumulated.
+DEFAULT_WORKLOAD = "gpt175b_hidden_32768x12288"
 
 
 def default_threads() -> int:

@@ -102,3 +102,24 @@ def test_repeat_stats():
     assert st["ms_per_step_median"] == pytest.approx(0.0255)
     assert st["pct_hbm_peak_median"] == pytest.approx(
         100 * res["bytes_step"] / 25.5e-6 / 1e9 / bench.HBM_PEAK_GBS, abs=0.01)
+
+
+def test_default_line_is_the_largest_workload():
+    """The default line times the four-payload X[32768,12288] workload at
+    B = 256, and reports the round-trip workloads beside it."""
+    import synth
+    assert synth.DEFAULT_WORKLOAD == "gpt175b_hidden_32768x12288"
+    assert synth.WORKLOADS[synth.DEFAULT_WORKLOAD].blocks[0] == 256
+    assert max(w.numel for w in synth.WORKLOADS.values()) == \
+        synth.WORKLOADS[synth.DEFAULT_WORKLOAD].numel
+    names = {(n, b) for n, b in bench.ROUNDTRIP_CONFIGS}
+    for name, w in synth.WORKLOADS.items():
+        if name != synth.DEFAULT_WORKLOAD:
+            assert {(name, b) for b in w.blocks} <= names
+
+
+@pytest.mark.parametrize("flag,value", [("--steps", "0"), ("--warmup", "-1")])
+def test_bad_step_counts_are_refused(flag, value):
+    out = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), flag, value],
+                         capture_output=True, text=True, cwd=ROOT)
+    assert out.returncode == 2 and out.stdout == ""

@@ -52,3 +52,21 @@ def test_bench_line_fields():
     rep = rec["repeats"]
     assert rep["n"] == 20
     assert rep["ms_per_step_min"] <= rep["ms_per_step_median"] <= rep["ms_per_step_max"]
+
+
+def test_default_line_times_the_largest_workload_exactly():
+    """With no workload named, the line is the four-payload X[32768,12288]
+    workload at B = 256, with exactly the K timed and W warmup steps asked
+    for, and the accumulate kernel (the slower one) as its roofline."""
+    rec = run_bench("--steps", "3", "--warmup", "2", "--no-cpu-baseline", "--no-configs")
+    cfg = rec["config"]
+    assert cfg["workload"] == "gpt175b_hidden_32768x12288" and cfg["block"] == 256
+    assert cfg["tokens"] == 32768 and cfg["hidden"] == 12288
+    assert rec["steps"] == 3 and rec["warmup"] == 2
+    assert rec["roofline"]["kernel"] == "accumulate"
+    n = 32768 * 12288
+    # value: the four payloads' bf16 input bytes over the step time
+    assert rec["value"] == pytest.approx(4 * 2.0 * n / (rec["ms_per_step"] * 1e-3) / 1e9,
+                                         rel=1e-2)
+    assert 0 < rec["roofline"]["frac"] < 1
+    assert "configs" not in rec
