@@ -22,6 +22,27 @@ def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an AMD Instinct MI355X (gfx950) GPU")
 
 
+# The code-flip rate is asserted on the totals of the whole session, after
+# every test file has run: each comparison of codes against the oracle adds
+# its flips and elements to tests/parity.py's TOTALS (per kind and format).
+_FLIP_REPORT = []
+
+
+def pytest_sessionfinish(session, exitstatus):
+    parity = sys.modules.get("parity")
+    if parity is None:
+        return
+    lines, ok = parity.session_check()
+    _FLIP_REPORT[:] = lines
+    if not ok and session.exitstatus == 0:
+        session.exitstatus = pytest.ExitCode.TESTS_FAILED
+
+
+def pytest_terminal_summary(terminalreporter, exitstatus, config):
+    for line in _FLIP_REPORT:
+        terminalreporter.write_line(line)
+
+
 def build_helper(name: str) -> str:
     """Compile tests/helpers/<name>.c into a shared library next to it."""
     src = os.path.join(HELPERS, name + ".c")

@@ -4,13 +4,21 @@ contract:
 * codes identical, except flips to the adjacent code where the oracle's
   argument Z/s sits at a rounding tie (within the float32 error the kernel's
   evaluation order can carry), on at most 1e-5 of the elements (for every
-  code format: E4M3, E5M2 and INT8);
+  code format: E4M3, E5M2 and INT8); every differing code is verified;
 * alpha and s within 1e-6 relative;
-* reconstructions within 1e-3 relative RMS of the oracle's reconstruction.
+* reconstructions within 1e-3 relative RMS of the oracle's reconstruction,
+  and element by element within the float32 error of the kernel's arithmetic
+  (plus one output rounding).
+
+Large tensors are compared in full: the oracle runs on contiguous runs of
+blocks on several host threads (one oracle call per run; blocks are
+independent, so the result is the oracle's on the whole tensor).
 """
 from __future__ import annotations
 
 import math
+import os
+from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 
@@ -24,10 +32,147 @@ QMAX = 448.0
 QMAX_OF = {"e4m3": 448.0, "e5m2": 57344.0, "int8": 127.0}
 U32 = 2.0 ** -24          # float32 unit roundoff
 
-# Flips and elements over every comparison of the session: the rate bound
-# applies to this total (a test case smaller than 1e5 elements may show one
-# tie-verified flip on its own; the aggregate must still stay below 1e-5).
-TOTALS = {"flips": 0, "n": 0}
+# Owner step: the rate of tie flips depends on the data, since its codes are
+# decided on a float32 sum of decoded FP8 payloads, few-bit values whose
+# rotated sums land exactly on rounding ties far more often than bf16 data
+# do (2.7-5.4e-5 seen for two payloads without an own partial).  Its stated
+# rate, per case (Poisson bound) and over the session: 1e-4.  Every flip is
+# verified against the float32 bound of the sum individually.
+OWNER_FLIP_RATE = 1e-4
+
+#: Rate bound of each kind of comparison over the session.  "compress": the
+#: operator's sender side (and the fidelity round trips' codes), one
+#: rotation of exact bf16 inputs; "owner": the owner step.
+RATE_OF = {"compress": FLIP_RATE, "roundtrip": FLIP_RATE, "owner": OWNER_FLIP_RATE}
+
+# Flips and elements over every comparison of the session, per kind and code
+# format: {(kind, fmt): [flips, elements]}.  A case may show a few
+# tie-verified flips on its own (Poisson bound below); the session total of
+# each kind must stay within its rate (checked when the session ends, in
+# conftest.py, after every test file).
+TOTALS: dict = {}
+
+
+def tally(kind: str, fmt: str, flips: int, n: int) -> None:
+    t = TOTALS.setdefault((kind, fmt), [0, 0])
+    t[0] += int(flips)
+    t[1] += int(n)
+
+
+def session_report():
+    """[(kind, fmt, flips, elements, rate bound, within bound)] of the session."""
+    rows = []
+    for (kind, fmt), (f, n) in sorted(TOTALS.items()):
+        rate = RATE_OF[kind]
+        rows.append((kind, fmt, f, n, rate, f <= rate * max(n, 1)))
+    return rows
+
+
+def session_check():
+    """(report lines, every total within its rate) for the session's code
+    comparisons."""
+    rows = session_report()
+    lines = []
+    for kind, fmt, f, n, rate, ok in rows:
+        lines.append(f"code flips [{kind} {fmt}]: {f} in {n} elements "
+                     f"({f / max(n, 1):.2e}; bound {rate:g})" + ("" if ok else "  EXCEEDED"))
+    ok = all(r[-1] for r in rows)
+    if not ok:
+        lines.append("FAILED: a session total of code flips exceeds its rate")
+    return lines, ok
+
+
+def threads() -> int:
+    """Host threads for the oracle (the CPU share of one GPU: at most 16)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        n = os.cpu_count() or 1
+    return max(1, min(n, 16))
+
+
+#: Largest run of blocks handled by one oracle call or comparison step, in
+#: blocks: small runs keep each step's temporaries (a few MB) reusable from
+#: the heap instead of freshly mapped pages.
+RUN_BLOCKS = 4096
+
+
+def block_runs(m: int, nthreads: int | None = None, run: int | None = None):
+    """Contiguous runs [lo, hi) of blocks covering 0..m: at most `run`
+    blocks each, and at least one per thread when m allows."""
+    nt = nthreads or threads()
+    size = max(1, min(run or RUN_BLOCKS, -(-m // nt)))
+    return [(lo, min(lo + size, m)) for lo in range(0, m, size)]
+
+
+def run_blocks(fn, m: int, nthreads: int | None = None):
+    """fn(lo, hi) over runs of blocks, on a thread pool (each oracle call is
+    one C call, which releases the GIL).  Returns the list of results."""
+    runs = block_runs(m, nthreads)
+    if len(runs) == 1:
+        return [fn(*runs[0])]
+    with ThreadPoolExecutor(nthreads or threads()) as pool:
+        return list(pool.map(lambda r: fn(*r), runs))
+
+
+def oracle_compress(x_bits, B, tau=1.0, fmt="e4m3"):
+    """oracle.compress of a flattened tensor, runs of blocks on host threads."""
+    x = np.ascontiguousarray(x_bits).reshape(-1)
+    m = x.size // B
+    codes = np.empty(x.size, np.uint8)
+    alpha = np.empty(m, np.float32)
+    scale = np.empty(m, np.float32)
+
+    def part(lo, hi):
+        c, a, s = oracle.compress(x[lo * B:hi * B], B, tau, fmt=fmt)
+        codes[lo * B:hi * B] = c.reshape(-1)
+        alpha[lo:hi] = a
+        scale[lo:hi] = s
+    run_blocks(part, m)
+    return codes, alpha, scale
+
+
+def oracle_decompress(codes, alpha, scale, B, fmt="e4m3"):
+    """oracle.decompress (bf16 bit patterns) of a flattened payload, runs of
+    blocks on host threads."""
+    c = np.ascontiguousarray(codes).reshape(-1)
+    m = c.size // B
+    y = np.empty(c.size, np.uint16)
+
+    def part(lo, hi):
+        y[lo * B:hi * B] = oracle.decompress(c[lo * B:hi * B], alpha[lo:hi], scale[lo:hi], B,
+                                             fmt=fmt)
+    run_blocks(part, m)
+    return y
+
+
+def oracle_accumulate(codes, alpha, scale, B, acc, fmt="e4m3"):
+    """oracle.decompress_accumulate of a flattened payload into acc (float32,
+    in place), runs of blocks on host threads."""
+    c = np.ascontiguousarray(codes).reshape(-1)
+    assert acc.dtype == np.float32 and acc.flags["C_CONTIGUOUS"] and acc.size == c.size
+    a = acc.reshape(-1)
+
+    def part(lo, hi):
+        oracle.decompress_accumulate(c[lo * B:hi * B], alpha[lo:hi], scale[lo:hi], B,
+                                     a[lo * B:hi * B], fmt=fmt)
+    run_blocks(part, c.size // B)
+    return acc
+
+
+def bf16_rel_rms(y_bits, ref_bits) -> float:
+    """Relative RMS of one bf16 tensor against another (runs on host threads)."""
+    a = np.ascontiguousarray(y_bits).reshape(-1)
+    b = np.ascontiguousarray(ref_bits).reshape(-1)
+
+    def part(lo, hi):
+        ya = synth.bits_to_f32(a[lo:hi]).astype(np.float64)
+        yb = synth.bits_to_f32(b[lo:hi]).astype(np.float64)
+        d = ya - yb
+        return float(np.dot(d, d)), float(np.dot(yb, yb))
+    res = run_blocks(part, a.size)
+    num, den = sum(r[0] for r in res), sum(r[1] for r in res)
+    return math.sqrt(num / den) if den > 0 else math.sqrt(num)
 
 
 def allowed_flips(n: int, rate: float = FLIP_RATE) -> float:
@@ -101,20 +246,20 @@ def _tie_ok(x_block, code_gpu, code_or, j, B, fmt="e4m3") -> tuple[bool, str]:
     return True, ""
 
 
-def compare_compress(x_bits, B, codes, alpha, scale, tau=1.0, max_flip_checks=200, fmt="e4m3"):
-    """Check the GPU's (codes, alpha, scale) of x_bits against the oracle.
-    Returns a dict of statistics; raises AssertionError on a violation."""
+def compare_compress(x_bits, B, codes, alpha, scale, tau=1.0, fmt="e4m3", kind="compress"):
+    """Check the GPU's (codes, alpha, scale) of x_bits against the oracle;
+    every differing code is verified to be one the kernel's float32
+    evaluation can give.  Returns a dict of statistics; raises
+    AssertionError on a violation."""
     x_bits = np.ascontiguousarray(x_bits).reshape(-1)
     codes = np.ascontiguousarray(codes).reshape(-1)
-    o_codes, o_alpha, o_scale = oracle.compress(x_bits, B, tau, fmt=fmt)
-    o_codes = o_codes.reshape(-1)
+    o_codes, o_alpha, o_scale = oracle_compress(x_bits, B, tau, fmt)
     bad = np.nonzero(codes != o_codes)[0]
     n = x_bits.size
-    TOTALS["flips"] += int(bad.size)
-    TOTALS["n"] += int(n)
+    tally(kind, fmt, bad.size, n)
     assert bad.size <= allowed_flips(n), \
         f"{bad.size} code mismatches in {n} elements (allowed {allowed_flips(n):.1f})"
-    for i in bad[:max_flip_checks]:
+    for i in bad:
         k, j = divmod(int(i), B)
         ok, why = _tie_ok(x_bits[k * B:(k + 1) * B], codes[i], o_codes[i], j, B, fmt)
         assert ok, f"element {i} (block {k}): {why}"
@@ -129,30 +274,193 @@ def compare_compress(x_bits, B, codes, alpha, scale, tau=1.0, max_flip_checks=20
 def compare_decompress(y_bits, o_codes, o_alpha, o_scale, B, fmt="e4m3"):
     """GPU bf16 output y_bits (from the oracle's codes) against the oracle's
     bf16 output (relative RMS) and against its exact reconstruction
-    (element-wise, one bf16 rounding plus the kernel's float32 error)."""
-    ref = oracle.reconstruct_f64(o_codes, o_alpha, o_scale, B, fmt=fmt).reshape(-1)
-    ref_bf16 = synth.bits_to_f32(oracle.decompress(o_codes, o_alpha, o_scale, B,
-                                                   fmt=fmt)).reshape(-1)
-    y = synth.bits_to_f32(np.asarray(y_bits).reshape(-1)).astype(np.float64)
-    r = rel_rms(y, ref_bf16)
+    (element-wise, one bf16 rounding plus the kernel's float32 error).
+    Runs of blocks on host threads."""
+    y_all = np.ascontiguousarray(y_bits).reshape(-1)
+    c_all = np.ascontiguousarray(o_codes).reshape(-1)
+    m = c_all.size // B
+
+    def part(lo, hi):
+        sl = slice(lo * B, hi * B)
+        c, a, s = c_all[sl], o_alpha[lo:hi], o_scale[lo:hi]
+        ref = oracle.reconstruct_f64(c, a, s, B, fmt=fmt)
+        ref_bf16 = synth.bits_to_f32(oracle.decompress(c, a, s, B, fmt=fmt)).astype(np.float64)
+        y = synth.bits_to_f32(y_all[sl]).astype(np.float64)
+        # Element-wise: within one bf16 step of the exact value, plus the
+        # kernel's float32 rounding relative to the block's largest output.
+        blk_max = np.repeat(np.max(np.abs(ref.reshape(-1, B)), axis=1), B)
+        # (bf16 subnormals, below 2^-126, are spaced 2^-133 apart.)
+        tol = 2.0 ** -8 * np.abs(ref) + 2.0 ** -16 * blk_max + 2.0 ** -133
+        worst = float(np.max(np.abs(y - ref) - tol))
+        d = y - ref_bf16
+        return worst, float(np.dot(d, d)), float(np.dot(ref_bf16, ref_bf16))
+
+    res = run_blocks(part, m)
+    worst = max(r[0] for r in res)
+    num, den = sum(r[1] for r in res), sum(r[2] for r in res)
+    r = math.sqrt(num / den) if den > 0 else math.sqrt(num)
     assert r <= RECON_RTOL, f"decompress rel RMS {r:.3g}"
-    # Element-wise: within one bf16 step of the exact value, plus the
-    # kernel's float32 rounding relative to the block's largest output.
-    blk_max = np.repeat(np.max(np.abs(ref.reshape(-1, B)), axis=1), B)
-    # (bf16 subnormals, below 2^-126, are spaced 2^-133 apart.)
-    tol = 2.0 ** -8 * np.abs(ref) + 2.0 ** -16 * blk_max + 2.0 ** -133
-    worst = float(np.max(np.abs(y - ref) - tol))
     assert worst <= 0, f"decompress element error exceeds tolerance by {worst:.3g}"
     return {"rel_rms": r}
 
 
-# Owner step: cap on tie flips per case, a guard against systematic error.
-# Every flip is verified against the float32 bound individually; the rate
-# itself depends on the data, since a sum of decoded FP8 payloads is made of
-# few-bit values whose rotated sums land exactly on rounding ties far more
-# often than bf16 data do (2.7-5.4e-5 seen for two payloads without an own
-# partial).
-OWNER_FLIP_RATE = 1e-4
+def compare_accumulate(got_acc, acc0, payloads, B, fmt="e4m3", out=None):
+    """GPU float32 accumulator after acc0 += G'_p for the payloads, in order
+    (each payload the oracle's own codes, alpha and s, so that the kernel is
+    checked alone), against the oracle's (decompress_accumulate per payload),
+    element by element.  Per payload the kernel's G'_p carries the float32
+    error of an inverse FWHT of the decoded codes d_p (at most log2(B)
+    roundings of partial sums bounded by |d_p|_1, times the factor
+    f_p = s_p / (sqrt(B) alpha_p)) and of the factor and product (a few units
+    of G'_p); the accumulator adds one rounding on each side:
+        |acc - acc_oracle| <= sum_p 2^-23 (log2(B) |f_p| |d_p|_1 + 4 |G'_p|
+                                           + 2 (|acc0| + sum_{q<=p} |G'_q|)),
+    twice the first-order bound, plus a few subnormal steps.  Also the
+    relative RMS against the oracle (<= 1e-6).  Runs of blocks on host
+    threads.  out (float32, optional) receives the oracle's accumulator."""
+    got = np.ascontiguousarray(got_acc).reshape(-1)
+    a0 = np.ascontiguousarray(acc0, dtype=np.float32).reshape(-1)
+    pays = [(np.ascontiguousarray(c).reshape(-1), np.asarray(a, np.float32).reshape(-1),
+             np.asarray(s, np.float32).reshape(-1)) for c, a, s in payloads]
+    m = got.size // B
+    log_b = math.log2(B)
+
+    def part(lo, hi):
+        sl = slice(lo * B, hi * B)
+        ref = a0[sl].copy()
+        run = np.abs(ref).astype(np.float64)
+        tol = np.zeros(ref.size)
+        for c, a, s in pays:
+            cc, aa, ss = c[sl], a[lo:hi], s[lo:hi]
+            oracle.decompress_accumulate(cc, aa, ss, B, ref, fmt=fmt)
+            g = np.abs(oracle.reconstruct_f64(cc, aa, ss, B, fmt=fmt))
+            with np.errstate(divide="ignore", invalid="ignore"):
+                f = np.where(aa != 0, ss.astype(np.float64) / (math.sqrt(B) * aa), 0.0)
+            d1 = np.sum(np.abs(oracle.decode(cc, fmt)).reshape(-1, B), axis=1)
+            run += g
+            tol += 2.0 ** -23 * (log_b * np.repeat(np.abs(f) * d1, B) + 4 * g + 2 * run)
+        tol += len(pays) * 4 * 2.0 ** -149
+        if out is not None:
+            out[sl] = ref
+        diff = np.abs(got[sl].astype(np.float64) - ref)
+        worst = float(np.max(diff - tol)) if diff.size else 0.0
+        e = got[sl].astype(np.float64) - ref
+        return worst, float(np.dot(e, e)), float(np.dot(ref.astype(np.float64), ref))
+
+    res = run_blocks(part, m)
+    worst = max(r[0] for r in res)
+    num, den = sum(r[1] for r in res), sum(r[2] for r in res)
+    r = math.sqrt(num / den) if den > 0 else math.sqrt(num)
+    assert worst <= 0, f"accumulator element error exceeds its float32 bound by {worst:.3g}"
+    assert r <= 1e-6, f"accumulate rel RMS {r:.3g}"
+    return {"rel_rms": r}
+
+
+#: Round-trip variants that rotate the block (their codes live in the
+#: rotated domain).
+ROTATING = {"taco", "ash", "hadamard"}
+_CODE_VALUES = {}
+
+
+def code_values(fmt: str) -> np.ndarray:
+    """The distinct finite values of a format's codes, ascending."""
+    if fmt not in _CODE_VALUES:
+        v = oracle.decode(np.arange(256, dtype=np.uint8), fmt)
+        _CODE_VALUES[fmt] = np.unique(v[np.isfinite(v)])
+    return _CODE_VALUES[fmt]
+
+
+def adjacent_changes(value: float, fmt: str) -> np.ndarray:
+    """Changes that move the code value nearest `value` to a neighbouring
+    code value (0 included: no change)."""
+    vals = code_values(fmt)
+    i = int(np.argmin(np.abs(vals - value)))
+    out = [0.0]
+    if i > 0:
+        out.append(vals[i - 1] - vals[i])
+    if i + 1 < vals.size:
+        out.append(vals[i + 1] - vals[i])
+    return np.array(out)
+
+
+def _code_factor(x_block, B, variant, fmt, tau, tensor_delta):
+    """c such that the oracle's round trip of a block is c * decode(q) in the
+    code domain (H x' / sqrt(B) for the rotating variants, x' itself for the
+    others): s/alpha (the operator), 1/alpha (ASH alone), s (DS alone), the
+    tensor step, or 1 (direct cast, plain rotation)."""
+    if variant in ("direct", "hadamard"):
+        return 1.0
+    if variant == "tensor":
+        return tensor_delta
+    if variant == "ds":
+        m = float(np.max(np.abs(synth.bits_to_f32(x_block).astype(np.float64))))
+        return float(np.float32(m / QMAX_OF[fmt]))
+    _, a, sc = oracle.compress(x_block, B, tau, fmt=fmt)
+    a, sc = float(a[0]), float(sc[0])
+    if a == 0.0:
+        return 0.0
+    return 1.0 / a if variant == "ash" else sc / a
+
+
+def compare_roundtrip(y_bits, x_bits, B, variant, fmt="e4m3", tau=1.0, xo=None):
+    """GPU bf16 output of a fidelity round trip (taco_roundtrip) against the
+    oracle's (roundtrip_variant), element by element.  Where no code
+    differs, an element is within one bf16 rounding of the oracle's value
+    plus the float32 error of the kernel's arithmetic relative to the
+    block's largest value.  The round trip does not return its codes, so a
+    tie flip shows only in its output.  A block beyond that bound must be
+    explained by at most two adjacent-code changes: in the code domain (the
+    rotated domain H x' / sqrt(B) for the rotating variants, x' itself for
+    the others), where the oracle's block is c * decode(q), each of the two
+    largest entries of the difference is matched with the change to a
+    neighbouring code of the oracle's code there (or none) that leaves the
+    smallest remainder; those changes, times c, are subtracted, and what is
+    left must be within the element bound.  The number of such blocks counts
+    as flips against the rate.  Also the relative RMS (1e-3)."""
+    y = synth.bits_to_f32(np.ascontiguousarray(y_bits).reshape(-1)).astype(np.float64)
+    xb_all = np.ascontiguousarray(x_bits).reshape(-1)
+    if xo is None:
+        xo = oracle.roundtrip_variant(xb_all, B, variant, fmt, tau).reshape(-1)
+    ref = synth.bits_to_f32(oracle.double_to_bf16(xo)).astype(np.float64)
+    n = y.size
+    r = rel_rms(y, ref)
+    assert r <= RECON_RTOL, f"{variant}/{fmt}: reconstruction rel RMS {r:.3g}"
+    xo2 = xo.reshape(-1, B)
+    blk = np.max(np.abs(xo2), axis=1, keepdims=True)
+    tol = (2.0 ** -8 * np.abs(xo2) + 2.0 ** -16 * blk + 2.0 ** -133)
+    err = (y - xo).reshape(-1, B)
+    over = np.nonzero(np.any(np.abs(err) > tol, axis=1))[0]
+    tally("roundtrip", fmt, over.size, n)
+    assert over.size <= allowed_flips(n), \
+        f"{variant}/{fmt}: {over.size} blocks beyond the element bound in {n} elements"
+    rot = variant in ROTATING
+    delta = 0.0
+    if variant == "tensor" and over.size:
+        tmax = float(np.max(np.abs(synth.bits_to_f32(xb_all).astype(np.float64))))
+        delta = float(np.float32(tmax / QMAX_OF[fmt]))
+    for k in over:
+        e, t = err[k], tol[k]
+        c = _code_factor(xb_all[k * B:(k + 1) * B], B, variant, fmt, tau, delta)
+        assert c != 0.0, f"{variant}/{fmt} block {k}: an all-zero block differs"
+        if rot:
+            dom = oracle.fwht(e) / math.sqrt(B)
+            ref_dom = oracle.fwht(xo2[k]) / math.sqrt(B)
+        else:
+            dom, ref_dom = e.copy(), xo2[k].copy()
+        change = np.zeros(B)
+        for j in np.argsort(-np.abs(dom))[:2]:
+            steps = adjacent_changes(ref_dom[j] / c, fmt) * c
+            change[j] = steps[int(np.argmin(np.abs(dom[j] - steps)))]
+        back = oracle.fwht(change) / math.sqrt(B) if rot else change
+        rest = e - back
+        # The kernel rounds its own value (the oracle's plus the change) to
+        # bf16: the bound follows the larger of the two magnitudes.
+        moved = np.abs(xo2[k] + back)
+        t = np.maximum(t, 2.0 ** -8 * moved + 2.0 ** -16 * np.max(moved) + 2.0 ** -133)
+        assert np.all(np.abs(rest) <= t * (1 + 1e-9)), \
+            (f"{variant}/{fmt} block {k}: error beyond the bound that no two adjacent-code "
+             f"changes explain (worst remainder {np.max(np.abs(rest) - t):.3g})")
+    return {"rel_rms": r, "flip_blocks": int(over.size)}
 
 
 def reachable(code, v, bound, fmt="e4m3") -> bool:
@@ -185,8 +493,8 @@ def rotated_sum_error(own_bits, payloads, B, fmt="e4m3"):
     return 2.0 ** -23 * (np.log2(B) * np.repeat(own_l1, B) + (P + 2) * pay)
 
 
-def compare_reduce(own_bits, payloads, B, codes, alpha, scale, tau=1.0, max_flip_checks=200,
-                   fmt="e4m3", cancelling=False):
+def compare_reduce(own_bits, payloads, B, codes, alpha, scale, tau=1.0, fmt="e4m3",
+                   cancelling=False):
     """Check the GPU owner step (codes, alpha, scale of own + sum of payload
     reconstructions) against the oracle.  The kernel decides the codes on a
     float32 rotated-domain sum of the own partial and every payload, the
@@ -215,8 +523,8 @@ def compare_reduce(own_bits, payloads, B, codes, alpha, scale, tau=1.0, max_flip
     for c, a, s in payloads:
         x += oracle.reconstruct_f64(c, a, s, B, fmt=fmt).reshape(-1)
     bad = np.nonzero(codes != o_codes)[0]
-    TOTALS["flips"] += int(bad.size)
-    TOTALS["n"] += int(n)
+    if not cancelling:
+        tally("owner", fmt, bad.size, n)
     # The codes are decided on a float32 sum of `terms` rotated vectors, each
     # adding its own rounding: the flip rate of the operator (one rotation
     # of exact bf16 inputs) applies per term.

@@ -180,7 +180,7 @@ def sample_blocks(M, n, seed):
 
 @pytest.mark.parametrize("fmt", FMTS)
 @pytest.mark.parametrize("name,B,full", [("gpt2.7b_rowpar_8192x2560", 128, True),
-                                         ("grad_8192x8192", 256, False)])
+                                         ("grad_8192x8192", 256, True)])
 def test_workloads(taco, fmt, name, B, full):
     import torch
     r = synth.WORKLOADS[name]

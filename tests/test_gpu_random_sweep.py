@@ -10,7 +10,7 @@ import pytest
 
 import oracle
 import synth
-from parity import compare_compress, compare_decompress, compare_reduce
+from parity import FLIP_RATE, compare_compress, compare_decompress, compare_reduce
 from test_gpu_accumulate_n import check as accumulate_n_check
 from test_gpu_fidelity import check_variant
 
@@ -32,7 +32,8 @@ def test_random_sweep():
 
     names = sorted(synth.WORKLOADS)
     rng = np.random.default_rng(20261202)
-    flips = n_all = owners = 0
+    flips = {"e4m3": [0, 0], "e5m2": [0, 0], "int8": [0, 0]}
+    owners = 0
     for case in range(CASES):
         B = int(rng.choice([32, 64, 128, 256, 512]))
         fmt = str(rng.choice(["e4m3", "e4m3", "e5m2", "int8"]))
@@ -55,8 +56,8 @@ def test_random_sweep():
         c, a, s = taco.compress(gpu_bf16(x), block=B, fmt=fmt)
         torch.cuda.synchronize()
         st = compare_compress(x, B, c.cpu().numpy(), a.cpu().numpy(), s.cpu().numpy(), fmt=fmt)
-        flips += st["flips"]
-        n_all += st["n"]
+        flips[fmt][0] += st["flips"]
+        flips[fmt][1] += st["n"]
         oc, oa, os_ = st.pop("oracle")
         y = taco.decompress(gpu(oc, x.shape), gpu(oa), gpu(os_), block=B, fmt=fmt)
         torch.cuda.synchronize()
@@ -79,5 +80,8 @@ def test_random_sweep():
             compare_reduce(own, pays, B, co.cpu().numpy(), ao.cpu().numpy(), so.cpu().numpy(),
                            fmt=fmt)
             owners += 1
-    print(f"sweep: {CASES} cases ({owners} owner steps), compress flips {flips} of {n_all}",
-          flush=True)
+    print(f"sweep: {CASES} cases ({owners} owner steps), compress flips per format "
+          f"(flips, elements): {flips}", flush=True)
+    # The contract's rate on the sweep's own compress comparisons, per format.
+    for fmt, (f, n) in flips.items():
+        assert f <= FLIP_RATE * max(n, 1), f"{fmt}: {f} flips in {n} elements"
