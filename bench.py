@@ -681,6 +681,64 @@ def add_reference(torch, n: int, use_graph: bool) -> dict:
     return {"bytes": 3 * n, "us": round(t * 1e6, 3), "GBps": round(3 * n / t / 1e9, 1)}
 
 
+def launch_groups(n: int, block: int) -> int:
+    """Work-groups of libtaco's compress / decompress launch on n elements
+    (four wavefronts each; one wave-step of 64 / LPB blocks per wavefront,
+    LPB = 4, 8, 8, 8, 16 lanes per block for B = 32 ... 512; two wave-steps
+    per wavefront at B <= 64 from 16384 wave-steps up)."""
+    lpb = {32: 4, 64: 8, 128: 8, 256: 8, 512: 16}[block]
+    steps = -(-(n // block) // (64 // lpb))
+    if block <= 64 and steps >= 16384:
+        steps = -(-steps // 2)
+    return max(1, -(-steps // 4))
+
+
+def launch_floor(torch, probe, groups: int, use_graph: bool, count: int = 2000) -> dict:
+    """An empty kernel on the same grid, `count` launches back to back (one
+    graph, one untimed replay first): what any launch of that shape costs."""
+    timer = Timer(torch)
+    fn = make_graph(torch, lambda: [probe.empty(groups) for _ in range(count)], use_graph)
+    fn()
+    t = timer.time(fn, 1) / count
+    return {"kernel": "empty", "groups": groups, "us": round(t * 1e6, 3)}
+
+
+def stream_floor(torch, probe, mix: str, n: int, algorithmic_bytes_: float, kernel_s: float,
+                 use_graph: bool) -> dict:
+    """A plain stream of the kernel's byte mix over the same number of
+    elements (16-byte non-temporal loads and stores, 1 KiB per instruction,
+    no arithmetic; libtaco_probe), timed like the operator's kernels: buffer
+    sets rotated over more than 1 GiB of loads, graphs, a continuous warmup.
+    Its rate is the streaming ceiling a single launch of that size reaches."""
+    ld, sto = probe.MIXES[mix]
+    waves = max(1, n // 1024)
+    load_bytes, store_bytes = waves * ld * 1024, waves * sto * 1024
+    nsets = rotation_sets(load_bytes, load_bytes + store_bytes)
+    sets = [(torch.ones(load_bytes // 2, dtype=torch.bfloat16, device="cuda"),
+             torch.empty(store_bytes, dtype=torch.uint8, device="cuda")) for _ in range(nsets)]
+    timer = Timer(torch)
+    count = max(20, int(-(-WARM_BYTES // (4 * (load_bytes + store_bytes)))))
+
+    def run():
+        for i in range(count):
+            src, dst = sets[i % nsets]
+            probe.stream(mix, src, dst, waves)
+    fn = make_graph(torch, run, use_graph, prerun=False)
+    for _ in range(3):                      # continuous warmup
+        fn()
+    t = timer.time(fn, 1) / count
+    del sets, fn
+    torch.cuda.empty_cache()
+    moved = load_bytes + store_bytes
+    rate = moved / t / 1e9
+    # The kernel's algorithmic bytes add the per-block scalars (8 / B bytes
+    # per element) to the same mix: compare rates, not times.
+    return {"kernel": f"plain stream, {ld} KiB in / {sto} KiB out per wavefront ({mix} mix)",
+            "bytes": moved, "us": round(t * 1e6, 3), "GBps": round(rate, 1),
+            "frac": round(rate / HBM_PEAK_GBS, 4),
+            "kernel_rate_vs_stream": round((algorithmic_bytes_ / kernel_s) / (moved / t), 4)}
+
+
 def torch_reference(torch, synth, cases, use_graph: bool):
     """Context for the roofline: torch's own elementwise kernels moving the
     same bytes as compress at each workload's size (add of two bf16 halves:
@@ -760,6 +818,22 @@ def same_mix_reference(torch, res, use_graph: bool) -> dict:
     return ref
 
 
+def add_floors(torch, rec: dict, res: dict, use_graph: bool) -> None:
+    """roofline.launch_floor and roofline.stream_floor for the line's
+    dominant kernel (compress, decompress or accumulate), measured in the
+    same run."""
+    import gradients_taco_compress_amd.probe as probe
+    roof = rec["roofline"]
+    kern = roof["kernel"]
+    if kern not in ("compress", "decompress", "accumulate"):
+        return
+    print("[bench] launch and stream floors (libtaco_probe)", file=sys.stderr, flush=True)
+    n, block = res["n"], res["block"]
+    roof["launch_floor"] = launch_floor(torch, probe, launch_groups(n, block), use_graph)
+    roof["stream_floor"] = stream_floor(torch, probe, kern, n, roof["algorithmic_bytes"],
+                                        res["kernels"][kern], use_graph)
+
+
 def config_summary(rec: dict) -> dict:
     """The figures of one round-trip workload for the default line's
     "configs" list (never part of its value)."""
@@ -770,8 +844,9 @@ def config_summary(rec: dict) -> dict:
            "repeats_pct_hbm_peak_median": (rec.get("repeats") or {}).get("pct_hbm_peak_median")}
     roof = rec["roofline"]
     out["roofline"] = {k: roof.get(k) for k in ("kernel", "achieved", "frac", "traffic")}
-    if "same_mix_stream" in roof:
-        out["same_mix_stream"] = roof["same_mix_stream"]
+    for key in ("same_mix_stream", "launch_floor", "stream_floor"):
+        if key in roof:
+            out[key] = roof[key]
     return out
 
 
@@ -833,6 +908,8 @@ def main():
                 (i == 0 or (base, block) in ROUNDTRIP_CONFIGS):
             print("[bench] same-mix stream reference (torch add)", file=sys.stderr, flush=True)
             rec["roofline"]["same_mix_stream"] = same_mix_reference(torch, res, use_graph)
+        if i == 0 and not name.split(":")[1:]:
+            add_floors(torch, rec, res, use_graph)
         recs.append(rec)
         if args.all:
             print(json.dumps(rec), file=sys.stderr, flush=True)
@@ -845,6 +922,7 @@ def main():
             res, base, _ = run_case(torch, taco, synth, name, block, None, None, use_graph)
             rec = record(res, base, args)
             rec["roofline"]["same_mix_stream"] = same_mix_reference(torch, res, use_graph)
+            add_floors(torch, rec, res, use_graph)
             configs.append(config_summary(rec))
         recs[0]["configs"] = configs
     if args.out:

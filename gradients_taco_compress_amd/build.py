@@ -22,6 +22,9 @@ ALL_FILES = SOURCES + [os.path.join(CSRC, "taco_kernels.hpp"),
                        os.path.join(CSRC, "taco_internal.hpp")]
 HEADER = os.path.join(ROOT, "include", "taco.h")
 LIB = os.path.join(PKG, "libtaco.so")
+#: The measurement kernels (not part of the operator), a library of their own.
+PROBE_SOURCE = os.path.join(CSRC, "taco_probe.hip")
+PROBE_LIB = os.path.join(PKG, "libtaco_probe.so")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
@@ -51,21 +54,26 @@ def _run(cmd, verbose: bool) -> None:
 
 
 def build(verbose: bool = False) -> str:
-    """Compile every source (in parallel) and link LIB; always recompiles."""
+    """Compile every source (in parallel), link LIB and PROBE_LIB; always
+    recompiles.  Returns LIB."""
     from concurrent.futures import ThreadPoolExecutor
     tag = f".tmp{os.getpid()}"
-    objs = [os.path.join(CSRC, os.path.basename(src) + tag + ".o") for src in SOURCES]
+    sources = SOURCES + [PROBE_SOURCE]
+    objs = [os.path.join(CSRC, os.path.basename(src) + tag + ".o") for src in sources]
     try:
-        with ThreadPoolExecutor(max_workers=len(SOURCES)) as pool:
+        with ThreadPoolExecutor(max_workers=len(sources)) as pool:
             jobs = [pool.submit(_run, [HIPCC, *FLAGS, "-I", os.path.join(ROOT, "include"),
                                        "-c", src, "-o", obj], verbose)
-                    for src, obj in zip(SOURCES, objs)]
+                    for src, obj in zip(sources, objs)]
             for j in jobs:
                 j.result()
-        _run([HIPCC, "--offload-arch=gfx950", "-shared", *objs, "-o", LIB + tag], verbose)
+        _run([HIPCC, "--offload-arch=gfx950", "-shared", *objs[:-1], "-o", LIB + tag], verbose)
+        _run([HIPCC, "--offload-arch=gfx950", "-shared", objs[-1], "-o", PROBE_LIB + tag],
+             verbose)
         os.replace(LIB + tag, LIB)
+        os.replace(PROBE_LIB + tag, PROBE_LIB)
     finally:
-        for path in objs + [LIB + tag]:
+        for path in objs + [LIB + tag, PROBE_LIB + tag]:
             if os.path.exists(path):
                 os.remove(path)
     return LIB

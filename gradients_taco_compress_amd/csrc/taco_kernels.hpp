@@ -1741,7 +1741,9 @@ __global__ __launch_bounds__(kGroup) void decode_kernel(const uint8_t *__restric
 unsigned grid_for(int64_t nsteps) {
     constexpr int64_t per_group = (int64_t)kWavesPerGroup * TACO_STEPS_PER_WAVE;
     int64_t g = (nsteps + per_group - 1) / per_group;
-    const int64_t cap = INT64_C(1) << 30;
+    // A dispatch counts its work-items in 32 bits: at most 2^32 - 1 threads.
+    // Larger tensors take several wave-steps per wave (grid-stride loops).
+    const int64_t cap = (INT64_C(0xFFFFFFFF) / kGroup);
     g = g < cap ? g : cap;
     return (unsigned)(g > 0 ? g : 1);
 }

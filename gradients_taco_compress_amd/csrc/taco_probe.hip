@@ -1,0 +1,82 @@
+// libtaco_probe (declared in include/taco_probe.h): an empty kernel and
+// plain streaming kernels with the byte mixes of libtaco's kernels, for
+// measuring the launch floor and the streaming ceiling at each tensor size.
+// Not part of the operator; built as its own library.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "taco_probe.h"
+
+namespace {
+
+constexpr int kGroup = TACO_PROBE_GROUP;
+constexpr int kWave = 64;
+constexpr int kWavesPerGroup = kGroup / kWave;
+typedef unsigned int u4v __attribute__((ext_vector_type(4)));
+
+__global__ __launch_bounds__(kGroup) void probe_empty_kernel() {}
+
+// Wavefront w moves LD KiB in and ST KiB out: lane l reads the 16 bytes at
+// 1024 i + 16 l of its KiB i (one contiguous KiB per instruction) and
+// writes likewise.  All loads are issued before the first store.
+template <int LD, int ST>
+__global__ __launch_bounds__(kGroup) void probe_stream_kernel(const u4v *__restrict__ src,
+                                                              u4v *__restrict__ dst,
+                                                              int64_t waves) {
+    const int64_t w = (int64_t)blockIdx.x * kWavesPerGroup +
+                      __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    if (w >= waves) return;
+    const int lane = threadIdx.x & (kWave - 1);
+    const u4v *s = src + w * (LD * kWave) + lane;
+    u4v v[LD];
+#pragma unroll
+    for (int i = 0; i < LD; ++i) v[i] = __builtin_nontemporal_load(s + i * kWave);
+    u4v acc = v[0];
+#pragma unroll
+    for (int i = 1; i < LD; ++i) acc ^= v[i];
+    u4v *d = dst + w * (ST * kWave) + lane;
+#pragma unroll
+    for (int j = 0; j < ST; ++j) __builtin_nontemporal_store(acc + (unsigned)j, d + j * kWave);
+}
+
+template <int LD, int ST>
+int launch_stream(const void *src, void *dst, int64_t waves, hipStream_t stream) {
+    const int64_t groups = (waves + kWavesPerGroup - 1) / kWavesPerGroup;
+    hipLaunchKernelGGL((probe_stream_kernel<LD, ST>), dim3((unsigned)groups), dim3(kGroup), 0,
+                       stream, static_cast<const u4v *>(src), static_cast<u4v *>(dst), waves);
+    return hipGetLastError() == hipSuccess ? TACO_PROBE_OK : TACO_PROBE_ERR_HIP;
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+}  // namespace
+
+// A dispatch counts its work-items in 32 bits.
+constexpr int64_t kMaxGroups = INT64_C(0xFFFFFFFF) / kGroup;
+
+extern "C" {
+
+int taco_probe_empty(int64_t groups, hipStream_t stream) {
+    if (groups < 1 || groups > kMaxGroups) return TACO_PROBE_ERR_ARGS;
+    hipLaunchKernelGGL(probe_empty_kernel, dim3((unsigned)groups), dim3(kGroup), 0, stream);
+    return hipGetLastError() == hipSuccess ? TACO_PROBE_OK : TACO_PROBE_ERR_HIP;
+}
+
+int taco_probe_stream(int32_t loads, int32_t stores, const void *src, void *dst, int64_t waves,
+                      hipStream_t stream) {
+    if (waves < 1 || (waves + kWavesPerGroup - 1) / kWavesPerGroup > kMaxGroups)
+        return TACO_PROBE_ERR_ARGS;
+    if (!src || !dst || !aligned16(src) || !aligned16(dst)) return TACO_PROBE_ERR_ARGS;
+    const uintptr_t s0 = reinterpret_cast<uintptr_t>(src), d0 = reinterpret_cast<uintptr_t>(dst);
+    const uintptr_t ns = (uintptr_t)waves * (uintptr_t)(loads > 0 ? loads : 0) * 1024u;
+    const uintptr_t nd = (uintptr_t)waves * (uintptr_t)(stores > 0 ? stores : 0) * 1024u;
+    if (s0 < d0 + nd && d0 < s0 + ns) return TACO_PROBE_ERR_ARGS;
+    if (loads == 2 && stores == 1) return launch_stream<2, 1>(src, dst, waves, stream);
+    if (loads == 1 && stores == 2) return launch_stream<1, 2>(src, dst, waves, stream);
+    if (loads == 5 && stores == 4) return launch_stream<5, 4>(src, dst, waves, stream);
+    if (loads == 1 && stores == 1) return launch_stream<1, 1>(src, dst, waves, stream);
+    return TACO_PROBE_ERR_ARGS;
+}
+
+}  // extern "C"

@@ -389,3 +389,38 @@ def test_accumulate_n_validation(lib):
     assert ap(npay=0, pays=None, acc=None) == OK
     assert lib.taco_decompress_accumulate_n_packed_fmt(2, None, 4, 256, 128, 3, 2 * A,
                                                        None) == FORMAT
+
+
+PROBE_HEADER = os.path.join(ROOT, "include", "taco_probe.h")
+PROBE_LIB = os.path.join(ROOT, "gradients_taco_compress_amd", "libtaco_probe.so")
+
+
+def test_probe_library_exports_and_validation():
+    """The measurement library exports exactly what its header declares and
+    refuses bad arguments before any launch (without a GPU a valid call
+    fails at the launch)."""
+    text = re.sub(r"/\*.*?\*/", "", open(PROBE_HEADER).read(), flags=re.S)
+    names = sorted(set(re.findall(r"\b(taco_probe_[a-z0-9_]+)\s*\(", text)))
+    out = subprocess.run(["nm", "-D", "--defined-only", PROBE_LIB], capture_output=True,
+                         text=True).stdout
+    assert set(re.findall(r" T (taco_\w+)", out)) == set(names) == {"taco_probe_empty",
+                                                                    "taco_probe_stream"}
+    import gradients_taco_compress_amd.probe as probe
+    assert set(probe.EXPORTS) == set(names)
+    L = ctypes.CDLL(PROBE_LIB)
+    L.taco_probe_empty.argtypes = [ctypes.c_int64, ctypes.c_void_p]
+    L.taco_probe_stream.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
+                                    ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
+    ARGS, LAUNCH = 1, 2
+    assert L.taco_probe_empty(0, None) == ARGS
+    assert L.taco_probe_empty(1 << 24, None) == ARGS          # 2^32 threads: too many
+    assert L.taco_probe_empty(5120, None) == LAUNCH
+    st = lambda ld=2, sto=1, src=A, dst=64 * A, waves=1024: L.taco_probe_stream(
+        ld, sto, src, dst, waves, None)
+    assert st(ld=3) == ARGS and st(ld=2, sto=2) == ARGS        # unsupported mixes
+    assert st(waves=0) == ARGS
+    assert st(src=None) == ARGS and st(dst=A + 8) == ARGS     # null, misaligned
+    assert st(dst=A + 1024) == ARGS                            # overlap
+    assert st(dst=A + 2 * 1024 * 1024) == LAUNCH               # just past src
+    for ld, sto in probe.MIXES.values():
+        assert st(ld=ld, sto=sto) == LAUNCH

@@ -123,3 +123,14 @@ def test_bad_step_counts_are_refused(flag, value):
     out = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), flag, value],
                          capture_output=True, text=True, cwd=ROOT)
     assert out.returncode == 2 and out.stdout == ""
+
+
+def test_launch_groups_follow_the_kernels_launch_shape():
+    # B = 128 and 256: 8 blocks per wave-step, four wave-steps per group.
+    assert bench.launch_groups(8192 * 2560, 128) == 8192 * 2560 // 128 // 8 // 4
+    assert bench.launch_groups(2048 * 1024, 128) == 512
+    assert bench.launch_groups(8192 * 8192, 256) == 8192 * 8192 // 256 // 8 // 4
+    # B = 512: 4 blocks per wave-step; B = 32: 16 blocks, paired from 16384 steps.
+    assert bench.launch_groups(512 * 4 * 4 * 10, 512) == 10
+    assert bench.launch_groups(32 * 16 * 16383, 32) == -(-16383 // 4)
+    assert bench.launch_groups(32 * 16 * 16384, 32) == 16384 // 2 // 4
