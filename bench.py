@@ -81,6 +81,9 @@ def parse():
     p.add_argument("--all", action="store_true", help="time every workload and block size")
     p.add_argument("--out", default=None, help="also write the JSON record(s) to this file")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-floors", action="store_true",
+                   help="skip the launch / stream floors and the same-mix reference (for "
+                        "counter runs, where every dispatch is slow)")
     p.add_argument("--no-configs", action="store_true",
                    help="default line only: skip the round trips of the other workloads "
                         "(reported under 'configs')")
@@ -116,11 +119,16 @@ def algorithmic_bytes(op: str, n: int, block: int) -> float:
     raise ValueError(op)
 
 
+#: libtaco's sources (the measurement kernels of libtaco_probe are not part of it).
+LIBTACO_SOURCES = ("taco_abi.hip", "taco_e4m3.hip", "taco_e5m2.hip", "taco_int8.hip",
+                   "taco_internal.hpp", "taco_kernels.hpp")
+
+
 def kernel_hash() -> str:
-    """sha256[:16] over the library's sources (file names and contents, sorted)."""
+    """sha256[:16] over libtaco's sources (file names and contents, sorted)."""
     h = hashlib.sha256()
     for name in sorted(os.listdir(KERNEL_DIR)):
-        if name.endswith((".hip", ".hpp")):
+        if name in LIBTACO_SOURCES:
             h.update(name.encode())
             with open(os.path.join(KERNEL_DIR, name), "rb") as f:
                 h.update(f.read())
@@ -704,12 +712,14 @@ def launch_floor(torch, probe, groups: int, use_graph: bool, count: int = 2000) 
 
 
 def stream_floor(torch, probe, mix: str, n: int, algorithmic_bytes_: float, kernel_s: float,
-                 use_graph: bool) -> dict:
+                 use_graph: bool, valu: int = 0) -> dict:
     """A plain stream of the kernel's byte mix over the same number of
-    elements (16-byte non-temporal loads and stores, 1 KiB per instruction,
-    no arithmetic; libtaco_probe), timed like the operator's kernels: buffer
-    sets rotated over more than 1 GiB of loads, graphs, a continuous warmup.
-    Its rate is the streaming ceiling a single launch of that size reaches."""
+    elements (16-byte non-temporal loads and stores, 1 KiB per instruction;
+    libtaco_probe), timed like the operator's kernels: buffer sets rotated
+    over more than 1 GiB of loads, graphs, a continuous warmup.  Its rate is
+    the streaming ceiling a single launch of that size reaches.  With valu >
+    0 each wavefront also issues that many dependent VALU instructions
+    between its loads and its stores."""
     ld, sto = probe.MIXES[mix]
     waves = max(1, n // 1024)
     load_bytes, store_bytes = waves * ld * 1024, waves * sto * 1024
@@ -722,7 +732,7 @@ def stream_floor(torch, probe, mix: str, n: int, algorithmic_bytes_: float, kern
     def run():
         for i in range(count):
             src, dst = sets[i % nsets]
-            probe.stream(mix, src, dst, waves)
+            probe.stream(mix, src, dst, waves, valu)
     fn = make_graph(torch, run, use_graph, prerun=False)
     for _ in range(3):                      # continuous warmup
         fn()
@@ -733,8 +743,10 @@ def stream_floor(torch, probe, mix: str, n: int, algorithmic_bytes_: float, kern
     rate = moved / t / 1e9
     # The kernel's algorithmic bytes add the per-block scalars (8 / B bytes
     # per element) to the same mix: compare rates, not times.
-    return {"kernel": f"plain stream, {ld} KiB in / {sto} KiB out per wavefront ({mix} mix)",
-            "bytes": moved, "us": round(t * 1e6, 3), "GBps": round(rate, 1),
+    what = f"plain stream, {ld} KiB in / {sto} KiB out per wavefront ({mix} mix)"
+    if valu:
+        what += f", {valu} dependent VALU instructions per wavefront"
+    return {"kernel": what, "bytes": moved, "us": round(t * 1e6, 3), "GBps": round(rate, 1),
             "frac": round(rate / HBM_PEAK_GBS, 4),
             "kernel_rate_vs_stream": round((algorithmic_bytes_ / kernel_s) / (moved / t), 4)}
 
@@ -832,6 +844,14 @@ def add_floors(torch, rec: dict, res: dict, use_graph: bool) -> None:
     roof["launch_floor"] = launch_floor(torch, probe, launch_groups(n, block), use_graph)
     roof["stream_floor"] = stream_floor(torch, probe, kern, n, roof["algorithmic_bytes"],
                                         res["kernels"][kern], use_graph)
+    valu = roof.get("valu", {}).get("wave_instructions")
+    if valu:
+        # The same stream carrying the kernel's own VALU work: its committed
+        # SQ_INSTS_VALU count per launch spread over the stream's
+        # wavefronts (one per 1024 elements), to a multiple of 4.
+        per_wave = max(4, int(round(valu / max(1, n // 1024) / 4.0)) * 4)
+        roof["stream_valu_floor"] = stream_floor(torch, probe, kern, n, roof["algorithmic_bytes"],
+                                                 res["kernels"][kern], use_graph, per_wave)
 
 
 def config_summary(rec: dict) -> dict:
@@ -844,7 +864,7 @@ def config_summary(rec: dict) -> dict:
            "repeats_pct_hbm_peak_median": (rec.get("repeats") or {}).get("pct_hbm_peak_median")}
     roof = rec["roofline"]
     out["roofline"] = {k: roof.get(k) for k in ("kernel", "achieved", "frac", "traffic")}
-    for key in ("same_mix_stream", "launch_floor", "stream_floor"):
+    for key in ("same_mix_stream", "launch_floor", "stream_floor", "stream_valu_floor"):
         if key in roof:
             out[key] = roof[key]
     return out
@@ -904,11 +924,11 @@ def main():
             print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
             cpu = cpu_baseline(synth, base, block, args.cpu_seconds, acc)
         rec = record(res, base, args, cpu)
-        if rec["roofline"]["kernel"] == "compress" and not res.get("packed") and \
-                (i == 0 or (base, block) in ROUNDTRIP_CONFIGS):
+        if not args.no_floors and rec["roofline"]["kernel"] == "compress" and \
+                not res.get("packed") and (i == 0 or (base, block) in ROUNDTRIP_CONFIGS):
             print("[bench] same-mix stream reference (torch add)", file=sys.stderr, flush=True)
             rec["roofline"]["same_mix_stream"] = same_mix_reference(torch, res, use_graph)
-        if i == 0 and not name.split(":")[1:]:
+        if i == 0 and not name.split(":")[1:] and not args.no_floors:
             add_floors(torch, rec, res, use_graph)
         recs.append(rec)
         if args.all:
@@ -921,8 +941,9 @@ def main():
             print(f"[bench] config {name} block {block}", file=sys.stderr, flush=True)
             res, base, _ = run_case(torch, taco, synth, name, block, None, None, use_graph)
             rec = record(res, base, args)
-            rec["roofline"]["same_mix_stream"] = same_mix_reference(torch, res, use_graph)
-            add_floors(torch, rec, res, use_graph)
+            if not args.no_floors:
+                rec["roofline"]["same_mix_stream"] = same_mix_reference(torch, res, use_graph)
+                add_floors(torch, rec, res, use_graph)
             configs.append(config_summary(rec))
         recs[0]["configs"] = configs
     if args.out:

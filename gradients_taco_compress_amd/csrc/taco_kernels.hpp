@@ -1743,7 +1743,11 @@ unsigned grid_for(int64_t nsteps) {
     int64_t g = (nsteps + per_group - 1) / per_group;
     // A dispatch counts its work-items in 32 bits: at most 2^32 - 1 threads.
     // Larger tensors take several wave-steps per wave (grid-stride loops).
+#ifdef TACO_MAX_GROUPS
+    const int64_t cap = TACO_MAX_GROUPS;
+#else
     const int64_t cap = (INT64_C(0xFFFFFFFF) / kGroup);
+#endif
     g = g < cap ? g : cap;
     return (unsigned)(g > 0 ? g : 1);
 }

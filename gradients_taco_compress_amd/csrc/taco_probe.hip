@@ -19,11 +19,14 @@ __global__ __launch_bounds__(kGroup) void probe_empty_kernel() {}
 
 // Wavefront w moves LD KiB in and ST KiB out: lane l reads the 16 bytes at
 // 1024 i + 16 l of its KiB i (one contiguous KiB per instruction) and
-// writes likewise.  All loads are issued before the first store.
-template <int LD, int ST>
+// writes likewise.  All loads are issued before the first store.  Between
+// them each lane issues `valu` (a multiple of 4) dependent float32 adds on
+// the loaded bits, standing in for a kernel's arithmetic (WORK: a separate
+// instantiation, so that traces tell the two streams apart).
+template <int LD, int ST, bool WORK>
 __global__ __launch_bounds__(kGroup) void probe_stream_kernel(const u4v *__restrict__ src,
                                                               u4v *__restrict__ dst,
-                                                              int64_t waves) {
+                                                              int64_t waves, int valu) {
     const int64_t w = (int64_t)blockIdx.x * kWavesPerGroup +
                       __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     if (w >= waves) return;
@@ -35,16 +38,36 @@ __global__ __launch_bounds__(kGroup) void probe_stream_kernel(const u4v *__restr
     u4v acc = v[0];
 #pragma unroll
     for (int i = 1; i < LD; ++i) acc ^= v[i];
+    if (WORK) {
+        float f0 = __uint_as_float(acc.x), f1 = __uint_as_float(acc.y);
+        float f2 = __uint_as_float(acc.z), f3 = __uint_as_float(acc.w);
+        for (int k = 0; k < valu; k += 4) {
+            // A chain the compiler cannot fold or reorder: each add needs the
+            // previous one's result.
+            asm volatile("v_add_f32 %0, %0, %1" : "+v"(f0) : "v"(f1));
+            asm volatile("v_add_f32 %0, %0, %1" : "+v"(f1) : "v"(f2));
+            asm volatile("v_add_f32 %0, %0, %1" : "+v"(f2) : "v"(f3));
+            asm volatile("v_add_f32 %0, %0, %1" : "+v"(f3) : "v"(f0));
+        }
+        acc = (u4v){__float_as_uint(f0), __float_as_uint(f1), __float_as_uint(f2),
+                    __float_as_uint(f3)};
+    }
     u4v *d = dst + w * (ST * kWave) + lane;
 #pragma unroll
     for (int j = 0; j < ST; ++j) __builtin_nontemporal_store(acc + (unsigned)j, d + j * kWave);
 }
 
 template <int LD, int ST>
-int launch_stream(const void *src, void *dst, int64_t waves, hipStream_t stream) {
+int launch_stream(const void *src, void *dst, int64_t waves, int valu, hipStream_t stream) {
     const int64_t groups = (waves + kWavesPerGroup - 1) / kWavesPerGroup;
-    hipLaunchKernelGGL((probe_stream_kernel<LD, ST>), dim3((unsigned)groups), dim3(kGroup), 0,
-                       stream, static_cast<const u4v *>(src), static_cast<u4v *>(dst), waves);
+    if (valu > 0)
+        hipLaunchKernelGGL((probe_stream_kernel<LD, ST, true>), dim3((unsigned)groups),
+                           dim3(kGroup), 0, stream, static_cast<const u4v *>(src),
+                           static_cast<u4v *>(dst), waves, valu);
+    else
+        hipLaunchKernelGGL((probe_stream_kernel<LD, ST, false>), dim3((unsigned)groups),
+                           dim3(kGroup), 0, stream, static_cast<const u4v *>(src),
+                           static_cast<u4v *>(dst), waves, 0);
     return hipGetLastError() == hipSuccess ? TACO_PROBE_OK : TACO_PROBE_ERR_HIP;
 }
 
@@ -63,19 +86,20 @@ int taco_probe_empty(int64_t groups, hipStream_t stream) {
     return hipGetLastError() == hipSuccess ? TACO_PROBE_OK : TACO_PROBE_ERR_HIP;
 }
 
-int taco_probe_stream(int32_t loads, int32_t stores, const void *src, void *dst, int64_t waves,
-                      hipStream_t stream) {
+int taco_probe_stream(int32_t loads, int32_t stores, int32_t valu, const void *src, void *dst,
+                      int64_t waves, hipStream_t stream) {
     if (waves < 1 || (waves + kWavesPerGroup - 1) / kWavesPerGroup > kMaxGroups)
         return TACO_PROBE_ERR_ARGS;
+    if (valu < 0 || valu > 65536 || (valu & 3)) return TACO_PROBE_ERR_ARGS;
     if (!src || !dst || !aligned16(src) || !aligned16(dst)) return TACO_PROBE_ERR_ARGS;
     const uintptr_t s0 = reinterpret_cast<uintptr_t>(src), d0 = reinterpret_cast<uintptr_t>(dst);
     const uintptr_t ns = (uintptr_t)waves * (uintptr_t)(loads > 0 ? loads : 0) * 1024u;
     const uintptr_t nd = (uintptr_t)waves * (uintptr_t)(stores > 0 ? stores : 0) * 1024u;
     if (s0 < d0 + nd && d0 < s0 + ns) return TACO_PROBE_ERR_ARGS;
-    if (loads == 2 && stores == 1) return launch_stream<2, 1>(src, dst, waves, stream);
-    if (loads == 1 && stores == 2) return launch_stream<1, 2>(src, dst, waves, stream);
-    if (loads == 5 && stores == 4) return launch_stream<5, 4>(src, dst, waves, stream);
-    if (loads == 1 && stores == 1) return launch_stream<1, 1>(src, dst, waves, stream);
+    if (loads == 2 && stores == 1) return launch_stream<2, 1>(src, dst, waves, valu, stream);
+    if (loads == 1 && stores == 2) return launch_stream<1, 2>(src, dst, waves, valu, stream);
+    if (loads == 5 && stores == 4) return launch_stream<5, 4>(src, dst, waves, valu, stream);
+    if (loads == 1 && stores == 1) return launch_stream<1, 1>(src, dst, waves, valu, stream);
     return TACO_PROBE_ERR_ARGS;
 }
 

@@ -17,8 +17,9 @@ if not os.path.exists(LIB_PATH):
 _lib = ctypes.CDLL(LIB_PATH)
 _lib.taco_probe_empty.argtypes = [ctypes.c_int64, ctypes.c_void_p]
 _lib.taco_probe_empty.restype = ctypes.c_int
-_lib.taco_probe_stream.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
-                                   ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
+_lib.taco_probe_stream.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                   ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                                   ctypes.c_void_p]
 _lib.taco_probe_stream.restype = ctypes.c_int
 
 #: Symbols the library exports (checked against include/taco_probe.h).
@@ -32,9 +33,9 @@ def taco_probe_empty(groups: int, stream: int) -> int:
     return _lib.taco_probe_empty(groups, stream)
 
 
-def taco_probe_stream(loads: int, stores: int, src: int, dst: int, waves: int,
+def taco_probe_stream(loads: int, stores: int, valu: int, src: int, dst: int, waves: int,
                       stream: int) -> int:
-    return _lib.taco_probe_stream(loads, stores, src, dst, waves, stream)
+    return _lib.taco_probe_stream(loads, stores, valu, src, dst, waves, stream)
 
 
 def _stream():
@@ -48,13 +49,15 @@ def empty(groups: int) -> None:
         raise RuntimeError(f"taco_probe_empty failed ({st})")
 
 
-def stream(mix: str, src, dst, waves: int) -> None:
-    """One plain stream of a byte mix over `waves` wavefronts: src and dst are
-    device tensors of at least waves * loads and waves * stores KiB."""
+def stream(mix: str, src, dst, waves: int, valu: int = 0) -> None:
+    """One plain stream of a byte mix over `waves` wavefronts (with `valu`
+    dependent VALU instructions per wavefront between loads and stores): src
+    and dst are device tensors of at least waves * loads and waves * stores
+    KiB."""
     ld, sto = MIXES[mix]
     if src.numel() * src.element_size() < waves * ld * 1024 or \
             dst.numel() * dst.element_size() < waves * sto * 1024:
         raise ValueError("buffers too small for the stream")
-    st = taco_probe_stream(ld, sto, src.data_ptr(), dst.data_ptr(), waves, _stream())
+    st = taco_probe_stream(ld, sto, valu, src.data_ptr(), dst.data_ptr(), waves, _stream())
     if st != 0:
         raise RuntimeError(f"taco_probe_stream failed ({st})")

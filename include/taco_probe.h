@@ -38,7 +38,10 @@ int taco_probe_empty(int64_t groups, hipStream_t stream);
  * reads `loads` KiB from src starting at byte w * loads * 1024 and writes
  * `stores` KiB to dst starting at byte w * stores * 1024, 1 KiB per
  * instruction (16 bytes per lane, non-temporal, like the operator's bulk
- * traffic).  Supported (loads, stores): (2, 1), the compress mix at B = 128
+ * traffic).  Between its loads and its stores each wavefront issues `valu`
+ * dependent float32 vector instructions (0 <= valu <= 65536, a multiple of
+ * 4), standing in for the arithmetic of a kernel with that many VALU
+ * instructions per wavefront.  Supported (loads, stores): (2, 1), the compress mix at B = 128
  * (2 bytes of bf16 in, 1 byte of code out per element); (1, 2), the
  * decompress mix; (5, 4), the accumulate mix (1 + 4 bytes in, 4 out per
  * element); (1, 1), a copy.  src holds waves * loads KiB and dst
@@ -46,8 +49,8 @@ int taco_probe_empty(int64_t groups, hipStream_t stream);
  * written are a function of the bytes read (their XOR), so nothing is
  * optimised away.
  */
-int taco_probe_stream(int32_t loads, int32_t stores, const void *src, void *dst, int64_t waves,
-                      hipStream_t stream);
+int taco_probe_stream(int32_t loads, int32_t stores, int32_t valu, const void *src, void *dst,
+                      int64_t waves, hipStream_t stream);
 
 #ifdef __cplusplus
 }

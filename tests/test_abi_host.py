@@ -409,16 +409,19 @@ def test_probe_library_exports_and_validation():
     assert set(probe.EXPORTS) == set(names)
     L = ctypes.CDLL(PROBE_LIB)
     L.taco_probe_empty.argtypes = [ctypes.c_int64, ctypes.c_void_p]
-    L.taco_probe_stream.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
-                                    ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
+    L.taco_probe_stream.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                    ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                                    ctypes.c_void_p]
     ARGS, LAUNCH = 1, 2
     assert L.taco_probe_empty(0, None) == ARGS
     assert L.taco_probe_empty(1 << 24, None) == ARGS          # 2^32 threads: too many
     assert L.taco_probe_empty(5120, None) == LAUNCH
-    st = lambda ld=2, sto=1, src=A, dst=64 * A, waves=1024: L.taco_probe_stream(
-        ld, sto, src, dst, waves, None)
+    st = lambda ld=2, sto=1, src=A, dst=64 * A, waves=1024, valu=0: L.taco_probe_stream(
+        ld, sto, valu, src, dst, waves, None)
     assert st(ld=3) == ARGS and st(ld=2, sto=2) == ARGS        # unsupported mixes
     assert st(waves=0) == ARGS
+    assert st(valu=-4) == ARGS and st(valu=6) == ARGS and st(valu=1 << 20) == ARGS
+    assert st(valu=276) == LAUNCH
     assert st(src=None) == ARGS and st(dst=A + 8) == ARGS     # null, misaligned
     assert st(dst=A + 1024) == ARGS                            # overlap
     assert st(dst=A + 2 * 1024 * 1024) == LAUNCH               # just past src

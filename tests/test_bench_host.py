@@ -134,3 +134,12 @@ def test_launch_groups_follow_the_kernels_launch_shape():
     assert bench.launch_groups(512 * 4 * 4 * 10, 512) == 10
     assert bench.launch_groups(32 * 16 * 16383, 32) == -(-16383 // 4)
     assert bench.launch_groups(32 * 16 * 16384, 32) == 16384 // 2 // 4
+
+
+def test_kernel_hash_covers_exactly_libtaco_sources():
+    import importlib.util
+    spec = importlib.util.spec_from_file_location(
+        "_b", os.path.join(ROOT, "gradients_taco_compress_amd", "build.py"))
+    b = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(b)
+    assert sorted(os.path.basename(f) for f in b.ALL_FILES) == sorted(bench.LIBTACO_SOURCES)
