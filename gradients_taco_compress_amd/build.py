@@ -1,6 +1,10 @@
 """Build libtaco.so in-tree with hipcc for gfx950.
 
     python gradients_taco_compress_amd/build.py
+    TACO_HIPCC_FLAGS="-DTACO_WAVES_PER_GROUP=8" python gradients_taco_compress_amd/build.py
+
+(TACO_HIPCC_FLAGS: extra hipcc flags, e.g. the kernels' compile-time tuning
+knobs, for timing a variant with bench.py; unset for the default build)
 
 (run as a script: importing it through the package would load the package,
 which needs the library this builds)
@@ -53,16 +57,22 @@ def _run(cmd, verbose: bool) -> None:
         print("\n".join(msgs))
 
 
+def extra_flags() -> list:
+    """Extra hipcc flags from TACO_HIPCC_FLAGS (whitespace-separated)."""
+    return os.environ.get("TACO_HIPCC_FLAGS", "").split()
+
+
 def build(verbose: bool = False) -> str:
     """Compile every source (in parallel), link LIB and PROBE_LIB; always
     recompiles.  Returns LIB."""
     from concurrent.futures import ThreadPoolExecutor
     tag = f".tmp{os.getpid()}"
+    flags = FLAGS + extra_flags()
     sources = SOURCES + [PROBE_SOURCE]
     objs = [os.path.join(CSRC, os.path.basename(src) + tag + ".o") for src in sources]
     try:
         with ThreadPoolExecutor(max_workers=len(sources)) as pool:
-            jobs = [pool.submit(_run, [HIPCC, *FLAGS, "-I", os.path.join(ROOT, "include"),
+            jobs = [pool.submit(_run, [HIPCC, *flags, "-I", os.path.join(ROOT, "include"),
                                        "-c", src, "-o", obj], verbose)
                     for src, obj in zip(sources, objs)]
             for j in jobs:

@@ -25,3 +25,12 @@ def test_build_script_runs_as_a_script_without_the_package():
     assert "import gradients_taco_compress_amd" not in src
     assert "from gradients_taco_compress_amd" not in src
     assert "from ." not in src
+
+
+def test_extra_hipcc_flags_come_from_the_environment(monkeypatch):
+    import __graft_entry__ as g
+    m = g._load_hip_build()
+    monkeypatch.delenv("TACO_HIPCC_FLAGS", raising=False)
+    assert m.extra_flags() == []
+    monkeypatch.setenv("TACO_HIPCC_FLAGS", " -DTACO_WAVES_PER_GROUP=8  -DTACO_MAX_GROUPS=2048 ")
+    assert m.extra_flags() == ["-DTACO_WAVES_PER_GROUP=8", "-DTACO_MAX_GROUPS=2048"]
