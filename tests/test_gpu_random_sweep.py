@@ -5,6 +5,8 @@ and the fidelity round trip's variants, each compared with the oracle
 through the same helpers as the other parity tests."""
 from __future__ import annotations
 
+import os
+
 import numpy as np
 import pytest
 
@@ -16,7 +18,10 @@ from test_gpu_fidelity import check_variant
 
 pytestmark = pytest.mark.gpu
 
-CASES = 300
+# 300 fixed-seed cases by default; TACO_SWEEP_CASES / TACO_SWEEP_SEED run a
+# longer sweep or another seed.
+CASES = int(os.environ.get("TACO_SWEEP_CASES", "300"))
+SEED = int(os.environ.get("TACO_SWEEP_SEED", "20261202"))
 
 
 def test_random_sweep():
@@ -31,7 +36,7 @@ def test_random_sweep():
         return t.reshape(shape) if shape is not None else t
 
     names = sorted(synth.WORKLOADS)
-    rng = np.random.default_rng(20261202)
+    rng = np.random.default_rng(SEED)
     flips = {"e4m3": [0, 0], "e5m2": [0, 0], "int8": [0, 0]}
     owners = 0
     for case in range(CASES):
