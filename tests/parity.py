@@ -345,7 +345,9 @@ def compare_accumulate(got_acc, acc0, payloads, B, fmt="e4m3", out=None):
         diff = np.abs(got[sl].astype(np.float64) - ref)
         worst = float(np.max(diff - tol)) if diff.size else 0.0
         e = got[sl].astype(np.float64) - ref
-        return worst, float(np.dot(e, e)), float(np.dot(ref.astype(np.float64), ref))
+        blk = np.repeat(np.max(run.reshape(-1, B), axis=1), B)
+        ratio = float(np.max(diff / np.maximum(blk, 2.0 ** -149))) if diff.size else 0.0
+        return worst, float(np.dot(e, e)), float(np.dot(ref.astype(np.float64), ref)), ratio
 
     res = run_blocks(part, m)
     worst = max(r[0] for r in res)
@@ -353,7 +355,7 @@ def compare_accumulate(got_acc, acc0, payloads, B, fmt="e4m3", out=None):
     r = math.sqrt(num / den) if den > 0 else math.sqrt(num)
     assert worst <= 0, f"accumulator element error exceeds its float32 bound by {worst:.3g}"
     assert r <= 1e-6, f"accumulate rel RMS {r:.3g}"
-    return {"rel_rms": r}
+    return {"rel_rms": r, "max_err_over_block_magnitude": max(q[3] for q in res)}
 
 
 #: Round-trip variants that rotate the block (their codes live in the
@@ -493,6 +495,31 @@ def rotated_sum_error(own_bits, payloads, B, fmt="e4m3"):
     return 2.0 ** -23 * (np.log2(B) * np.repeat(own_l1, B) + (P + 2) * pay)
 
 
+def oracle_reduce_compress(own_bits, payloads, B, tau=1.0, fmt="e4m3"):
+    """oracle.reduce_compress of flattened tensors, runs of blocks on host
+    threads.  own_bits: bf16 bit patterns or None; payloads: list of
+    (codes, alpha, scale)."""
+    pays = [(np.ascontiguousarray(c).reshape(-1), np.asarray(a, np.float32).reshape(-1),
+             np.asarray(sc, np.float32).reshape(-1)) for c, a, sc in payloads]
+    own = None if own_bits is None else np.ascontiguousarray(own_bits).reshape(-1)
+    n = own.size if own is not None else pays[0][0].size
+    m = n // B
+    codes = np.empty(n, np.uint8)
+    alpha = np.empty(m, np.float32)
+    scale = np.empty(m, np.float32)
+
+    def part(lo, hi):
+        sl = slice(lo * B, hi * B)
+        c, a, sc = oracle.reduce_compress(None if own is None else own[sl],
+                                          [(pc[sl], pa[lo:hi], ps[lo:hi]) for pc, pa, ps in pays],
+                                          B, tau, fmt=fmt)
+        codes[sl] = c.reshape(-1)
+        alpha[lo:hi] = a
+        scale[lo:hi] = sc
+    run_blocks(part, m)
+    return codes, alpha, scale
+
+
 def compare_reduce(own_bits, payloads, B, codes, alpha, scale, tau=1.0, fmt="e4m3",
                    cancelling=False):
     """Check the GPU owner step (codes, alpha, scale of own + sum of payload
@@ -503,7 +530,9 @@ def compare_reduce(own_bits, payloads, B, codes, alpha, scale, tau=1.0, fmt="e4m
     plus the oracle's own double rounding) around the exact value.  At a
     tie that is the adjacent code; near zero, where a format's codes are
     finer than that error (E5M2's reach far below it), it may be a few codes
-    away.  The number of such codes is capped at OWNER_FLIP_RATE.
+    away.  The number of such codes is capped at OWNER_FLIP_RATE.  The
+    exact sum and its bound are formed only for the blocks that hold a
+    differing code, so whole tensors of any size can be compared.
 
     cancelling: the sum cancels to a small fraction of its terms (own = x
     plus a payload compressed from -x leaves only the quantisation error).
@@ -514,48 +543,53 @@ def compare_reduce(own_bits, payloads, B, codes, alpha, scale, tau=1.0, fmt="e4m
     same bound implies for the block's energy (Parseval) and maximum."""
     codes = np.ascontiguousarray(codes).reshape(-1)
     qmax = QMAX_OF[fmt]
-    o_codes, o_alpha, o_scale = oracle.reduce_compress(own_bits, payloads, B, tau, fmt=fmt)
-    o_codes = o_codes.reshape(-1)
+    o_codes, o_alpha, o_scale = oracle_reduce_compress(own_bits, payloads, B, tau, fmt)
     n = o_codes.size
-    x = np.zeros(n)
-    if own_bits is not None:
-        x += synth.bits_to_f32(np.asarray(own_bits).reshape(-1)).astype(np.float64)
-    for c, a, s in payloads:
-        x += oracle.reconstruct_f64(c, a, s, B, fmt=fmt).reshape(-1)
+    M = n // B
     bad = np.nonzero(codes != o_codes)[0]
     if not cancelling:
         tally("owner", fmt, bad.size, n)
-    # The codes are decided on a float32 sum of `terms` rotated vectors, each
-    # adding its own rounding: the flip rate of the operator (one rotation
-    # of exact bf16 inputs) applies per term.
-    terms = len(payloads) + (own_bits is not None)
-    allowed = allowed_flips(n, OWNER_FLIP_RATE)
-    if not cancelling:
+        allowed = allowed_flips(n, OWNER_FLIP_RATE)
         assert bad.size <= allowed, \
             f"{bad.size} code mismatches in {n} elements (allowed {allowed:.1f})"
-    err = rotated_sum_error(own_bits, payloads, B, fmt) if (bad.size or cancelling) else None
-    if err is not None:
+    # The blocks to examine: those with a differing code (every block when
+    # the scalars are held to the bound as well).
+    sel = np.arange(M) if cancelling else np.unique(bad // B)
+    terms = len(payloads) + (own_bits is not None)
+    x = e = None
+    if sel.size:
+        own_sel = None
+        x = np.zeros((sel.size, B))
+        if own_bits is not None:
+            own_sel = np.ascontiguousarray(np.asarray(own_bits).reshape(M, B)[sel])
+            x += synth.bits_to_f32(own_sel).astype(np.float64)
+        pays_sel = []
+        for c, a, sc in payloads:
+            ps = (np.ascontiguousarray(np.asarray(c).reshape(M, B)[sel]),
+                  np.asarray(a, np.float32).reshape(-1)[sel], np.asarray(sc, np.float32).reshape(-1)[sel])
+            pays_sel.append(ps)
+            x += oracle.reconstruct_f64(*ps, B, fmt=fmt).reshape(sel.size, B)
+        e = rotated_sum_error(own_sel, pays_sel, B, fmt).reshape(sel.size, B)
         # The oracle's own rounding: it reconstructs every payload in double
         # and rotates the sum again, which leaves noise of order 2^-52 times
         # the block's L1 norm (enough to give an exact zero a sign).
-        l1 = np.repeat(np.sum(np.abs(x.reshape(-1, B)), axis=1), B)
-        err = err + 2.0 ** -52 * (np.log2(B) + 2 * terms + 2) * l1
+        l1 = np.sum(np.abs(x), axis=1, keepdims=True)
+        e = e + 2.0 ** -52 * (np.log2(B) + 2 * terms + 2) * l1
+    pos = {int(k): q for q, k in enumerate(sel)}
     for i in bad:
         k, j = divmod(int(i), B)
-        xb = x[k * B:(k + 1) * B]
-        r = oracle.fwht(xb)
+        q = pos[k]
+        r = oracle.fwht(x[q])
         m = np.max(np.abs(r))
         v = qmax * r[j] / m
         cg, co = int(codes[i]), int(o_codes[i])
-        bound = qmax * err[i] / m + 4 * U32 * abs(v)
+        bound = qmax * e[q, j] / m + 4 * U32 * abs(v)
         assert reachable(cg, v, bound, fmt), \
             f"element {i}: code {cg:#x} (oracle {co:#x}) is no code of a value within {bound:.3g} of {v!r}"
     ea = max_rel(alpha, o_alpha)
     es = max_rel(scale, o_scale)
     if cancelling:
-        M = n // B
-        R = np.stack([oracle.fwht(x[k * B:(k + 1) * B]) for k in range(M)])
-        e = err.reshape(M, B)
+        R = np.stack([oracle.fwht(x[q]) for q in range(M)])
         m = np.max(np.abs(R), axis=1)
         # alpha = tau / sqrt(sum R^2 / B^2 + eps): half the relative error of
         # the energy, which carries the rotated sum's error plus the float32
@@ -574,3 +608,49 @@ def compare_reduce(own_bits, payloads, B, codes, alpha, scale, tau=1.0, fmt="e4m
         assert ea <= SCALAR_RTOL, f"alpha max rel err {ea:.3g}"
         assert es <= SCALAR_RTOL, f"scale max rel err {es:.3g}"
     return {"flips": int(bad.size), "n": int(n), "alpha_rel": ea, "scale_rel": es}
+
+
+def compare_accumulate_n(got_acc, acc0, payloads, B, fmt="e4m3"):
+    """GPU float32 accumulator after one multi-payload accumulate
+    (acc0 += sum_p G'_p in one pass) against the oracle's
+    (decompress_accumulate_n: the sum in double, rounded once), element by
+    element and by relative RMS (<= 1e-6).  The kernel sums the payloads in
+    the rotated domain, S = sum_p c_p d_p with c_p = sqrt(B) s_p / alpha_p
+    (each product nearly exact, each of the P additions one rounding), then
+    applies one inverse FWHT and the exact 1/B; so per element
+        |err| <= 2^-24 ((P + 2 + log2 B) sum_p |s_p / alpha_p| |d_p|_1 / sqrt(B))
+                 + 2^-23 (|acc0| + sum_p |G'_p|),
+    which is held with a factor of 2.  Runs of blocks on host threads."""
+    got = np.ascontiguousarray(got_acc).reshape(-1)
+    a0 = np.ascontiguousarray(acc0, dtype=np.float32).reshape(-1)
+    pays = [(np.ascontiguousarray(c).reshape(-1), np.asarray(a, np.float32).reshape(-1),
+             np.asarray(sc, np.float32).reshape(-1)) for c, a, sc in payloads]
+    P = len(pays)
+    log_b = math.log2(B)
+
+    def part(lo, hi):
+        sl = slice(lo * B, hi * B)
+        sub = [(c[sl], a[lo:hi], sc[lo:hi]) for c, a, sc in pays]
+        ref = oracle.decompress_accumulate_n(sub, B, a0[sl].copy(), fmt)
+        mag = np.abs(a0[sl]).astype(np.float64)
+        t_blk = np.zeros(hi - lo)
+        for c, a, sc in sub:
+            mag += np.abs(oracle.reconstruct_f64(c, a, sc, B, fmt=fmt))
+            with np.errstate(divide="ignore", invalid="ignore"):
+                f = np.where(a != 0, sc.astype(np.float64) / a, 0.0)
+            t_blk += np.abs(f) * np.sum(np.abs(oracle.decode(c, fmt)).reshape(-1, B), axis=1)
+        tol = 2 * (2.0 ** -24 * (P + 2 + log_b) * np.repeat(t_blk, B) / math.sqrt(B)
+                   + 2.0 ** -23 * mag) + 4 * P * 2.0 ** -149
+        d = got[sl].astype(np.float64) - ref
+        blk = np.repeat(np.max(mag.reshape(-1, B), axis=1), B)
+        ratio = np.abs(d) / np.maximum(blk, 2.0 ** -149)
+        return (float(np.max(np.abs(d) - tol)), float(np.dot(d, d)),
+                float(np.dot(ref.astype(np.float64), ref)), float(np.max(ratio)))
+
+    res = run_blocks(part, got.size // B)
+    worst = max(r[0] for r in res)
+    num, den = sum(r[1] for r in res), sum(r[2] for r in res)
+    r = math.sqrt(num / den) if den > 0 else math.sqrt(num)
+    assert worst <= 0, f"multi-payload accumulator beyond its float32 bound by {worst:.3g}"
+    assert r <= 1e-6, f"multi-payload accumulate rel RMS {r:.3g}"
+    return {"rel_rms": r, "max_err_over_block_magnitude": max(q[3] for q in res)}

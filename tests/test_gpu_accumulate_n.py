@@ -11,7 +11,7 @@ import pytest
 
 import oracle
 import synth
-from parity import rel_rms
+from parity import compare_accumulate_n, rel_rms
 
 pytestmark = pytest.mark.gpu
 
@@ -62,12 +62,12 @@ def check(taco, xs, B, acc0, fmt="e4m3"):
     assert r <= 1e-6, f"vs oracle rel RMS {r:.3g}"
     r2 = rel_rms(got, seq.cpu().numpy().reshape(-1))
     assert r2 <= 1e-6, f"vs sequential accumulates rel RMS {r2:.3g}"
-    # Element-wise: float32 rounding relative to the sum of magnitudes.
-    mag = np.abs(acc0.reshape(-1)).astype(np.float64)
-    for c, a, s in h:
-        mag += np.abs(oracle.reconstruct_f64(c, a, s, B, fmt=fmt)).reshape(-1)
-    blk = np.repeat(np.max(mag.reshape(-1, B), axis=1), B)
-    assert np.all(np.abs(got - want) <= 2.0 ** -20 * blk + 1e-37)
+    # Element-wise: within the (worst-case) float32 bound of the
+    # rotated-domain sum, and within 2^-20 of the block's magnitude (a
+    # tighter bound that holds in practice: the rounding errors do not line
+    # up with one Walsh row).
+    st = compare_accumulate_n(got, acc0, h, B, fmt)
+    assert st["max_err_over_block_magnitude"] <= 2.0 ** -20, st
     return r, r2
 
 
@@ -136,15 +136,12 @@ def test_special_blocks(taco):
 
 
 def test_workload_scale_four_payloads(taco):
-    """The 32768x12288 workload: four payloads into one accumulator, sampled
-    blocks against the oracle."""
+    """The 32768x12288 workload: four payloads into one accumulator in one
+    pass, every element against the oracle (within the float32 bound of the
+    rotated-domain sum) and the relative RMS."""
     import torch
     name, B = "gpt175b_hidden_32768x12288", 256
     r = synth.WORKLOADS[name]
-    M = r.numel // B
-    rng = np.random.default_rng(9)
-    idx = np.unique(np.concatenate([np.arange(64), np.arange(M - 64, M), rng.integers(0, M, 2048)]))
-    tidx = torch.from_numpy(idx).cuda()
     g, h = [], []
     for seed in synth.ACCUMULATE_SEEDS:
         announce(f"accumulate_n workload payload seed={seed}")
@@ -152,11 +149,11 @@ def test_workload_scale_four_payloads(taco):
         c, a, s = taco.compress(x, block=B)
         del x
         g.append((c, a, s))
-        h.append((c.view(M, B)[tidx].cpu().numpy().reshape(-1), a[tidx].cpu().numpy(),
-                  s[tidx].cpu().numpy()))
+        h.append((c.cpu().numpy().reshape(-1), a.cpu().numpy(), s.cpu().numpy()))
     acc = torch.zeros((r.rows, r.cols), dtype=torch.float32, device="cuda")
     taco.decompress_accumulate_n(g, acc, block=B)
     torch.cuda.synchronize()
-    got = acc.view(M, B)[tidx].cpu().numpy().reshape(-1)
-    want = oracle.decompress_accumulate_n(h, B, np.zeros(idx.size * B, np.float32))
-    assert rel_rms(got, want) <= 1e-6
+    announce("accumulate_n workload vs the oracle (full)")
+    st = compare_accumulate_n(acc.cpu().numpy(), np.zeros(r.numel, np.float32), h, B)
+    print(st, flush=True)
+    assert st["max_err_over_block_magnitude"] <= 2.0 ** -20, st

@@ -152,3 +152,34 @@ def test_roundtrip_bound_other_variants(oracle_mod, synth_mod, variant):
         xo = oracle_mod.roundtrip_variant(x, 256, variant, fmt).reshape(-1)
         st = parity.compare_roundtrip(oracle_mod.double_to_bf16(xo), x, 256, variant, fmt, xo=xo)
         assert st["flip_blocks"] == 0
+
+
+def test_owner_step_helpers(oracle_mod, synth_mod):
+    """The threaded oracle owner step equals one call; the oracle's own result
+    passes compare_reduce; a code moved away from a tie fails it."""
+    r = synth_mod.WORKLOADS["gpt2.7b_rowpar_8192x2560"].with_shape(200, seed=8)
+    own = synth_mod.generate(r)
+    pays = [oracle_mod.compress(synth_mod.generate(r, seed=80 + p), 128) for p in range(2)]
+    c1, a1, s1 = oracle_mod.reduce_compress(own, pays, 128)
+    c2, a2, s2 = parity.oracle_reduce_compress(own, pays, 128)
+    assert np.array_equal(c1.reshape(-1), c2) and np.array_equal(a1, a2) and np.array_equal(s1, s2)
+    assert parity.compare_reduce(own, pays, 128, c2, a2, s2)["flips"] == 0
+    bad = c2.copy()
+    bad[5000] ^= 0x02                          # two codes away: no tie explains it
+    with pytest.raises(AssertionError):
+        parity.compare_reduce(own, pays, 128, bad, a2, s2)
+    assert parity.compare_reduce(None, pays, 128, *parity.oracle_reduce_compress(None, pays, 128))[
+        "flips"] == 0
+
+
+def test_accumulate_n_bound(oracle_mod, synth_mod):
+    r = synth_mod.WORKLOADS["gpt175b_hidden_32768x12288"].with_shape(4, 3072)
+    pays = [oracle_mod.compress(synth_mod.generate(r, seed=50 + p), 256) for p in range(4)]
+    acc0 = (np.random.default_rng(6).standard_normal(4 * 3072) * 0.01).astype(np.float32)
+    ref = oracle_mod.decompress_accumulate_n(pays, 256, acc0.copy())
+    st = parity.compare_accumulate_n(ref, acc0, pays, 256)
+    assert st["max_err_over_block_magnitude"] == 0.0
+    far = ref.copy()
+    far[333] += np.float32(1e-3 * np.max(np.abs(ref[256:512])))
+    with pytest.raises(AssertionError):
+        parity.compare_accumulate_n(far, acc0, pays, 256)
