@@ -393,10 +393,12 @@ def fidelity_case(torch, taco, synth, name: str, block: int, steps: int, warmup,
 
 
 def accumulate_case(torch, taco, synth, name: str, block: int, steps: int, warmup,
-                    use_graph: bool, fused: bool = False):
+                    use_graph: bool, fused: bool = False, also_fused: bool = False):
     """Four payloads compressed and summed into one float32 accumulator: one
     taco_decompress_accumulate per payload, or (fused) one
-    taco_decompress_accumulate_n over all four."""
+    taco_decompress_accumulate_n over all four.  also_fused: after the timed
+    steps, time the fused form too on the same resident payloads (reported
+    beside the line, never in its value)."""
     import numpy as np
     r = synth.WORKLOADS[name]
     n = r.numel
@@ -448,11 +450,32 @@ def accumulate_case(torch, taco, synth, name: str, block: int, steps: int, warmu
     acc_fn()
     t_a = timer.time(acc_fn, reps) / ((1 if fused else nb) * reps)
     kname = "accumulate_n" if fused else "accumulate"
-    return {"n": n, "block": block, "steps": reps, "warmup": warm, "t_step": t_steps / reps,
-            "repeats": repeats, "t_compress": t_c, "t_accumulate": t_a, "sets": 1, "rows": r.rows, "cols": r.cols,
-            "fused": fused, "nb": nb,
-            "bytes_step": nb * algorithmic_bytes("compress", n, block) + acc_bytes,
-            "input_bytes_step": nb * 2.0 * n, "kernels": {"compress": t_c, kname: t_a}}
+    out = {"n": n, "block": block, "steps": reps, "warmup": warm, "t_step": t_steps / reps,
+           "repeats": repeats, "t_compress": t_c, "t_accumulate": t_a, "sets": 1, "rows": r.rows, "cols": r.cols,
+           "fused": fused, "nb": nb,
+           "bytes_step": nb * algorithmic_bytes("compress", n, block) + acc_bytes,
+           "input_bytes_step": nb * 2.0 * n, "kernels": {"compress": t_c, kname: t_a}}
+    if also_fused and not fused:
+        def run_fused():
+            run_compress()
+            taco.decompress_accumulate_n([(c, a, s) for _, c, a, s in payloads], acc, block=block)
+        fused_fn = make_graph(torch, run_fused, use_graph, prerun=False)
+        accn_fn = make_graph(torch, lambda: taco.decompress_accumulate_n(
+            [(c, a, s) for _, c, a, s in payloads], acc, block=block), use_graph, prerun=False)
+        fbytes = nb * algorithmic_bytes("compress", n, block) + \
+            algorithmic_bytes(f"accumulate_n:{nb}", n, block)
+        for _ in range(warmup_steps(None, 1, fbytes)):
+            fused_fn()
+        t_f = timer.time(fused_fn, reps) / reps
+        accn_fn()
+        t_n = timer.time(accn_fn, reps) / reps
+        out["fused_receive"] = {
+            "step": f"{nb}x compress + 1x decompress_accumulate_n of {nb} payloads",
+            "steps": reps, "ms_per_step": round(t_f * 1e3, 5),
+            "input_GBps": round(nb * 2.0 * n / t_f / 1e9, 2),
+            "pct_hbm_peak": round(100.0 * fbytes / t_f / 1e9 / HBM_PEAK_GBS, 2),
+            "kernel_us": {"compress": round(t_c * 1e6, 3), "accumulate_n": round(t_n * 1e6, 3)}}
+    return out
 
 
 def owner_case(torch, taco, synth, name: str, block: int, steps: int, warmup,
@@ -790,7 +813,8 @@ DEFAULT_STEPS_ACCUMULATE = 100
 DEFAULT_STEPS_ROUNDTRIP = 400
 
 
-def run_case(torch, taco, synth, name: str, block: int, steps, warmup, use_graph: bool):
+def run_case(torch, taco, synth, name: str, block: int, steps, warmup, use_graph: bool,
+             also_fused: bool = False):
     """Times one workload (NAME or NAME:variant).  Returns (res, base name,
     accumulate workload?)."""
     base = name.split(":")[0]
@@ -814,7 +838,8 @@ def run_case(torch, taco, synth, name: str, block: int, steps, warmup, use_graph
     elif kind:
         raise SystemExit(f"unknown workload variant {name!r}")
     elif acc:
-        res = accumulate_case(torch, taco, synth, base, block, steps, warmup, use_graph)
+        res = accumulate_case(torch, taco, synth, base, block, steps, warmup, use_graph,
+                              also_fused=also_fused)
     else:
         res = roundtrip_case(torch, taco, synth, base, block, steps, warmup, use_graph)
     torch.cuda.empty_cache()
@@ -918,12 +943,14 @@ def main():
     for i, (name, block) in enumerate(cases):
         print(f"[bench] {name} block {block}", file=sys.stderr, flush=True)
         res, base, acc = run_case(torch, taco, synth, name, block, args.steps, args.warmup,
-                                  use_graph)
+                                  use_graph, also_fused=default_line and not args.no_configs)
         cpu = None
         if not args.no_cpu_baseline and i == 0:
             print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
             cpu = cpu_baseline(synth, base, block, args.cpu_seconds, acc)
         rec = record(res, base, args, cpu)
+        if "fused_receive" in res:
+            rec["fused_receive"] = res["fused_receive"]
         if not args.no_floors and rec["roofline"]["kernel"] == "compress" and \
                 not res.get("packed") and (i == 0 or (base, block) in ROUNDTRIP_CONFIGS):
             print("[bench] same-mix stream reference (torch add)", file=sys.stderr, flush=True)

@@ -385,8 +385,9 @@ typedef struct {
  * The working memory does not grow with the tensor: every accepted shape
  * fits it, so no size is refused for lack of it.  The first call on a
  * device looks up that device's copy of the array (the current device,
- * which must be the device of `stream`; a failed lookup is TACO_ERR_HIP and
- * launches nothing); no call allocates or frees memory.  Every call on one
+ * which must be the device of `stream`, one of the first 64 devices; a
+ * failed lookup is TACO_ERR_HIP and launches nothing): make that first call
+ * before capturing a graph.  No call allocates or frees memory.  Every call on one
  * GPU shares that GPU's array, and each call clears it first (with a
  * kernel, on `stream`): calls on one GPU must therefore not overlap in time
  * (calls on different streams race, and their totals are then undefined);

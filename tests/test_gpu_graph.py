@@ -112,3 +112,62 @@ def test_graph_replays_equal_eager_calls(taco, fmt):
         for k in want:
             if k != "sums":
                 assert torch.equal(other[k], want[k]), f"eager call after replay {rep}: {k}"
+
+
+def test_noalloc_round_trip_in_a_graph(taco):
+    """taco_roundtrip_noalloc captured in a graph (its working sums live in
+    the library's per-GPU array, cleared by a kernel, so the graph holds no
+    memset and no allocation): every replay equals the eager call, with eager
+    calls on another tensor, sharing the same array, in between."""
+    import struct
+    import torch
+    B, rows, cols = 256, 64, 2048
+    announce(f"noalloc round trip in a graph, {rows}x{cols}, B={B}")
+    base = synth.WORKLOADS["grad_8192x8192"]
+    x = to_gpu_bf16(synth.generate(base.with_shape(rows, cols), seed=70))
+    x2 = to_gpu_bf16(synth.generate(base.with_shape(rows // 2, cols), seed=71))
+    f, v = taco.FORMATS["int8"], taco.VARIANTS["tensor"]
+
+    def call(xt, y, t):
+        r, c = xt.shape
+        st = taco.taco_roundtrip_noalloc(xt.data_ptr(), r, c, B, 1.0, f, v, y.data_ptr(),
+                                         t.data_ptr(), torch.cuda.current_stream().cuda_stream)
+        assert st == 0, taco.taco_status_string(st)
+
+    def totals(t):
+        return struct.unpack("<4d2f", bytes(t.cpu().numpy().tobytes()))
+
+    def out_for(xt):
+        return (torch.empty_like(xt),
+                torch.empty(taco.FIDELITY_TOTALS_BYTES, dtype=torch.uint8, device="cuda"))
+
+    y_ref, t_ref = out_for(x)
+    y2_ref, t2_ref = out_for(x2)
+    call(x, y_ref, t_ref)                 # the first call (outside capture) looks up the array
+    call(x2, y2_ref, t2_ref)
+    torch.cuda.synchronize()
+    want, want2 = totals(t_ref), totals(t2_ref)
+
+    y_g, t_g = out_for(x)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call(x, y_g, t_g)
+    y2, t2 = out_for(x2)
+    for rep in range(4):
+        announce(f"noalloc replay {rep}")
+        y_g.zero_()
+        t_g.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        call(x2, y2, t2)                  # eager, same stream, same working array
+        torch.cuda.synchronize()
+        assert torch.equal(y_g.view(torch.int16), y_ref.view(torch.int16)), rep
+        got = totals(t_g)
+        for a, b in zip(got[:4], want[:4]):
+            assert a == pytest.approx(b, rel=1e-12, abs=0.0), rep
+        assert got[4:] == want[4:], rep
+        assert torch.equal(y2.view(torch.int16), y2_ref.view(torch.int16)), rep
+        got2 = totals(t2)
+        for a, b in zip(got2[:4], want2[:4]):
+            assert a == pytest.approx(b, rel=1e-12, abs=0.0), rep
+        assert got2[4:] == want2[4:], rep
