@@ -32,18 +32,20 @@ QMAX = 448.0
 QMAX_OF = {"e4m3": 448.0, "e5m2": 57344.0, "int8": 127.0}
 U32 = 2.0 ** -24          # float32 unit roundoff
 
-# Owner step: the rate of tie flips depends on the data, since its codes are
-# decided on a float32 sum of decoded FP8 payloads, few-bit values whose
-# rotated sums land exactly on rounding ties far more often than bf16 data
-# do (2.7-5.4e-5 seen for two payloads without an own partial).  Its stated
-# rate, per case (Poisson bound) and over the session: 1e-4.  Every flip is
-# verified against the float32 bound of the sum individually.
+# Owner step, per case: the rate of tie flips depends on the data, since its
+# codes are decided on a float32 sum of decoded FP8 payloads, few-bit values
+# whose rotated sums land exactly on rounding ties far more often than bf16
+# data do in some small cases (2.7-5.4e-5 seen for two payloads without an
+# own partial).  One case may show flips at a Poisson bound of 1e-4; the
+# session total is held to the contract's 1e-5 like every other kind.  Every
+# flip is verified against the float32 bound of the sum individually.
 OWNER_FLIP_RATE = 1e-4
 
 #: Rate bound of each kind of comparison over the session.  "compress": the
-#: operator's sender side (and the fidelity round trips' codes), one
-#: rotation of exact bf16 inputs; "owner": the owner step.
-RATE_OF = {"compress": FLIP_RATE, "roundtrip": FLIP_RATE, "owner": OWNER_FLIP_RATE}
+#: operator's sender side, one rotation of exact bf16 inputs; "roundtrip":
+#: the fidelity round trips (blocks explained by adjacent-code changes);
+#: "owner": the owner step.
+RATE_OF = {"compress": FLIP_RATE, "roundtrip": FLIP_RATE, "owner": FLIP_RATE}
 
 # Flips and elements over every comparison of the session, per kind and code
 # format: {(kind, fmt): [flips, elements]}.  A case may show a few

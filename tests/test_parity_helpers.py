@@ -43,7 +43,7 @@ def test_session_totals_by_kind_and_format(monkeypatch):
     monkeypatch.setattr(parity, "TOTALS", {})
     parity.tally("compress", "e4m3", 3, 1_000_000)
     parity.tally("compress", "e4m3", 2, 1_000_000)
-    parity.tally("owner", "e4m3", 150, 2_000_000)
+    parity.tally("owner", "e4m3", 15, 2_000_000)
     lines, ok = parity.session_check()
     assert ok and len(lines) == 2
     assert "[compress e4m3]: 5 in 2000000" in lines[0]
