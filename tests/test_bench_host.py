@@ -143,3 +143,16 @@ def test_kernel_hash_covers_exactly_libtaco_sources():
     b = importlib.util.module_from_spec(spec)
     spec.loader.exec_module(b)
     assert sorted(os.path.basename(f) for f in b.ALL_FILES) == sorted(bench.LIBTACO_SOURCES)
+
+
+def test_config_summary_carries_the_floors():
+    rec = bench.record(_res("roundtrip"), "gpt2.7b_rowpar_8192x2560", _Args())
+    rec["roofline"]["launch_floor"] = {"kernel": "empty", "groups": 5120, "us": 2.1}
+    rec["roofline"]["stream_floor"] = {"us": 11.2, "frac": 0.70}
+    rec["roofline"]["stream_valu_floor"] = {"us": 13.4}
+    out = bench.config_summary(rec)
+    assert out["workload"] == "gpt2.7b_rowpar_8192x2560" and out["block"] == 128
+    assert out["pct_hbm_peak"] == rec["pct_hbm_peak"] and out["input_GBps"] == rec["value"]
+    for key in ("launch_floor", "stream_floor", "stream_valu_floor"):
+        assert out[key] == rec["roofline"][key]
+    assert out["roofline"]["kernel"] == "compress"
