@@ -57,18 +57,26 @@ __global__ __launch_bounds__(kGroup) void probe_stream_kernel(const u4v *__restr
     for (int j = 0; j < ST; ++j) __builtin_nontemporal_store(acc + (unsigned)j, d + j * kWave);
 }
 
+// Launches fn on `groups` work-groups with the given arguments; the status
+// is the launch's own (not an earlier error left in the runtime).
+template <typename... Args>
+int launch(const void *fn, int64_t groups, hipStream_t stream, Args... args) {
+    void *ptrs[] = {static_cast<void *>(&args)...};
+    const hipError_t err =
+        hipLaunchKernel(fn, dim3((unsigned)groups), dim3(kGroup), ptrs, 0, stream);
+    return err == hipSuccess ? TACO_PROBE_OK : TACO_PROBE_ERR_HIP;
+}
+
 template <int LD, int ST>
 int launch_stream(const void *src, void *dst, int64_t waves, int valu, hipStream_t stream) {
     const int64_t groups = (waves + kWavesPerGroup - 1) / kWavesPerGroup;
+    const u4v *s = static_cast<const u4v *>(src);
+    u4v *d = static_cast<u4v *>(dst);
     if (valu > 0)
-        hipLaunchKernelGGL((probe_stream_kernel<LD, ST, true>), dim3((unsigned)groups),
-                           dim3(kGroup), 0, stream, static_cast<const u4v *>(src),
-                           static_cast<u4v *>(dst), waves, valu);
-    else
-        hipLaunchKernelGGL((probe_stream_kernel<LD, ST, false>), dim3((unsigned)groups),
-                           dim3(kGroup), 0, stream, static_cast<const u4v *>(src),
-                           static_cast<u4v *>(dst), waves, 0);
-    return hipGetLastError() == hipSuccess ? TACO_PROBE_OK : TACO_PROBE_ERR_HIP;
+        return launch(reinterpret_cast<const void *>(&probe_stream_kernel<LD, ST, true>), groups,
+                      stream, s, d, waves, valu);
+    return launch(reinterpret_cast<const void *>(&probe_stream_kernel<LD, ST, false>), groups,
+                  stream, s, d, waves, 0);
 }
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -82,8 +90,7 @@ extern "C" {
 
 int taco_probe_empty(int64_t groups, hipStream_t stream) {
     if (groups < 1 || groups > kMaxGroups) return TACO_PROBE_ERR_ARGS;
-    hipLaunchKernelGGL(probe_empty_kernel, dim3((unsigned)groups), dim3(kGroup), 0, stream);
-    return hipGetLastError() == hipSuccess ? TACO_PROBE_OK : TACO_PROBE_ERR_HIP;
+    return launch(reinterpret_cast<const void *>(&probe_empty_kernel), groups, stream);
 }
 
 int taco_probe_stream(int32_t loads, int32_t stores, int32_t valu, const void *src, void *dst,
