@@ -34,11 +34,13 @@ U32 = 2.0 ** -24          # float32 unit roundoff
 
 # Owner step, per case: the rate of tie flips depends on the data, since its
 # codes are decided on a float32 sum of decoded FP8 payloads, few-bit values
-# whose rotated sums land exactly on rounding ties far more often than bf16
-# data do in some small cases (2.7-5.4e-5 seen for two payloads without an
-# own partial).  One case may show flips at a Poisson bound of 1e-4; the
-# session total is held to the contract's 1e-5 like every other kind.  Every
-# flip is verified against the float32 bound of the sum individually.
+# whose rotated sums land on rounding ties far more often than bf16 data do
+# in some small cases (2.7-5.4e-5 seen for two payloads without an own
+# partial), and exactly on them in clusters (three exact ties in one block
+# of 512).  The flips at inexact ties of one case are held to a Poisson
+# bound of 1e-4; flips at exact ties are not capped per case.  The session
+# total of all flips is held to the contract's 1e-5 like every other kind,
+# and every flip is verified against the float32 bound of the sum.
 OWNER_FLIP_RATE = 1e-4
 
 #: Rate bound of each kind of comparison over the session.  "compress": the
@@ -374,17 +376,51 @@ def code_values(fmt: str) -> np.ndarray:
     return _CODE_VALUES[fmt]
 
 
-def adjacent_changes(value: float, fmt: str) -> np.ndarray:
-    """Changes that move the code value nearest `value` to a neighbouring
-    code value (0 included: no change)."""
+def tie_changes(v, bound, fmt: str):
+    """[(j, change)]: the elements j of a block whose code argument v[j]
+    (exact, as the oracle defines it) lies within bound[j] of a rounding
+    midpoint between the oracle's code value there and a neighbouring code
+    value, with the change of code value (neighbour minus the oracle's) that
+    a float32 evaluation on the other side of that midpoint gives."""
     vals = code_values(fmt)
-    i = int(np.argmin(np.abs(vals - value)))
-    out = [0.0]
-    if i > 0:
-        out.append(vals[i - 1] - vals[i])
-    if i + 1 < vals.size:
-        out.append(vals[i + 1] - vals[i])
-    return np.array(out)
+    v = np.asarray(v, np.float64)
+    o = oracle.decode(oracle.encode(v.astype(np.float32), fmt), fmt).astype(np.float64)
+    i = np.searchsorted(vals, o)
+    out = []
+    for side in (-1, 1):
+        q = i + side
+        ok = (q >= 0) & (q < vals.size)
+        nb = vals[np.clip(q, 0, vals.size - 1)]
+        hit = ok & (np.abs(v - 0.5 * (o + nb)) <= bound)
+        out += [(int(j), float(nb[j] - o[j])) for j in np.nonzero(hit)[0]]
+    return out
+
+
+def code_arguments(x_block, B, variant, fmt, tau, tensor_max):
+    """(v, bound) of one block: each element's code argument as the oracle
+    defines it (in double) and a bound on the float32 error of the kernel's
+    evaluation of it.  The rotation accumulates at most log2(B) roundings of
+    partial sums bounded by sum|x|; quotients and products add a few units
+    of v."""
+    qmax = QMAX_OF[fmt]
+    xs = synth.bits_to_f32(x_block).astype(np.float64)
+    if variant == "direct":
+        return xs, np.zeros(B)
+    if variant in ("ds", "tensor"):
+        m = np.max(np.abs(xs)) if variant == "ds" else tensor_max
+        v = xs * qmax / m if m > 0 else np.zeros(B)
+        return v, 4 * U32 * np.abs(v)
+    R = oracle.fwht(xs)
+    ferr = np.log2(B) * U32 * np.sum(np.abs(xs))
+    if variant == "taco":
+        m = np.max(np.abs(R))
+        v = qmax * R / m if m > 0 else np.zeros(B)
+        return v, (qmax * ferr / m if m > 0 else 0.0) + 4 * U32 * np.abs(v)
+    if variant == "hadamard":
+        v = R / math.sqrt(B)
+        return v, ferr / math.sqrt(B) + 4 * U32 * np.abs(v)
+    alpha, _, z = oracle.ash_block(x_block, B, tau)            # "ash"
+    return z, alpha * ferr / math.sqrt(B) + 8 * U32 * np.abs(z)
 
 
 def _code_factor(x_block, B, variant, fmt, tau, tensor_delta):
@@ -412,23 +448,29 @@ def compare_roundtrip(y_bits, x_bits, B, variant, fmt="e4m3", tau=1.0, xo=None):
     differs, an element is within one bf16 rounding of the oracle's value
     plus the float32 error of the kernel's arithmetic relative to the
     block's largest value.  The round trip does not return its codes, so a
-    tie flip shows only in its output.  A block beyond that bound must be
-    explained by at most two adjacent-code changes: in the code domain (the
-    rotated domain H x' / sqrt(B) for the rotating variants, x' itself for
-    the others), where the oracle's block is c * decode(q), each of the two
-    largest entries of the difference is matched with the change to a
-    neighbouring code of the oracle's code there (or none) that leaves the
-    smallest remainder; those changes, times c, are subtracted, and what is
-    left must be within the element bound.  The number of such blocks counts
-    as flips against the rate.  Also the relative RMS (1e-3)."""
+    tie flip shows only in its output, and one flip of a rotating variant
+    moves every element of the block by about the code step over sqrt(B):
+    below the bf16 noise of the other elements in the code domain, yet
+    enough to take an element near zero past its bound.  A block beyond the
+    bound must therefore be explained by flips at rounding ties: the
+    elements whose code argument lies within the kernel's float32 error
+    bound of a midpoint between the oracle's code and a neighbouring one
+    are found (tie_changes), and some set of them (of the six whose flip
+    alone best matches the difference), each moved to the other code of its
+    tie, must bring the whole block within the element bound.  In the code domain (H x'/sqrt(B) for
+    the rotating variants, x' itself for the others) the oracle's block is
+    c * decode(q), so a flip at j changes it by c times the code step at j.
+    The number of such blocks counts as flips against the rate.  Also the
+    relative RMS (1e-3) against the oracle's output with those explained
+    flips applied: with few, coarse codes one legitimate flip moves a small
+    tensor's RMS by more than that (ASH alone in INT8 maps a block to values
+    of RMS about 1, so one code step is a few percent of the block)."""
+    import itertools
     y = synth.bits_to_f32(np.ascontiguousarray(y_bits).reshape(-1)).astype(np.float64)
     xb_all = np.ascontiguousarray(x_bits).reshape(-1)
     if xo is None:
         xo = oracle.roundtrip_variant(xb_all, B, variant, fmt, tau).reshape(-1)
-    ref = synth.bits_to_f32(oracle.double_to_bf16(xo)).astype(np.float64)
     n = y.size
-    r = rel_rms(y, ref)
-    assert r <= RECON_RTOL, f"{variant}/{fmt}: reconstruction rel RMS {r:.3g}"
     xo2 = xo.reshape(-1, B)
     blk = np.max(np.abs(xo2), axis=1, keepdims=True)
     tol = (2.0 ** -8 * np.abs(xo2) + 2.0 ** -16 * blk + 2.0 ** -133)
@@ -438,32 +480,48 @@ def compare_roundtrip(y_bits, x_bits, B, variant, fmt="e4m3", tau=1.0, xo=None):
     assert over.size <= allowed_flips(n), \
         f"{variant}/{fmt}: {over.size} blocks beyond the element bound in {n} elements"
     rot = variant in ROTATING
-    delta = 0.0
+    tmax = delta = 0.0
+    flipped = xo2.copy()
     if variant == "tensor" and over.size:
         tmax = float(np.max(np.abs(synth.bits_to_f32(xb_all).astype(np.float64))))
         delta = float(np.float32(tmax / QMAX_OF[fmt]))
     for k in over:
-        e, t = err[k], tol[k]
-        c = _code_factor(xb_all[k * B:(k + 1) * B], B, variant, fmt, tau, delta)
+        e = err[k]
+        xblock = xb_all[k * B:(k + 1) * B]
+        c = _code_factor(xblock, B, variant, fmt, tau, delta)
         assert c != 0.0, f"{variant}/{fmt} block {k}: an all-zero block differs"
-        if rot:
-            dom = oracle.fwht(e) / math.sqrt(B)
-            ref_dom = oracle.fwht(xo2[k]) / math.sqrt(B)
-        else:
-            dom, ref_dom = e.copy(), xo2[k].copy()
-        change = np.zeros(B)
-        for j in np.argsort(-np.abs(dom))[:2]:
-            steps = adjacent_changes(ref_dom[j] / c, fmt) * c
-            change[j] = steps[int(np.argmin(np.abs(dom[j] - steps)))]
-        back = oracle.fwht(change) / math.sqrt(B) if rot else change
-        rest = e - back
-        # The kernel rounds its own value (the oracle's plus the change) to
-        # bf16: the bound follows the larger of the two magnitudes.
-        moved = np.abs(xo2[k] + back)
-        t = np.maximum(t, 2.0 ** -8 * moved + 2.0 ** -16 * np.max(moved) + 2.0 ** -133)
-        assert np.all(np.abs(rest) <= t * (1 + 1e-9)), \
-            (f"{variant}/{fmt} block {k}: error beyond the bound that no two adjacent-code "
-             f"changes explain (worst remainder {np.max(np.abs(rest) - t):.3g})")
+        v, vb = code_arguments(xblock, B, variant, fmt, tau, tmax)
+        dom = oracle.fwht(e) / math.sqrt(B) if rot else e
+        # Ties ranked by how much their flip alone lowers the difference in
+        # the code domain; the six best are tried in every combination.
+        ties = sorted(((abs(dom[j]) - abs(dom[j] - d * c), j, d * c)
+                       for j, d in tie_changes(v, vb, fmt)), reverse=True)[:6]
+        least = float(np.max(np.abs(e) - tol[k]))
+        explained = False
+        for size in range(1, len(ties) + 1):
+            for sub in itertools.combinations(ties, size):
+                change = np.zeros(B)
+                for _, j, dc in sub:
+                    change[j] += dc
+                back = oracle.fwht(change) / math.sqrt(B) if rot else change
+                # The kernel rounds its own value (the oracle's plus the
+                # change) to bf16: the bound follows the larger magnitude.
+                moved = np.abs(xo2[k] + back)
+                t = np.maximum(tol[k], 2.0 ** -8 * moved + 2.0 ** -16 * np.max(moved) + 2.0 ** -133)
+                excess = float(np.max(np.abs(e - back) - t * (1 + 1e-9)))
+                least = min(least, excess)
+                if excess <= 0:
+                    explained = True
+                    flipped[k] = xo2[k] + back
+                    break
+            if explained:
+                break
+        assert explained, (f"{variant}/{fmt} block {k}: error beyond the bound that no flips at "
+                           f"its {len(ties)} rounding ties explain (least remaining excess "
+                           f"{least:.3g})")
+    ref = synth.bits_to_f32(oracle.double_to_bf16(flipped.reshape(-1))).astype(np.float64)
+    r = rel_rms(y, ref)
+    assert r <= RECON_RTOL, f"{variant}/{fmt}: reconstruction rel RMS {r:.3g}"
     return {"rel_rms": r, "flip_blocks": int(over.size)}
 
 
@@ -532,7 +590,12 @@ def compare_reduce(own_bits, payloads, B, codes, alpha, scale, tau=1.0, fmt="e4m
     plus the oracle's own double rounding) around the exact value.  At a
     tie that is the adjacent code; near zero, where a format's codes are
     finer than that error (E5M2's reach far below it), it may be a few codes
-    away.  The number of such codes is capped at OWNER_FLIP_RATE.  The
+    away.  A sum of a few decoded payloads can sit exactly on a midpoint
+    between two codes: both are then equally near the exact sum, the
+    oracle's choice is round-half-even's and the kernel's follows the sign
+    of its float32 error, so such flips come in clusters of exact ties.  The
+    flips at inexact ties are capped at OWNER_FLIP_RATE per case; every flip
+    is counted in the session total.  The
     exact sum and its bound are formed only for the blocks that hold a
     differing code, so whole tensors of any size can be compared.
 
@@ -551,9 +614,11 @@ def compare_reduce(own_bits, payloads, B, codes, alpha, scale, tau=1.0, fmt="e4m
     bad = np.nonzero(codes != o_codes)[0]
     if not cancelling:
         tally("owner", fmt, bad.size, n)
-        allowed = allowed_flips(n, OWNER_FLIP_RATE)
-        assert bad.size <= allowed, \
-            f"{bad.size} code mismatches in {n} elements (allowed {allowed:.1f})"
+        # A coarse cap first, so that a broken result is not verified code by
+        # code over the whole tensor; the per-case cap follows the checks.
+        coarse = allowed_flips(n, 1e-3)
+        assert bad.size <= coarse, \
+            f"{bad.size} code mismatches in {n} elements (coarse cap {coarse:.1f})"
     # The blocks to examine: those with a differing code (every block when
     # the scalars are held to the bound as well).
     sel = np.arange(M) if cancelling else np.unique(bad // B)
@@ -578,6 +643,7 @@ def compare_reduce(own_bits, payloads, B, codes, alpha, scale, tau=1.0, fmt="e4m
         l1 = np.sum(np.abs(x), axis=1, keepdims=True)
         e = e + 2.0 ** -52 * (np.log2(B) + 2 * terms + 2) * l1
     pos = {int(k): q for q, k in enumerate(sel)}
+    exact = 0
     for i in bad:
         k, j = divmod(int(i), B)
         q = pos[k]
@@ -588,6 +654,13 @@ def compare_reduce(own_bits, payloads, B, codes, alpha, scale, tau=1.0, fmt="e4m
         bound = qmax * e[q, j] / m + 4 * U32 * abs(v)
         assert reachable(cg, v, bound, fmt), \
             f"element {i}: code {cg:#x} (oracle {co:#x}) is no code of a value within {bound:.3g} of {v!r}"
+        dg, do = oracle.decode(np.array([cg, co], np.uint8), fmt)
+        exact += abs(v - 0.5 * (dg + do)) <= 1e-12 * abs(v)
+    if not cancelling:
+        allowed = allowed_flips(n, OWNER_FLIP_RATE)
+        assert bad.size - exact <= allowed, \
+            (f"{bad.size} code mismatches in {n} elements, {exact} of them at exact ties "
+             f"(allowed {allowed:.1f} others)")
     ea = max_rel(alpha, o_alpha)
     es = max_rel(scale, o_scale)
     if cancelling:

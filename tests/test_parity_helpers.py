@@ -103,44 +103,86 @@ def test_accumulate_bound(oracle_mod, synth_mod):
         parity.compare_accumulate(far, acc0, pays, 256)
 
 
+# Two-spike blocks [a, b, 0, ...]: the rotation gives a + b on even rows and
+# a - b on odd rows, so Q*(a - b)/(a + b) is exactly the midpoint between two
+# code values on every odd row (E4M3: 432 between 416 and 448; E5M2: 53248
+# between 49152 and 57344; INT8: 0.5 between 0 and 1).
+TIE_SPIKES = {"e4m3": (55, 1), "e5m2": (27, 1), "int8": (255, 253)}
+
+
 @pytest.mark.parametrize("fmt", ["e4m3", "e5m2", "int8"])
 def test_roundtrip_bound_explains_a_flip(oracle_mod, synth_mod, fmt, monkeypatch):
-    """The oracle's own round trip passes with no flagged block; a round trip
-    whose codes differ from the oracle's by one adjacent code in one block
-    passes with one flagged block; three code steps, or a smooth error of
-    1e-2 over a block, fail."""
+    """The oracle's own round trip passes with no flagged block; one code
+    moved to the other side of its rounding tie passes with one flagged
+    block; the same step at a code that is not at a tie, three codes down at
+    a tie, or a smooth error of 1e-2 over a block, fail."""
     monkeypatch.setattr(parity, "TOTALS", {})
-    B = 128
-    # (large enough that one changed top code stays within the RMS tolerance)
+    B, k = 128, 5
     r = synth_mod.WORKLOADS["laplace_2048x1024"].with_shape(256, 1024, seed=6)
-    x = synth_mod.generate(r)
+    x = synth_mod.generate(r).reshape(-1).copy()
+    a, b = TIE_SPIKES[fmt]
+    blk = synth_mod.bits_to_f32(x[k * B:(k + 1) * B])
+    p = int(np.round(np.log2(np.max(np.abs(blk)) / a)))
+    spikes = np.zeros(B, np.float32)
+    spikes[:2] = np.ldexp(np.array([a, b], np.float32), p)
+    x[k * B:(k + 1) * B] = (spikes.view(np.uint32) >> 16).astype(np.uint16)   # exact in bf16
     xo = oracle_mod.roundtrip_variant(x, B, "taco", fmt).reshape(-1)
-    y = oracle_mod.double_to_bf16(xo)
-    assert parity.compare_roundtrip(y, x, B, "taco", fmt, xo=xo)["flip_blocks"] == 0
-    c, a, s = oracle_mod.compress(x, B, fmt=fmt)
-    c = c.reshape(-1).copy()
-    k = 5
-    # The block's largest code (+-Q_max): one step toward zero is visible in
-    # every element.
-    i = k * B + int(np.argmax(np.abs(oracle_mod.decode(c[k * B:(k + 1) * B], fmt))))
-    d = oracle_mod.decode(c[i:i + 1], fmt)[0]
-    assert abs(d) == parity.QMAX_OF[fmt]
+    assert parity.compare_roundtrip(oracle_mod.double_to_bf16(xo), x, B, "taco", fmt,
+                                    xo=xo)["flip_blocks"] == 0
+    c, al, s = oracle_mod.compress(x, B, fmt=fmt)
+    c = c.reshape(-1)
+    v, vb = parity.code_arguments(x[k * B:(k + 1) * B], B, "taco", fmt, 1.0, 0.0)
+    ties = dict(parity.tie_changes(v, vb, fmt))
+    assert sorted(ties) == list(range(1, B, 2))                # every odd row is at a tie
+    j = 7
+    top = 0                                                    # even row: Q exactly, no tie
 
-    def toward_zero(steps):
+    def moved(i, delta):
         cc = c.copy()
-        if fmt == "int8" and d < 0:
-            cc[i] = (int(c[i]) + steps) & 0xFF
-        else:
-            cc[i] = int(c[i]) - steps
-        return oracle_mod.double_to_bf16(oracle_mod.reconstruct_f64(cc, a, s, B, fmt=fmt))
+        d = oracle_mod.decode(cc[k * B + i:k * B + i + 1], fmt)[0]
+        cc[k * B + i] = oracle_mod.encode(np.array([d + delta], np.float32), fmt)[0]
+        assert oracle_mod.decode(cc[k * B + i:k * B + i + 1], fmt)[0] == d + delta
+        return oracle_mod.double_to_bf16(oracle_mod.reconstruct_f64(cc, al, s, B, fmt=fmt))
 
-    assert parity.compare_roundtrip(toward_zero(1), x, B, "taco", fmt, xo=xo)["flip_blocks"] == 1
-    with pytest.raises(AssertionError):
-        parity.compare_roundtrip(toward_zero(3), x, B, "taco", fmt, xo=xo)
+    vals = parity.code_values(fmt)
+    step = ties[j]
+    assert parity.compare_roundtrip(moved(j, step), x, B, "taco", fmt, xo=xo)["flip_blocks"] == 1
+    dtop = oracle_mod.decode(c[k * B:k * B + 1], fmt)[0]
+    below = vals[np.searchsorted(vals, dtop) - 1]
+    with pytest.raises(AssertionError, match="rounding ties"):
+        parity.compare_roundtrip(moved(top, below - dtop), x, B, "taco", fmt, xo=xo)
+    dj = oracle_mod.decode(c[k * B + j:k * B + j + 1], fmt)[0]
+    three = vals[np.searchsorted(vals, dj) - 3]                # three codes down
+    with pytest.raises(AssertionError, match="rounding ties"):
+        parity.compare_roundtrip(moved(j, three - dj), x, B, "taco", fmt, xo=xo)
     smooth = xo.copy()
     smooth[k * B:(k + 1) * B] *= 1 + 1e-2
     with pytest.raises(AssertionError):
         parity.compare_roundtrip(oracle_mod.double_to_bf16(smooth), x, B, "taco", fmt, xo=xo)
+
+
+def test_roundtrip_flip_below_the_code_domain_noise(oracle_mod, synth_mod):
+    """A tie flip whose change is smaller than the bf16 noise of the block in
+    the rotated domain, yet takes an element near zero past its bound
+    (block 623 of the GPT-2.7B row-parallel workload at 139 x 9728, seed
+    699807680, B = 512): the flip at element 274 alone, and with the tie at
+    element 4 flipped too, are explained."""
+    r = synth_mod.WORKLOADS["gpt2.7b_rowpar_8192x2560"].with_shape(139, 9728, seed=699807680)
+    xb = synth_mod.generate(r).reshape(-1)[623 * 512:624 * 512].copy()
+    B = 512
+    assert xb.size == B
+    xo = oracle_mod.roundtrip_variant(xb, B, "taco", "e4m3").reshape(-1)
+    c, al, s = oracle_mod.compress(xb, B)
+    v, vb = parity.code_arguments(xb, B, "taco", "e4m3", 1.0, 0.0)
+    ties = dict(parity.tie_changes(v, vb, "e4m3"))
+    assert sorted(ties) == [4, 274]
+    for flips in ([274], [4, 274]):
+        cc = c.reshape(-1).copy()
+        for j in flips:
+            d = oracle_mod.decode(cc[j:j + 1], "e4m3")[0]
+            cc[j] = oracle_mod.encode(np.array([d + ties[j]], np.float32), "e4m3")[0]
+        y = oracle_mod.double_to_bf16(oracle_mod.reconstruct_f64(cc, al, s, B))
+        assert parity.compare_roundtrip(y, xb, B, "taco", "e4m3", xo=xo)["flip_blocks"] == 1
 
 
 @pytest.mark.parametrize("variant", ["ds", "tensor", "ash", "hadamard"])
@@ -183,3 +225,57 @@ def test_accumulate_n_bound(oracle_mod, synth_mod):
     far[333] += np.float32(1e-3 * np.max(np.abs(ref[256:512])))
     with pytest.raises(AssertionError):
         parity.compare_accumulate_n(far, acc0, pays, 256)
+
+
+def test_roundtrip_one_flip_of_a_coarse_variant(oracle_mod, synth_mod):
+    """ASH alone in INT8 has codes -3..3 on this gradient tensor (28 x 2560,
+    seed 993876353, B = 512): block 23's one rounding tie, flipped, moves the
+    whole tensor's relative RMS by more than 1e-3; the flip is explained and
+    the RMS is taken with it applied."""
+    import math
+    r = synth_mod.WORKLOADS["grad_8192x8192"].with_shape(28, 2560, seed=993876353)
+    x = synth_mod.generate(r).reshape(-1)
+    B, k = 512, 23
+    xo = oracle_mod.roundtrip_variant(x, B, "ash", "int8").reshape(-1)
+    xb = x[k * B:(k + 1) * B]
+    v, vb = parity.code_arguments(xb, B, "ash", "int8", 1.0, 0.0)
+    ties = parity.tie_changes(v, vb, "int8")
+    assert len(ties) == 1
+    j, d = ties[0]
+    a, _, _ = oracle_mod.ash_block(xb, B)
+    change = np.zeros(B)
+    change[j] = d / float(np.float32(a))               # code domain -> x: 1/alpha
+    y = xo.copy()
+    y[k * B:(k + 1) * B] += oracle_mod.fwht(change) / math.sqrt(B)
+    yb = oracle_mod.double_to_bf16(y)
+    ref = synth_mod.bits_to_f32(oracle_mod.double_to_bf16(xo)).astype(np.float64)
+    assert parity.rel_rms(synth_mod.bits_to_f32(yb).astype(np.float64), ref) > parity.RECON_RTOL
+    assert parity.compare_roundtrip(yb, x, B, "ash", "int8", xo=xo)["flip_blocks"] == 1
+
+
+def test_owner_step_exact_ties(oracle_mod, synth_mod):
+    """Two payloads with no own partial (Qwen-7B activation workload, 4 x 512,
+    seed 619818529, B = 512): the rotated sum of block 1 sits exactly on a
+    midpoint between two E4M3 codes at three elements.  All three flipped
+    (more than the per-case bound on 2048 elements allows) pass as exact
+    ties; a flip that is at no tie still fails."""
+    rows, cols, B, seed = 4, 512, 512, 619818529
+    r = synth_mod.WORKLOADS["qwen7b_act_16384x3584"].with_shape(rows, cols, seed=seed)
+    pays = [oracle_mod.compress(synth_mod.generate(r.with_shape(rows, cols, seed=seed + 1 + p)), B)
+            for p in range(2)]
+    c, a, s = parity.oracle_reduce_compress(None, pays, B)
+    x = sum(oracle_mod.reconstruct_f64(pc, pa, ps, B).reshape(-1, B)[1] for pc, pa, ps in pays)
+    R = oracle_mod.fwht(x)
+    v = 448.0 * R / np.max(np.abs(R))
+    ties = parity.tie_changes(v, 1e-12 * np.abs(v), "e4m3")   # exact up to the oracle's rounding
+    assert len(ties) == 3 and parity.allowed_flips(rows * cols, parity.OWNER_FLIP_RATE) < 3
+    bad = c.copy()
+    for j, d in ties:
+        o = oracle_mod.decode(c[B + j:B + j + 1])[0]
+        bad[B + j] = oracle_mod.encode(np.array([o + d], np.float32))[0]
+        assert bad[B + j] != c[B + j]
+    assert parity.compare_reduce(None, pays, B, bad, a, s)["flips"] == 3
+    far = c.copy()
+    far[5] ^= 0x02
+    with pytest.raises(AssertionError):
+        parity.compare_reduce(None, pays, B, far, a, s)
