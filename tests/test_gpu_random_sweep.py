@@ -19,9 +19,14 @@ from test_gpu_fidelity import check_variant
 pytestmark = pytest.mark.gpu
 
 # 300 fixed-seed cases by default; TACO_SWEEP_CASES / TACO_SWEEP_SEED run a
-# longer sweep or another seed.
+# longer sweep or another seed.  TACO_SWEEP_MAX_ROWS raises the row count's
+# upper end (default 200), and TACO_SWEEP_PACKED (a probability, default 0)
+# also sends cases through the interleaved wire layout; both are drawn from
+# a generator of their own, so the default sequence of cases is unchanged.
 CASES = int(os.environ.get("TACO_SWEEP_CASES", "300"))
 SEED = int(os.environ.get("TACO_SWEEP_SEED", "20261202"))
+MAX_ROWS = int(os.environ.get("TACO_SWEEP_MAX_ROWS", "200"))
+PACKED = float(os.environ.get("TACO_SWEEP_PACKED", "0"))
 
 
 def test_random_sweep():
@@ -37,6 +42,7 @@ def test_random_sweep():
 
     names = sorted(synth.WORKLOADS)
     rng = np.random.default_rng(SEED)
+    extra = np.random.default_rng([SEED, 1])
     flips = {"e4m3": [0, 0], "e5m2": [0, 0], "int8": [0, 0]}
     owners = 0
     for case in range(CASES):
@@ -52,10 +58,13 @@ def test_random_sweep():
         accn = rng.random() < 0.1
         variant = str(rng.choice(["taco", "direct", "ds", "ash", "hadamard", "tensor"]))
         study = rng.random() < 0.1
+        if MAX_ROWS > 200 and extra.random() < 0.5:
+            rows = int(extra.integers(200, MAX_ROWS + 1))
+        packed = extra.random() < PACKED
         print(f"[case] sweep {case}: {name} {rows}x{cols} B={B} fmt={fmt} seed={seed}"
               + (f" owner P={P} own={with_own}" if owner else "")
-              + (f" accumulate_n P={P}" if accn else "") + (f" roundtrip {variant}" if study else ""),
-              flush=True)
+              + (f" accumulate_n P={P}" if accn else "") + (f" roundtrip {variant}" if study else "")
+              + (" packed" if packed else ""), flush=True)
         r = synth.WORKLOADS[name].with_shape(rows, cols, seed=seed)
         x = synth.generate(r)
         c, a, s = taco.compress(gpu_bf16(x), block=B, fmt=fmt)
@@ -68,6 +77,20 @@ def test_random_sweep():
         torch.cuda.synchronize()
         compare_decompress(y.view(torch.int16).cpu().numpy().view(np.uint16), oc, oa, os_, B,
                            fmt=fmt)
+        if packed:
+            # The interleaved layout: the GPU payload unpacked and compared
+            # like the separate buffers, and the oracle's payload decompressed.
+            pay = taco.compress_packed(gpu_bf16(x), block=B, fmt=fmt)
+            torch.cuda.synchronize()
+            pc, pa, ps = oracle.unpack(pay.cpu().numpy(), B)
+            stp = compare_compress(x, B, pc, pa, ps, fmt=fmt)
+            flips[fmt][0] += stp["flips"]
+            flips[fmt][1] += stp["n"]
+            yp = taco.decompress_packed(gpu(oracle.pack(oc, oa, os_, B).reshape(-1)), x.shape,
+                                        block=B, fmt=fmt)
+            torch.cuda.synchronize()
+            compare_decompress(yp.view(torch.int16).cpu().numpy().view(np.uint16), oc, oa, os_,
+                               B, fmt=fmt)
         if accn:
             xs = [synth.generate(r.with_shape(rows, cols, seed=seed + 100 + p)) for p in range(P)]
             accumulate_n_check(taco, xs, B, (rng.standard_normal(x.size) * 0.01).astype(np.float32),
