@@ -2,9 +2,14 @@
 
     python gradients_taco_compress_amd/build.py
     TACO_HIPCC_FLAGS="-DTACO_WAVES_PER_GROUP=8" python gradients_taco_compress_amd/build.py
+    TACO_HIPCC_FLAGS="-DTACO_WAVES_PER_GROUP=8" python gradients_taco_compress_amd/build.py \
+        --out /tmp/libtaco_wpg8.so
 
 (TACO_HIPCC_FLAGS: extra hipcc flags, e.g. the kernels' compile-time tuning
-knobs, for timing a variant with bench.py; unset for the default build)
+knobs, for timing a variant with bench.py; unset for the default build.
+--out PATH builds only the operator library, to PATH, leaving the in-tree
+libraries alone: a variant to time beside the default one with
+``python -m gradients_taco_compress_amd.abtime``)
 
 (run as a script: importing it through the package would load the package,
 which needs the library this builds)
@@ -62,14 +67,17 @@ def extra_flags() -> list:
     return os.environ.get("TACO_HIPCC_FLAGS", "").split()
 
 
-def build(verbose: bool = False) -> str:
+def build(verbose: bool = False, out: str | None = None) -> str:
     """Compile every source (in parallel), link LIB and PROBE_LIB; always
-    recompiles.  Returns LIB."""
+    recompiles.  Returns LIB.  With out, only the operator library is
+    built, to that path."""
     from concurrent.futures import ThreadPoolExecutor
     tag = f".tmp{os.getpid()}"
     flags = FLAGS + extra_flags()
-    sources = SOURCES + [PROBE_SOURCE]
+    sources = SOURCES + ([] if out else [PROBE_SOURCE])
+    lib = os.path.abspath(out) if out else LIB
     objs = [os.path.join(CSRC, os.path.basename(src) + tag + ".o") for src in sources]
+    temps = objs + [lib + tag, PROBE_LIB + tag]
     try:
         with ThreadPoolExecutor(max_workers=len(sources)) as pool:
             jobs = [pool.submit(_run, [HIPCC, *flags, "-I", os.path.join(ROOT, "include"),
@@ -77,17 +85,26 @@ def build(verbose: bool = False) -> str:
                     for src, obj in zip(sources, objs)]
             for j in jobs:
                 j.result()
-        _run([HIPCC, "--offload-arch=gfx950", "-shared", *objs[:-1], "-o", LIB + tag], verbose)
-        _run([HIPCC, "--offload-arch=gfx950", "-shared", objs[-1], "-o", PROBE_LIB + tag],
+        _run([HIPCC, "--offload-arch=gfx950", "-shared", *objs[:len(SOURCES)], "-o", lib + tag],
              verbose)
-        os.replace(LIB + tag, LIB)
-        os.replace(PROBE_LIB + tag, PROBE_LIB)
+        if not out:
+            _run([HIPCC, "--offload-arch=gfx950", "-shared", objs[-1], "-o", PROBE_LIB + tag],
+                 verbose)
+        os.replace(lib + tag, lib)
+        if not out:
+            os.replace(PROBE_LIB + tag, PROBE_LIB)
     finally:
-        for path in objs + [LIB + tag, PROBE_LIB + tag]:
+        for path in temps:
             if os.path.exists(path):
                 os.remove(path)
-    return LIB
+    return lib
 
 
 if __name__ == "__main__":
-    print(build(verbose="-q" not in sys.argv))
+    import argparse
+    ap = argparse.ArgumentParser(description="Build libtaco (and libtaco_probe) for gfx950.")
+    ap.add_argument("-q", action="store_true", help="quiet")
+    ap.add_argument("--out", default=None,
+                    help="build only the operator library, to this path")
+    a = ap.parse_args()
+    print(build(verbose=not a.q, out=a.out))

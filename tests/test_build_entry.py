@@ -34,3 +34,28 @@ def test_extra_hipcc_flags_come_from_the_environment(monkeypatch):
     assert m.extra_flags() == []
     monkeypatch.setenv("TACO_HIPCC_FLAGS", " -DTACO_WAVES_PER_GROUP=8  -DTACO_MAX_GROUPS=2048 ")
     assert m.extra_flags() == ["-DTACO_WAVES_PER_GROUP=8", "-DTACO_MAX_GROUPS=2048"]
+
+
+def test_variant_build_goes_to_its_own_path(monkeypatch, tmp_path):
+    """build(out=...) compiles the operator's sources with the extra flags and
+    links them to that path only: the in-tree libraries are not rebuilt and
+    the probe library is left out."""
+    import __graft_entry__ as g
+    m = g._load_hip_build()
+    cmds = []
+
+    def fake_run(cmd, verbose):
+        cmds.append(cmd)
+        if "-o" in cmd:
+            open(cmd[cmd.index("-o") + 1], "wb").close()
+    monkeypatch.setattr(m, "_run", fake_run)
+    monkeypatch.setenv("TACO_HIPCC_FLAGS", "-DTACO_WAVES_PER_GROUP=8")
+    out = str(tmp_path / "libtaco_wpg8.so")
+    assert m.build(out=out) == out and os.path.exists(out)
+    compiles = [c for c in cmds if "-c" in c]
+    links = [c for c in cmds if "-shared" in c]
+    assert sorted(c[c.index("-c") + 1] for c in compiles) == sorted(m.SOURCES)
+    assert all("-DTACO_WAVES_PER_GROUP=8" in c for c in compiles)
+    assert len(links) == 1 and links[0][links[0].index("-o") + 1].startswith(out)
+    assert not any(m.LIB in " ".join(c) or m.PROBE_LIB in " ".join(c) for c in cmds)
+    assert not [f for f in os.listdir(m.CSRC) if ".tmp" in f]      # objects removed
