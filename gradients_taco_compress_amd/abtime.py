@@ -84,7 +84,11 @@ def outputs(torch, lib, bufs, rows, cols, block):
     return [t.clone() for t in (c, a, s, y, acc)]
 
 
-def compare(libs, workload: str, block: int, ops=OPS, repeats: int = REPEATS) -> dict:
+def compare(libs, workload: str, block: int, ops=OPS, repeats: int = REPEATS,
+            rotate_bytes: int = ROTATE_LOAD_BYTES, launches: int | None = None) -> dict:
+    """Times ops of every build in libs on a workload (see the module
+    docstring); rotate_bytes and launches (per graph) shrink the run for a
+    quick check."""
     import numpy as np
     import torch
     import synth
@@ -92,7 +96,7 @@ def compare(libs, workload: str, block: int, ops=OPS, repeats: int = REPEATS) ->
     n, m = r.numel, r.numel // block
     rows, cols = r.rows, r.cols
     x0 = torch.from_numpy(synth.generate(r).view(np.int16)).cuda().view(torch.bfloat16)
-    nsets = max(1, -(-ROTATE_LOAD_BYTES // n))           # the codes: n bytes per set
+    nsets = max(1, -(-rotate_bytes // n))                # the codes: n bytes per set
     sets = []
     for _ in range(nsets):
         sets.append((x0.clone(), torch.empty(n, dtype=torch.uint8, device="cuda"),
@@ -110,7 +114,7 @@ def compare(libs, workload: str, block: int, ops=OPS, repeats: int = REPEATS) ->
     for bufs in sets:
         launcher(loaded[0], "compress", bufs, rows, cols, block)(stream.cuda_stream)
     torch.cuda.synchronize()
-    K = max(nsets, 50, int(2e9 // (3 * n)))
+    K = launches or max(nsets, 50, int(2e9 // (3 * n)))
     graphs = {}
     for li, lib in enumerate(loaded):
         for op in ops:
