@@ -59,3 +59,30 @@ def test_variant_build_goes_to_its_own_path(monkeypatch, tmp_path):
     assert len(links) == 1 and links[0][links[0].index("-o") + 1].startswith(out)
     assert not any(m.LIB in " ".join(c) or m.PROBE_LIB in " ".join(c) for c in cmds)
     assert not [f for f in os.listdir(m.CSRC) if ".tmp" in f]      # objects removed
+
+
+def test_every_compile_targets_gfx950_without_packed_fp32(monkeypatch, tmp_path):
+    """Each hipcc compile of build() (the default build and a variant built
+    with --out) targets gfx950 and turns the packed-FP32 feature off, with
+    the optimisation level and no sanitizer."""
+    import __graft_entry__ as g
+    m = g._load_hip_build()
+    cmds = []
+
+    def fake_run(cmd, verbose):
+        cmds.append(cmd)
+        if "-o" in cmd:
+            open(cmd[cmd.index("-o") + 1], "wb").close()
+    monkeypatch.setattr(m, "_run", fake_run)
+    monkeypatch.setattr(m, "LIB", str(tmp_path / "libtaco.so"))
+    monkeypatch.setattr(m, "PROBE_LIB", str(tmp_path / "libtaco_probe.so"))
+    monkeypatch.delenv("TACO_HIPCC_FLAGS", raising=False)
+    m.build()
+    m.build(out=str(tmp_path / "variant.so"))
+    compiles = [c for c in cmds if "-c" in c]
+    assert len(compiles) == 2 * len(m.SOURCES) + 1            # the probe in the default build
+    feature = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+    for c in compiles:
+        assert "--offload-arch=gfx950" in c and "-O3" in c
+        assert any(c[i:i + 4] == feature for i in range(len(c) - 3)), c
+        assert not any(a.startswith("-fsanitize") for a in c)
