@@ -124,14 +124,28 @@ LIBTACO_SOURCES = ("taco_abi.hip", "taco_e4m3.hip", "taco_e5m2.hip", "taco_int8.
                    "taco_internal.hpp", "taco_kernels.hpp")
 
 
+def build_flags() -> list:
+    """The hipcc flags of the default build (build.py's FLAGS), read without
+    importing the package."""
+    import importlib.util
+    spec = importlib.util.spec_from_file_location(
+        "_taco_build_flags", os.path.join(os.path.dirname(KERNEL_DIR), "build.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return list(mod.FLAGS)
+
+
 def kernel_hash() -> str:
-    """sha256[:16] over libtaco's sources (file names and contents, sorted)."""
+    """sha256[:16] over libtaco's sources (file names and contents, sorted)
+    and the compile flags of the default build: the committed counter runs
+    count only while the code they were taken on is the code that runs."""
     h = hashlib.sha256()
     for name in sorted(os.listdir(KERNEL_DIR)):
         if name in LIBTACO_SOURCES:
             h.update(name.encode())
             with open(os.path.join(KERNEL_DIR, name), "rb") as f:
                 h.update(f.read())
+    h.update(("flags:" + " ".join(build_flags())).encode())
     return h.hexdigest()[:16]
 
 

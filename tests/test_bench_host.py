@@ -145,6 +145,16 @@ def test_kernel_hash_covers_exactly_libtaco_sources():
     assert sorted(os.path.basename(f) for f in b.ALL_FILES) == sorted(bench.LIBTACO_SOURCES)
 
 
+def test_kernel_hash_follows_the_build_flags(monkeypatch):
+    """The same sources built with other flags are other code: the hash, and
+    with it the committed counter runs, change with build.py's FLAGS."""
+    h0 = bench.kernel_hash()
+    flags = bench.build_flags()
+    assert "-amdgpu-kernarg-preload-count=16" in flags and "-packed-fp32-ops" in flags
+    monkeypatch.setattr(bench, "build_flags", lambda: flags[:-2])
+    assert bench.kernel_hash() != h0
+
+
 def test_config_summary_carries_the_floors():
     rec = bench.record(_res("roundtrip"), "gpt2.7b_rowpar_8192x2560", _Args())
     rec["roofline"]["launch_floor"] = {"kernel": "empty", "groups": 5120, "us": 2.1}
